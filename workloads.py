@@ -1,0 +1,196 @@
+"""Seeded synthetic inputs for the attention workloads (shared by tests, bench and smoke).
+
+This module only draws random numbers, rounds them to the storage dtype and lays
+them out (padding, paged cache, block table). It holds none of the attention
+arithmetic: the CPU oracle and the HIP library both receive what it returns.
+
+Workload shapes are those of the five attention cases this library is measured
+on: a tiny 128x128 head, a BERT-base-shaped ragged encoder batch, a
+Llama3-8B-shaped causal prefill (batch 2, 512 tokens, 32/8 heads), a
+Qwen2.5-1.5B-shaped paged decode batch (64 sequences, 12/2 heads, 16-token
+blocks) and a 16384-token causal prefill. Values are N(0,1) as the pages'
+micro-benchmarks use random activations; the paged cache is laid out with a
+seeded random permutation of physical blocks, as in a vLLM-style block pool.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+BLOCK = 16  # tokens per KV-cache block (vLLM example uses block_size=16)
+
+
+def round_to(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float32 values to bf16/fp16 (round to nearest even); return float32 holding them."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == "fp16":
+        return x.astype(np.float16).astype(np.float32)
+    if dtype == "bf16":
+        u = x.view(np.uint32).astype(np.uint64)
+        lsb = (u >> 16) & 1
+        u = (u + 0x7FFF + lsb) & 0xFFFF0000
+        out = u.astype(np.uint32).view(np.float32)
+        # keep NaN payloads NaN (inputs are finite except planted sentinels)
+        out = np.where(np.isnan(x), np.float32("nan"), out)
+        return out
+    if dtype == "fp32":
+        return x
+    raise ValueError(dtype)
+
+
+@dataclass
+class PrefillCase:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    T: int
+    D: int
+    dtype: str
+    causal: bool
+    ragged: bool
+    seed: int
+    scale: float = field(default=0.0)
+
+    def __post_init__(self):
+        if self.scale == 0.0:
+            self.scale = 1.0 / math.sqrt(self.D)
+
+
+@dataclass
+class DecodeCase:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    dtype: str
+    ctx_lo: int
+    ctx_hi: int
+    seed: int
+    spare_blocks: int = 8
+    scale: float = field(default=0.0)
+
+    def __post_init__(self):
+        if self.scale == 0.0:
+            self.scale = 1.0 / math.sqrt(self.D)
+
+
+# The five measured cases.
+TINY = PrefillCase("tiny fp16 1x1x128x64", B=1, Hq=1, Hkv=1, T=128, D=64, dtype="fp16",
+                   causal=False, ragged=False, seed=1)
+BERT = PrefillCase("bert-base ragged fp16 B=8 H=12 Tmax=512 D=64", B=8, Hq=12, Hkv=12, T=512, D=64,
+                   dtype="fp16", causal=False, ragged=True, seed=2)
+LLAMA = PrefillCase("llama3-8b causal bf16 B=2 Hq=32 Hkv=8 T=512 D=128", B=2, Hq=32, Hkv=8, T=512, D=128,
+                    dtype="bf16", causal=True, ragged=False, seed=3)
+QWEN = DecodeCase("qwen2.5-1.5b paged decode bf16 B=64 Hq=12 Hkv=2 D=128 ctx~U[512,4096]", B=64, Hq=12,
+                  Hkv=2, D=128, dtype="bf16", ctx_lo=512, ctx_hi=4096, seed=4)
+LONG = PrefillCase("long causal bf16 B=1 Hq=32 Hkv=8 T=16384 D=128", B=1, Hq=32, Hkv=8, T=16384, D=128,
+                   dtype="bf16", causal=True, ragged=False, seed=5)
+
+ALL_PREFILL = [TINY, BERT, LLAMA, LONG]
+
+
+def prefill_inputs(case: PrefillCase, nan_padding: bool = False, Tq: int | None = None,
+                   Tk: int | None = None):
+    """Return dict(q, k, v, seq_lens) as float32 numpy arrays holding dtype-rounded values.
+
+    Draw order: q, k, v (N(0,1), float32) then the ragged lengths. Lengths are
+    uniform integers in [64, T] (both ends included). With ``nan_padding`` the
+    padded rows (position >= length) of q, k and v are set to NaN.
+    """
+    rng = np.random.default_rng(case.seed)
+    Tq = case.T if Tq is None else Tq
+    Tk = case.T if Tk is None else Tk
+    q = rng.standard_normal((case.B, case.Hq, Tq, case.D), dtype=np.float32)
+    k = rng.standard_normal((case.B, case.Hkv, Tk, case.D), dtype=np.float32)
+    v = rng.standard_normal((case.B, case.Hkv, Tk, case.D), dtype=np.float32)
+    q, k, v = (round_to(a, case.dtype) for a in (q, k, v))
+    seq_lens = None
+    if case.ragged:
+        lo = min(64, case.T)
+        seq_lens = rng.integers(lo, case.T + 1, case.B).astype(np.int32)
+        if nan_padding:
+            for b, L in enumerate(seq_lens):
+                q[b, :, L:, :] = np.nan
+                k[b, :, L:, :] = np.nan
+                v[b, :, L:, :] = np.nan
+    return dict(q=q, k=k, v=v, seq_lens=seq_lens)
+
+
+def decode_inputs(case: DecodeCase, nan_fill: bool = False, ctx_lens=None):
+    """Return dict(q, k_cache, v_cache, block_table, ctx_lens) for a paged decode batch.
+
+    Draw order: context lengths (uniform integers in [ctx_lo, ctx_hi]), then a
+    permutation of the physical blocks, then q, k_cache, v_cache (N(0,1)).
+    Logical block i of sequence b maps to physical block perm[off_b + i];
+    unused table entries are -1. ``spare_blocks`` extra physical blocks are never
+    referenced. With ``nan_fill`` unused slots (tail of the last block and the
+    spare blocks) hold NaN.
+    """
+    rng = np.random.default_rng(case.seed)
+    if ctx_lens is None:
+        ctx = rng.integers(case.ctx_lo, case.ctx_hi + 1, case.B).astype(np.int32)
+    else:
+        ctx = np.asarray(ctx_lens, dtype=np.int32)
+    nblk = (ctx + BLOCK - 1) // BLOCK
+    used = int(nblk.sum())
+    NB = used + case.spare_blocks
+    perm = rng.permutation(used).astype(np.int32)
+    max_blocks = int(-(-case.ctx_hi // BLOCK))
+    max_blocks = max(max_blocks, int(nblk.max()))
+    table = np.full((case.B, max_blocks), -1, dtype=np.int32)
+    off = 0
+    for b in range(case.B):
+        table[b, : nblk[b]] = perm[off: off + nblk[b]]
+        off += nblk[b]
+    q = rng.standard_normal((case.B, case.Hq, case.D), dtype=np.float32)
+    kc = rng.standard_normal((NB, case.Hkv, BLOCK, case.D), dtype=np.float32)
+    vc = rng.standard_normal((NB, case.Hkv, BLOCK, case.D), dtype=np.float32)
+    q, kc, vc = (round_to(a, case.dtype) for a in (q, kc, vc))
+    if nan_fill:
+        for b in range(case.B):
+            tail = int(ctx[b]) % BLOCK
+            if tail:
+                last = table[b, nblk[b] - 1]
+                kc[last, :, tail:, :] = np.nan
+                vc[last, :, tail:, :] = np.nan
+        kc[used:] = np.nan
+        vc[used:] = np.nan
+    return dict(q=q, k_cache=kc, v_cache=vc, block_table=table, ctx_lens=ctx)
+
+
+def prefill_flops(B, Hq, Tq, Tk, D, causal, seq_lens=None):
+    """Algorithmic flops: 4*D per unmasked (query, key) pair (QK^T and PV, one multiply-add each)."""
+    pairs = 0
+    for b in range(B):
+        Lq = Tq if seq_lens is None else int(seq_lens[b])
+        Lk = Tk if seq_lens is None else int(seq_lens[b])
+        if causal:
+            off = Lk - Lq
+            for_rows = 0
+            # row i sees keys 0..min(Lk-1, i+off)
+            for i in range(Lq):
+                n = min(Lk, i + off + 1)
+                for_rows += max(0, n)
+            pairs += for_rows
+        else:
+            pairs += Lq * Lk
+    return 4.0 * D * Hq * pairs
+
+
+def decode_bytes(ctx_lens, Hq, Hkv, D, elem=2, max_blocks=None):
+    """Algorithmic HBM bytes of one paged decode call.
+
+    K and V of every valid token, read once per kv head, plus q, o (elem bytes),
+    lse (fp32), ctx_lens and the block-table entries actually read.
+    """
+    ctx = np.asarray(ctx_lens, dtype=np.int64)
+    B = ctx.shape[0]
+    kv = int(ctx.sum()) * Hkv * D * elem * 2
+    qo = 2 * B * Hq * D * elem
+    lse = B * Hq * 4
+    table = int(((ctx + BLOCK - 1) // BLOCK).sum()) * 4
+    return kv + qo + lse + table + 4 * B
