@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Benchmark of libattn on one MI355X.
+
+One step = one pass of the whole hot path on seeded synthetic inputs:
+  * causal bf16 prefill, B=1, Hq=32, Hkv=8, T=16384, D=128 (attn_fwd), and
+  * paged bf16 decode, B=64, Hq=12, Hkv=2, D=128, ctx ~ U[512, 4096],
+    16-token blocks (attn_decode_paged).
+Each call is timed with HIP events on the stream it runs on; a write over a
+1 GiB buffer precedes each call (outside its events) so the 256 MB Infinity
+Cache does not serve the inputs from a previous repetition.
+
+Prints ONE JSON line. value = prefill TFLOP/s (algorithmic flops: 4*D per
+unmasked query/key pair); the decode figure (algorithmic HBM bytes: K and V of
+valid tokens once per kv head, plus q, o, lse, ctx_lens and the block-table
+entries read) sits in "decode". roofline = the prefill kernel against the
+dense bf16 MFMA peak (2.5 PFLOP/s); decode.roofline against 8 TB/s HBM.
+cpu_baseline = the float64 CPU oracle timed on a bounded sample of the same
+prefill workload on this host.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s (bf16 causal prefill) + decode HBM GB/s, % of MI355X peak"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = {
+    "prefill": ["tiled_attention_02_amd/csrc/prefill_fwd.hip", "tiled_attention_02_amd/csrc/attn_device.h"],
+    "decode": ["tiled_attention_02_amd/csrc/decode_paged.hip", "tiled_attention_02_amd/csrc/attn_device.h"],
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+
+
+def source_sha(kind):
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kind):
+    """HBM bytes per launch from committed rocprofv3 counters, if they match the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(kind)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != source_sha(kind):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-flush", action="store_true", help="skip the cache flush between calls")
+    p.add_argument("--only", choices=["prefill", "decode"], default=None,
+                   help="profile helper: run only one of the two calls (not a benchmark line)")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="run a plain device copy of this many MiB (counter calibration) and exit")
+    return p.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline_prefill(x, case, budget_heads=32, row_stride=8):
+    """Time the float64 oracle on a bounded sample of the prefill workload."""
+    import numpy as np
+    from oracle import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    heads = list(range(0, case.Hq, max(1, case.Hq // budget_heads)))[:budget_heads]
+    rows = np.arange(0, case.T, row_stride)
+    picks = np.array([(0, h, i) for h in heads for i in rows])
+    t0 = time.perf_counter()
+    O.prefill_rows(x["q"], x["k"], x["v"], case.scale, True, None, picks)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * case.D * float((rows + 1).sum()) * len(heads)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"float64 oracle on {len(heads)} of {case.Hq} heads x {len(rows)} query rows "
+                      f"(every {row_stride}th) of the 16384-token causal prefill; {dt:.1f} s wall; "
+                      f"algorithmic flops of the sampled rows / wall time"}
+
+
+def cpu_baseline_decode(x, case, nseq=64):
+    import numpy as np
+    import workloads as W
+    from oracle import oracle as O
+    sl = slice(0, nseq)
+    t0 = time.perf_counter()
+    O.decode_paged(x["q"][sl], x["k_cache"], x["v_cache"], x["block_table"][sl], x["ctx_lens"][sl], case.scale)
+    dt = time.perf_counter() - t0
+    nbytes = W.decode_bytes(x["ctx_lens"][sl], case.Hq, case.Hkv, case.D)
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "kind": "oracle",
+            "sample": f"float64 oracle on {nseq} of {case.B} sequences; {dt:.2f} s wall"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "libattn's benchmark runs on one GPU only: multi-GPU runs are not part of "
+                                   "this build (every figure is a single-GPU figure)", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import tiled_attention_02_amd as ta
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        log("bench.py needs a GPU")
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ta.lib()
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n}))
+        return
+
+    pc, dc = W.LONG, W.QWEN
+    log(f"[bench] building inputs: {pc.name}; {dc.name}")
+    xp = W.prefill_inputs(pc)
+    xd = W.decode_inputs(dc)
+    bf = torch.bfloat16
+    q = torch.from_numpy(xp["q"]).to(bf).to(dev)
+    k = torch.from_numpy(xp["k"]).to(bf).to(dev)
+    v = torch.from_numpy(xp["v"]).to(bf).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    dq = torch.from_numpy(xd["q"]).to(bf).to(dev)
+    kc = torch.from_numpy(xd["k_cache"]).to(bf).to(dev)
+    vc = torch.from_numpy(xd["v_cache"]).to(bf).to(dev)
+    bt = torch.from_numpy(xd["block_table"]).to(dev)
+    cl = torch.from_numpy(xd["ctx_lens"]).to(dev)
+    do = torch.empty_like(dq)
+    dlse = torch.empty(dq.shape[:2], dtype=torch.float32, device=dev)
+    ws = torch.empty(max(256, ta.attn_decode_workspace_bytes(dc.B, dc.Hq, dc.D, bt.shape[1])), dtype=torch.uint8,
+                     device=dev)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    pflops = W.prefill_flops(pc.B, pc.Hq, pc.T, pc.T, pc.D, True)
+    dbytes = W.decode_bytes(xd["ctx_lens"], dc.Hq, dc.Hkv, dc.D)
+    run_p = args.only in (None, "prefill")
+    run_d = args.only in (None, "decode")
+
+    def step(evs):
+        if run_p:
+            if not args.no_flush:
+                flush.zero_()
+            evs[0].record()
+            ta.attn_fwd(q, k, v, scale=pc.scale, causal=True, out=o, lse=lse)
+            evs[1].record()
+        if run_d:
+            if not args.no_flush:
+                flush.zero_()
+            evs[2].record()
+            ta.attn_decode_paged(dq, kc, vc, bt, cl, scale=dc.scale, out=do, lse=dlse, workspace=ws)
+            evs[3].record()
+
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(4)]  # noqa: E731
+    for i in range(args.warmup):
+        step(mk())
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps")
+    evs = [mk() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    p_ms = [e[0].elapsed_time(e[1]) for e in evs] if run_p else [float("nan")]
+    d_ms = [e[2].elapsed_time(e[3]) for e in evs] if run_d else [float("nan")]
+    p_avg, d_avg = float(np.mean(p_ms)), float(np.mean(d_ms))
+    log(f"[bench] prefill {p_avg:.3f} ms (min {min(p_ms):.3f}); decode {d_avg * 1e3:.1f} us "
+        f"(min {min(d_ms) * 1e3:.1f}); wall/step {wall / args.steps * 1e3:.2f} ms")
+    if args.only:
+        print(json.dumps({"only": args.only, "prefill_ms": p_avg, "decode_ms": d_avg}))
+        return
+
+    p_tfs = pflops / (p_avg * 1e-3) / 1e12
+    d_gbs = dbytes / (d_avg * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(p_tfs, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(p_avg + d_avg, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "causal bf16 prefill B=1 Hq=32 Hkv=8 T=16384 D=128 (value) + paged bf16 decode "
+                               "B=64 Hq=12 Hkv=2 D=128 ctx~U[512,4096] block=16 (decode)",
+                   "prefill_gflop_per_call": round(pflops / 1e9, 3),
+                   "decode_mb_per_call": round(dbytes / 1e6, 3),
+                   "cache_flush_between_calls": not args.no_flush,
+                   "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 3)},
+        "roofline": {"bound": "mfma", "achieved": round(p_tfs, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(p_tfs / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic("prefill"),
+                     "kernel": "prefill_kernel", "ms_per_launch": round(p_avg, 4),
+                     "algorithmic_flops_per_launch": pflops},
+        "decode": {"value": round(d_gbs, 1), "unit": "GB/s", "us_per_call": round(d_avg * 1e3, 2),
+                   "roofline": {"bound": "hbm", "achieved": round(d_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                "frac": round(d_gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic("decode"),
+                                "kernels": "decode_split_kernel + decode_combine_kernel",
+                                "algorithmic_bytes_per_call": dbytes}},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline: float64 oracle on a sample of the prefill workload")
+        out["cpu_baseline"] = cpu_baseline_prefill(xp, pc)
+        log("[bench] cpu baseline: float64 oracle on a sample of the decode workload")
+        out["decode"]["cpu_baseline"] = cpu_baseline_decode(xd, dc)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,129 @@
+/*
+ * libattn — fused scaled-dot-product attention for AMD Instinct MI355X (gfx950).
+ *
+ * O = softmax(scale * Q K^T + mask) V, computed tile by tile with online
+ * softmax statistics (running max, running sum, output rescaling) so that the
+ * T x T score matrix never reaches device memory, plus the per-row
+ * log-sum-exp. This is the blockwise attention described on the-ai.news,
+ * "Snelle attention-kernels en operatorfusie versnellen AI-modellen",
+ * section "FlashAttention-type aandacht en gepagineerde aandacht": per block
+ * a part of the scores is computed, the softmax statistics are updated and
+ * the output is accumulated on chip. The same section defines the paged KV
+ * cache read by attn_decode_paged: fixed-size blocks plus a block table that
+ * maps logical positions to physical blocks, 16 tokens per block in its vLLM
+ * example.
+ *
+ * Conventions shared by every call
+ *  - Ownership: every array argument is a caller-owned device pointer to a
+ *    contiguous, row-major buffer. The library allocates nothing, never
+ *    synchronises, and enqueues its kernels asynchronously on `stream`
+ *    (0 = the null stream). Calls are therefore stream-ordered and may be
+ *    captured in a HIP graph (stable addresses required).
+ *  - Errors: every entry point returns an attn_status. Problems visible on the
+ *    host (null or misaligned pointers, bad sizes, unsupported head size or
+ *    dtype, too small a workspace) return ATTN_ERR_INVALID or
+ *    ATTN_ERR_UNSUPPORTED before anything is launched; there is no silent
+ *    fallback (the same page notes that hard-coding a backend must fail when
+ *    no backend supports the inputs). A failed launch returns ATTN_ERR_HIP.
+ *    attn_last_error() returns a per-thread message for the last non-OK status.
+ *  - Device-resident values (seq_lens, ctx_lens, block ids) are trusted:
+ *    checking them would need a synchronisation. Out-of-range values there are
+ *    undefined behaviour.
+ *  - Alignment: q, k, v, o, k_cache, v_cache must be 16-byte aligned.
+ *  - Numerics: products accumulate in fp32; the probabilities are rounded to
+ *    the input dtype for the P.V product; O is rounded to the input dtype
+ *    (round to nearest even); lse is fp32, natural log.
+ */
+#ifndef LIBATTN_H
+#define LIBATTN_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID = 1,      /* malformed argument (null, size, alignment)        */
+  ATTN_ERR_UNSUPPORTED = 2,  /* well-formed but not served (head size, dtype ...) */
+  ATTN_ERR_HIP = 3           /* the HIP runtime reported an error at launch       */
+} attn_status;
+
+typedef enum { ATTN_F16 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+/*
+ * Prefill / encoder attention (blockwise attention of the section cited above).
+ *
+ *  q, o   : [B, Hq, Tq, D] elements of `dtype`.  o may not alias q, k or v.
+ *  k, v   : [B, Hkv, Tk, D] elements of `dtype`.
+ *  lse    : [B, Hq, Tq] fp32, natural-log log-sum-exp of the scaled, masked
+ *           scores of each query row; may be NULL.
+ *  Hq % Hkv == 0; query head h reads kv head h / (Hq / Hkv) (grouped-query
+ *  attention; Hq == Hkv is multi-head attention).
+ *  D in {64, 128}. B, Hq, Hkv, Tq, Tk >= 1; every tensor must hold fewer
+ *  than 2^31 elements.
+ *  scale  : multiplies q.k before the softmax (any finite value; 1/sqrt(D) is
+ *           the usual choice). Applied in fp32 to the fp32 dot products.
+ *  causal : nonzero -> key j is visible to query i iff j <= i + (Lk - Lq)
+ *           (bottom-right aligned, diagonal included).
+ *  seq_lens: NULL, or a device int32 array [B] of valid lengths
+ *           (1 <= seq_lens[b] <= Tq) for ragged batches; requires Tq == Tk and
+ *           applies to queries and keys alike (Lq = Lk = seq_lens[b]).
+ *           Positions >= seq_lens[b] are padding: they are never read into
+ *           the result, no work is spent on whole padding tiles, and the
+ *           padded output rows receive O = 0 and lse = -inf.
+ *  A query row that sees no key (possible only through the causal mask when
+ *  Lq > Lk) receives O = 0 and lse = -inf.
+ */
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int Hq, int Hkv, int Tq, int Tk, int D,
+                     float scale, int causal, const int* seq_lens,
+                     attn_dtype dtype, hipStream_t stream);
+
+/*
+ * One-token decode through a paged KV cache (paged attention of the section
+ * cited above): the key/value of position t of sequence b live in physical
+ * block block_table[b, t / block_size], slot t % block_size.
+ *
+ *  q, o        : [B, Hq, D] elements of `dtype` (one new token per sequence).
+ *  k_cache,
+ *  v_cache     : [num_blocks, Hkv, block_size, D] elements of `dtype`, so every
+ *                (block, kv head) holds block_size*D contiguous elements.
+ *  block_table : device int32 [B, max_blocks_per_seq]; entries at or beyond
+ *                ceil(ctx_lens[b] / block_size) are never read.
+ *  ctx_lens    : device int32 [B]; 1 <= ctx_lens[b] <= max_blocks_per_seq *
+ *                block_size. It counts every cached token including the new
+ *                one, whose key/value are already in the cache: the query sees
+ *                positions 0 .. ctx_lens[b]-1. Slots beyond it are never used.
+ *  lse         : [B, Hq] fp32 natural-log log-sum-exp; may be NULL.
+ *  block_size == 16, D in {64, 128}, Hq % Hkv == 0, Hq / Hkv <= 16.
+ *  workspace   : device scratch of at least attn_decode_workspace_bytes(...)
+ *                bytes, 256-byte aligned, owned by the caller; it holds the
+ *                per-split partial results (the key range of a long context is
+ *                split across workgroups and merged in a second pass).
+ *                Contents on entry are ignored; calls that share a workspace
+ *                must be ordered on one stream.
+ */
+attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                              const int* block_table, const int* ctx_lens, void* o, float* lse,
+                              int B, int Hq, int Hkv, int D, int block_size,
+                              int max_blocks_per_seq, int num_blocks, float scale,
+                              attn_dtype dtype, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/* Workspace bytes attn_decode_paged needs for these sizes (0 if they are invalid). */
+size_t attn_decode_workspace_bytes(int B, int Hq, int D, int max_blocks_per_seq, int block_size);
+
+/* Static, human-readable name of a status code. */
+const char* attn_status_str(attn_status s);
+
+/* Per-thread detail message of the last non-OK status ("" if none). */
+const char* attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBATTN_H */

@@ -1,0 +1,108 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+public header declares, and rejects malformed calls on the host before
+launching anything (no compute call is made here)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x10000)      # never dereferenced: every call below fails validation first
+FAKE_MIS = ctypes.c_void_p(0x10008)  # 8-byte aligned only
+
+
+def _declared():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w\s\*]*?\b(attn_\w+)\s*\(", src, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+@pytest.fixture(scope="module")
+def L():
+    import tiled_attention_02_amd as ta
+    if not os.path.exists(ta.LIB_PATH):
+        pytest.fail("libattn.so is not built (run __graft_entry__.build())")
+    return ta.lib()
+
+
+def test_header_declares_the_binding_exports():
+    import tiled_attention_02_amd as ta
+    assert _declared() == set(ta.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    import tiled_attention_02_amd as ta
+    assert ta.attn_status_str(0) == "ATTN_OK"
+    assert ta.attn_status_str(1) == "ATTN_ERR_INVALID"
+    assert ta.attn_status_str(2) == "ATTN_ERR_UNSUPPORTED"
+    assert ta.attn_status_str(3) == "ATTN_ERR_HIP"
+    assert ta.attn_status_str(77) == "ATTN_STATUS_UNKNOWN"
+
+
+def _fwd(L, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, Hq=4, Hkv=2, Tq=8, Tk=8, D=128, scale=0.1,
+         causal=0, seq=None, dtype=1):
+    return L.attn_fwd(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, D, ctypes.c_float(scale), causal, seq, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(o=None), 1), (dict(B=0), 1), (dict(Tk=0), 1), (dict(Hq=3), 1),
+    (dict(D=96), 2), (dict(D=256), 2), (dict(dtype=5), 2), (dict(scale=float("inf")), 1),
+    (dict(seq=FAKE, Tq=8, Tk=9), 1), (dict(q=FAKE_MIS), 1), (dict(lse=ctypes.c_void_p(0x10002)), 1),
+    (dict(B=1 << 16, Hq=1 << 10, Hkv=1, Tq=1 << 10), 2),
+])
+def test_fwd_rejects_before_launch(L, kw, code):
+    import tiled_attention_02_amd as ta
+    assert _fwd(L, **kw) == code
+    assert ta.attn_last_error().startswith("attn_fwd:")
+
+
+def _dec(L, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, cl=FAKE, o=FAKE, lse=None, B=2, Hq=12, Hkv=2, D=128, bs=16,
+         maxb=64, nb=100, scale=0.1, dtype=1, ws=FAKE, wsb=1 << 30):
+    return L.attn_decode_paged(q, kc, vc, bt, cl, o, lse, B, Hq, Hkv, D, bs, maxb, nb, ctypes.c_float(scale), dtype,
+                               ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bt=None), 1), (dict(cl=None), 1), (dict(B=0), 1), (dict(Hkv=5), 1), (dict(bs=32), 2), (dict(D=80), 2),
+    (dict(Hq=34, Hkv=2), 2), (dict(dtype=9), 2), (dict(ws=None), 1), (dict(wsb=16), 1),
+    (dict(ws=ctypes.c_void_p(0x10010)), 1), (dict(kc=FAKE_MIS), 1), (dict(scale=float("nan")), 1),
+])
+def test_decode_rejects_before_launch(L, kw, code):
+    import tiled_attention_02_amd as ta
+    assert _dec(L, **kw) == code
+    assert ta.attn_last_error().startswith("attn_decode_paged:")
+
+
+def test_workspace_size(L):
+    import tiled_attention_02_amd as ta
+    # 256 blocks of 16 tokens -> 16 splits of 256 tokens; each partial holds D values + log-sum
+    assert ta.attn_decode_workspace_bytes(64, 12, 128, 256) == 64 * 12 * 16 * 130 * 4
+    assert ta.attn_decode_workspace_bytes(64, 12, 128, 256, 8) == 0
+    assert ta.attn_decode_workspace_bytes(64, 12, 96, 256) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    import tiled_attention_02_amd as ta
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        ta.attn_fwd(x, x, x)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    import tiled_attention_02_amd as ta
+    monkeypatch.setattr(ta, "_lib", None)
+    monkeypatch.setattr(ta, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(ImportError):
+        ta.lib()

@@ -1,0 +1,281 @@
+"""GPU parity: libattn (HIP, through the C ABI) against the float64 CPU oracle.
+
+Tolerances (the accuracy target of this library): |O_gpu - O_ref| <= 1e-2 for
+bf16 and <= 2e-3 for fp16 over valid rows, widened element by element to one
+unit in the last place of the output format where that format cannot resolve
+the bound (|O| >= 2 in bf16, >= 4 in fp16); |lse_gpu - lse_ref| <= 1e-4 *
+max(1, |lse_ref|); padded rows exactly O = 0 and lse = -inf.
+Inputs come from workloads.py (seeded); padding and unused cache slots hold
+NaN so that any read of them into a result shows up.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 1e-2, "fp16": 2e-3}
+LSE_REL = 1e-4
+
+
+@pytest.fixture(scope="module")
+def ta(gpu):
+    import torch  # noqa: F401
+    import tiled_attention_02_amd as ta
+    ta.lib()
+    return ta
+
+
+def _tdt(dtype):
+    import torch
+    return torch.bfloat16 if dtype == "bf16" else torch.float16
+
+
+def _dev(x, dtype):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x)).to(_tdt(dtype)).cuda()
+
+
+def _note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _ulp(x, dtype):
+    """Spacing of the output format at |x| (bf16: 8 significant bits, fp16: 11)."""
+    mant = 8 if dtype == "bf16" else 11
+    ax = np.maximum(np.abs(x), 2.0 ** -14)
+    return 2.0 ** (np.floor(np.log2(ax)) - (mant - 1))
+
+
+def _compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype, valid=None, what=""):
+    """Element-wise bound: max(tol, one unit in the last place of the output dtype at O_ref).
+
+    The unit-in-the-last-place term only exceeds tol where the output format
+    itself cannot resolve tol (|O| >= 2 for bf16, >= 4 for fp16).
+    """
+    o_gpu = np.asarray(o_gpu, dtype=np.float64)
+    lse_gpu = np.asarray(lse_gpu, dtype=np.float64)
+    if valid is None:
+        valid = np.isfinite(lse_ref)
+    ov = valid[..., None] if o_ref.ndim == valid.ndim + 1 else valid
+    ov = np.broadcast_to(ov, o_ref.shape)
+    err = np.abs(o_gpu - o_ref)[ov]
+    allow = np.maximum(TOL[dtype], _ulp(o_ref[ov], dtype))
+    nrel = int((err > TOL[dtype]).sum())
+    emax = float(err.max()) if err.size else 0.0
+    ratio = float((err / allow).max()) if err.size else 0.0
+    lerr = float((np.abs(lse_gpu[valid] - lse_ref[valid]) / np.maximum(1.0, np.abs(lse_ref[valid]))).max()) \
+        if valid.any() else 0.0
+    _note(f"[parity] {what}: max|dO|={emax:.3e} (tol {TOL[dtype]}; {nrel} elements above tol within 1 ulp) "
+          f"max err/allowed={ratio:.3f} max rel dlse={lerr:.3e}")
+    assert np.isfinite(o_gpu[ov]).all(), f"{what}: non-finite output"
+    assert ratio <= 1.0, f"{what}: max |dO| = {emax} exceeds max(tol, 1 ulp)"
+    assert lerr <= LSE_REL, f"{what}: lse rel err = {lerr}"
+    inv = ~valid
+    if inv.any():
+        oi = np.broadcast_to(inv[..., None] if o_ref.ndim == inv.ndim + 1 else inv, o_ref.shape)
+        assert np.all(o_gpu[oi] == 0.0), f"{what}: padded rows not zero"
+        assert np.all(np.isneginf(lse_gpu[inv])), f"{what}: padded lse not -inf"
+
+
+def _run_prefill(ta, x, case, causal=None, scale=None):
+    import torch
+    causal = case.causal if causal is None else causal
+    scale = case.scale if scale is None else scale
+    q, k, v = (_dev(x[n], case.dtype) for n in ("q", "k", "v"))
+    sl = None if x["seq_lens"] is None else torch.from_numpy(x["seq_lens"]).cuda()
+    o, lse = ta.attn_fwd(q, k, v, scale=scale, causal=causal, seq_lens=sl)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def _full_check(ta, case, nan_padding=True, causal=None, scale=None, Tq=None, Tk=None, what=None):
+    x = W.prefill_inputs(case, nan_padding=nan_padding, Tq=Tq, Tk=Tk)
+    causal = case.causal if causal is None else causal
+    scale = case.scale if scale is None else scale
+    _note(f"[case] {what or case.name} causal={causal} scale={scale} Tq={x['q'].shape[2]} Tk={x['k'].shape[2]}")
+    o, lse = _run_prefill(ta, x, case, causal, scale)
+    o_ref, lse_ref = O.prefill(x["q"], x["k"], x["v"], scale, causal, x["seq_lens"])
+    _compare(o, lse, o_ref, lse_ref, case.dtype, what=what or case.name)
+    return o, lse
+
+
+# ---------------------------------------------------------------- the five workloads
+def test_tiny_fp16(ta):
+    _full_check(ta, W.TINY)
+
+
+def test_bert_ragged_fp16_nan_padding(ta):
+    _full_check(ta, W.BERT)
+
+
+def test_llama_causal_gqa_bf16(ta):
+    _full_check(ta, W.LLAMA)
+
+
+def test_long_causal_bf16_sampled(ta):
+    """16384-token causal prefill in the benchmark's launch configuration; oracle on sampled rows."""
+    import torch
+    case = W.LONG
+    x = W.prefill_inputs(case)
+    _note(f"[case] {case.name} (sampled rows)")
+    o, lse = _run_prefill(ta, x, case)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    rng = np.random.default_rng(99)
+    rows = np.unique(np.concatenate([[0, 1, 2, 31, 32, 63, 64, 127, 128, 129, 255, 256, 8191, 8192, 16256,
+                                      16383], rng.integers(0, case.T, 24)]))
+    picks = np.array([(0, h, i) for h in range(case.Hq) for i in rows])
+    o_ref, lse_ref = O.prefill_rows(x["q"], x["k"], x["v"], case.scale, True, None, picks)
+    _compare(o[0][picks[:, 1], picks[:, 2]], lse[0][picks[:, 1], picks[:, 2]], o_ref, lse_ref, "bf16",
+             what="long sampled")
+    del torch
+
+
+def _run_decode(ta, x, case, scale=None):
+    import torch
+    scale = case.scale if scale is None else scale
+    q = _dev(x["q"], case.dtype)
+    kc = _dev(x["k_cache"], case.dtype)
+    vc = _dev(x["v_cache"], case.dtype)
+    bt = torch.from_numpy(x["block_table"]).cuda()
+    cl = torch.from_numpy(x["ctx_lens"]).cuda()
+    o, lse = ta.attn_decode_paged(q, kc, vc, bt, cl, scale=scale)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def _decode_check(ta, case, ctx_lens=None, scale=None, what=None):
+    x = W.decode_inputs(case, nan_fill=True, ctx_lens=ctx_lens)
+    scale = case.scale if scale is None else scale
+    _note(f"[case] {what or case.name} ctx[min,max]=({x['ctx_lens'].min()},{x['ctx_lens'].max()}) scale={scale}")
+    o, lse = _run_decode(ta, x, case, scale)
+    o_ref, lse_ref = O.decode_paged(x["q"], x["k_cache"], x["v_cache"], x["block_table"], x["ctx_lens"], scale)
+    _compare(o, lse, o_ref, lse_ref, case.dtype, what=what or case.name)
+    return x, o, lse
+
+
+def test_qwen_paged_decode_bf16(ta):
+    _decode_check(ta, W.QWEN)
+
+
+# ---------------------------------------------------------------- prefill edge cases
+@pytest.mark.parametrize("D,dtype", [(64, "bf16"), (128, "fp16"), (64, "fp16"), (128, "bf16")])
+@pytest.mark.parametrize("causal", [False, True])
+def test_prefill_ragged_tails(ta, D, dtype, causal):
+    """Lengths that are not tile multiples, GQA group 3, several tiles plus a tail."""
+    case = W.PrefillCase("tails", B=3, Hq=6, Hkv=2, T=333, D=D, dtype=dtype, causal=causal, ragged=True, seed=21)
+    _full_check(ta, case, what=f"tails D={D} {dtype} causal={causal}")
+
+
+@pytest.mark.parametrize("Tq,Tk", [(77, 301), (300, 45), (1, 200), (200, 1), (129, 129)])
+def test_prefill_tq_ne_tk_bottom_right(ta, Tq, Tk):
+    case = W.PrefillCase("tq!=tk", B=2, Hq=4, Hkv=1, T=0, D=128, dtype="bf16", causal=True, ragged=False,
+                         seed=22, scale=0.0883883)
+    _full_check(ta, case, Tq=Tq, Tk=Tk, what=f"Tq={Tq} Tk={Tk} causal")
+    _full_check(ta, case, Tq=Tq, Tk=Tk, causal=False, what=f"Tq={Tq} Tk={Tk} non-causal")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, 1.0, 0.01])
+def test_prefill_scale_values(ta, scale):
+    case = W.PrefillCase("scale", B=1, Hq=2, Hkv=2, T=200, D=64, dtype="fp16", causal=True, ragged=False, seed=23)
+    _full_check(ta, case, scale=scale, what=f"scale={scale}")
+
+
+def test_prefill_peaked_scores(ta):
+    """Scores with std ~ 8: the running max moves across tiles (rescaling path)."""
+    import torch
+    case = W.PrefillCase("peaked", B=1, Hq=2, Hkv=1, T=700, D=128, dtype="bf16", causal=True, ragged=False,
+                         seed=24)
+    x = W.prefill_inputs(case)
+    x["q"] = W.round_to(x["q"] * 8.0, "bf16")
+    # make some late keys dominate so the max grows tile after tile
+    x["k"][0, 0, 600:] = W.round_to(x["k"][0, 0, 600:] * 2.0, "bf16")
+    _note("[case] peaked scores")
+    o, lse = _run_prefill(ta, x, case)
+    o_ref, lse_ref = O.prefill(x["q"], x["k"], x["v"], case.scale, True, None)
+    _compare(o, lse, o_ref, lse_ref, "bf16", what="peaked")
+    del torch
+
+
+def test_prefill_gqa_equals_expanded_mha(ta):
+    import torch
+    case = W.PrefillCase("gqa", B=2, Hq=8, Hkv=2, T=257, D=128, dtype="bf16", causal=True, ragged=False, seed=25)
+    x = W.prefill_inputs(case)
+    o1, l1 = _run_prefill(ta, x, case)
+    x2 = dict(x, k=np.repeat(x["k"], 4, axis=1), v=np.repeat(x["v"], 4, axis=1))
+    case2 = W.PrefillCase("mha", B=2, Hq=8, Hkv=8, T=257, D=128, dtype="bf16", causal=True, ragged=False, seed=25)
+    o2, l2 = _run_prefill(ta, x2, case2)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    del torch
+
+
+def test_prefill_deterministic(ta):
+    x = W.prefill_inputs(W.LLAMA)
+    o1, l1 = _run_prefill(ta, x, W.LLAMA)
+    o2, l2 = _run_prefill(ta, x, W.LLAMA)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_ragged_sequence_equals_unpadded_run(ta):
+    case = W.BERT
+    x = W.prefill_inputs(case, nan_padding=True)
+    o, lse = _run_prefill(ta, x, case)
+    b = int(np.argmin(x["seq_lens"]))
+    L = int(x["seq_lens"][b])
+    one = W.PrefillCase("one", B=1, Hq=12, Hkv=12, T=L, D=64, dtype="fp16", causal=False, ragged=False, seed=0)
+    xu = dict(q=x["q"][b:b + 1, :, :L].copy(), k=x["k"][b:b + 1, :, :L].copy(), v=x["v"][b:b + 1, :, :L].copy(),
+              seq_lens=None)
+    ou, lu = _run_prefill(ta, xu, one)
+    assert np.array_equal(o[b, :, :L], ou[0]) and np.array_equal(lse[b, :, :L], lu[0])
+
+
+# ---------------------------------------------------------------- decode edge cases
+@pytest.mark.parametrize("ctx", [[1, 2, 15, 16, 17, 31, 32, 33], [255, 256, 257, 511, 512, 513, 1000, 4096],
+                                 [4096] * 4 + [1] * 4])
+def test_decode_context_edges(ta, ctx):
+    case = W.DecodeCase("edges", B=len(ctx), Hq=12, Hkv=2, D=128, dtype="bf16", ctx_lo=1, ctx_hi=4096, seed=31)
+    _decode_check(ta, case, ctx_lens=ctx, what=f"decode ctx={ctx}")
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,dtype", [(8, 8, 128, "bf16"), (16, 1, 128, "bf16"), (12, 2, 64, "fp16"),
+                                            (32, 8, 128, "fp16"), (5, 1, 64, "bf16")])
+def test_decode_head_layouts(ta, Hq, Hkv, D, dtype):
+    case = W.DecodeCase("heads", B=5, Hq=Hq, Hkv=Hkv, D=D, dtype=dtype, ctx_lo=1, ctx_hi=1500, seed=32)
+    _decode_check(ta, case, what=f"decode Hq={Hq} Hkv={Hkv} D={D} {dtype}")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.09, 0.3])
+def test_decode_scale_values(ta, scale):
+    case = W.DecodeCase("dscale", B=4, Hq=12, Hkv=2, D=128, dtype="bf16", ctx_lo=100, ctx_hi=900, seed=33)
+    _decode_check(ta, case, scale=scale, what=f"decode scale={scale}")
+
+
+def test_decode_equals_last_causal_prefill_row(ta):
+    """Paged decode of context L = last row of a causal prefill over the same keys, gathered contiguously."""
+    import torch
+    case = W.DecodeCase("vs-prefill", B=3, Hq=12, Hkv=2, D=128, dtype="bf16", ctx_lo=300, ctx_hi=700, seed=34)
+    x, o, lse = _decode_check(ta, case, what="decode vs prefill")
+    for b in range(case.B):
+        L = int(x["ctx_lens"][b])
+        K = np.stack([O.gather_paged(x["k_cache"], x["v_cache"], x["block_table"], L, b, h)[0] for h in range(2)])
+        V = np.stack([O.gather_paged(x["k_cache"], x["v_cache"], x["block_table"], L, b, h)[1] for h in range(2)])
+        q = np.zeros((1, 12, L, 128), dtype=np.float32)
+        q[0, :, L - 1] = x["q"][b]
+        pc = W.PrefillCase("p", B=1, Hq=12, Hkv=2, T=L, D=128, dtype="bf16", causal=True, ragged=False, seed=0)
+        op, lp = _run_prefill(ta, dict(q=q, k=K[None].copy(), v=V[None].copy(), seq_lens=None), pc)
+        assert np.abs(op[0, :, L - 1] - o[b]).max() <= 2 * TOL["bf16"]
+        assert np.abs(lp[0, :, L - 1] - lse[b]).max() <= 2 * LSE_REL * max(1.0, np.abs(lse[b]).max())
+    del torch
+
+
+def test_decode_deterministic(ta):
+    x = W.decode_inputs(W.QWEN, nan_fill=True)
+    o1, l1 = _run_decode(ta, x, W.QWEN)
+    o2, l2 = _run_decode(ta, x, W.QWEN)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)

@@ -1,0 +1,163 @@
+"""Python binding of libattn (fused attention for MI355X / gfx950).
+
+Thin ctypes marshalling over the C ABI declared in include/libattn.h: torch
+tensors are checked for device, dtype, shape and contiguity, turned into
+pointers and sizes, and the call is enqueued on torch's current HIP stream.
+Every step of the computation runs in the HIP kernels of libattn.so; there is
+no fallback path. If the shared library is missing, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = ["attn_fwd", "attn_decode_paged", "attn_decode_workspace_bytes", "attn_status_str",
+           "attn_last_error", "AttnError", "lib", "LIB_PATH", "EXPORTS", "BLOCK_SIZE"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+EXPORTS = ("attn_fwd", "attn_decode_paged", "attn_decode_workspace_bytes", "attn_status_str", "attn_last_error")
+BLOCK_SIZE = 16
+
+ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
+ATTN_F16, ATTN_BF16 = 0, 1
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{attn_status_str(status)}: {msg}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libattn.so (built in-tree by tiled_attention_02_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m tiled_attention_02_amd.build` "
+                          "(the HIP library is required; there is no fallback)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, i, vp]
+    L.attn_fwd.restype = i
+    L.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, sz, vp]
+    L.attn_decode_paged.restype = i
+    L.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i]
+    L.attn_decode_workspace_bytes.restype = sz
+    L.attn_status_str.argtypes = [i]
+    L.attn_status_str.restype = ctypes.c_char_p
+    L.attn_last_error.argtypes = []
+    L.attn_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def attn_status_str(status: int) -> str:
+    return lib().attn_status_str(int(status)).decode()
+
+
+def attn_last_error() -> str:
+    return lib().attn_last_error().decode()
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float16:
+        return ATTN_F16
+    raise TypeError(f"libattn takes bfloat16 or float16 tensors, got {t.dtype}")
+
+
+def _check(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _raise(status):
+    if status != ATTN_OK:
+        raise AttnError(status, attn_last_error())
+
+
+def attn_fwd(q, k, v, scale: float | None = None, causal: bool = False, seq_lens=None, out=None, lse=None,
+             need_lse: bool = True):
+    """Fused attention forward. q [B,Hq,Tq,D], k/v [B,Hkv,Tk,D] on the GPU (bf16 or fp16).
+
+    Returns (o [B,Hq,Tq,D] like q, lse [B,Hq,Tq] float32 or None). seq_lens is an
+    int32 device tensor [B] for ragged batches (requires Tq == Tk).
+    """
+    import torch
+    dt = _dtype_code(q)
+    _check(q.is_cuda and k.is_cuda and v.is_cuda, "q, k, v must be GPU tensors")
+    _check(q.dim() == 4 and k.dim() == 4 and v.dim() == 4, "q, k, v must be 4-D [B,H,T,D]")
+    _check(k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v must share a dtype")
+    _check(q.is_contiguous() and k.is_contiguous() and v.is_contiguous(), "q, k, v must be contiguous")
+    B, Hq, Tq, D = q.shape
+    _check(k.shape[0] == B and k.shape[3] == D and v.shape == k.shape, "k/v shape mismatch")
+    Hkv, Tk = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out.shape == q.shape and out.dtype == q.dtype and out.is_contiguous() and out.is_cuda, "bad out")
+    if need_lse and lse is None:
+        lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check(lse.shape == (B, Hq, Tq) and lse.dtype == torch.float32 and lse.is_contiguous(), "bad lse")
+    if seq_lens is not None:
+        _check(seq_lens.is_cuda and seq_lens.dtype == torch.int32 and seq_lens.numel() == B
+               and seq_lens.is_contiguous(), "seq_lens must be a contiguous int32 GPU tensor [B]")
+    st = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Tq, Tk, D,
+                        ctypes.c_float(scale), int(bool(causal)), _ptr(seq_lens), dt, _stream(q.device))
+    _raise(st)
+    return out, lse
+
+
+def attn_decode_workspace_bytes(B: int, Hq: int, D: int, max_blocks_per_seq: int, block_size: int = BLOCK_SIZE):
+    return int(lib().attn_decode_workspace_bytes(B, Hq, D, max_blocks_per_seq, block_size))
+
+
+def attn_decode_paged(q, k_cache, v_cache, block_table, ctx_lens, scale: float | None = None, out=None,
+                      lse=None, workspace=None, need_lse: bool = True):
+    """Paged one-token decode. q [B,Hq,D]; caches [num_blocks,Hkv,16,D]; block_table int32
+    [B,max_blocks]; ctx_lens int32 [B]. Returns (o [B,Hq,D], lse [B,Hq] float32 or None)."""
+    import torch
+    dt = _dtype_code(q)
+    _check(q.dim() == 3 and k_cache.dim() == 4 and v_cache.shape == k_cache.shape, "bad q / cache rank or shape")
+    _check(k_cache.dtype == q.dtype and v_cache.dtype == q.dtype, "q and caches must share a dtype")
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (block_table, "block_table"),
+                 (ctx_lens, "ctx_lens")):
+        _check(t.is_cuda and t.is_contiguous(), f"{n} must be a contiguous GPU tensor")
+    _check(block_table.dtype == torch.int32 and ctx_lens.dtype == torch.int32, "block_table/ctx_lens: int32")
+    B, Hq, D = q.shape
+    NB, Hkv, bs, Dk = k_cache.shape
+    _check(Dk == D, "head size mismatch")
+    _check(block_table.dim() == 2 and block_table.shape[0] == B and ctx_lens.numel() == B, "table shape")
+    maxb = block_table.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if need_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    need = attn_decode_workspace_bytes(B, Hq, D, maxb, bs)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    st = lib().attn_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(ctx_lens),
+                                 _ptr(out), _ptr(lse), B, Hq, Hkv, D, bs, maxb, NB, ctypes.c_float(scale), dt,
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(q.device))
+    _raise(st)
+    return out, lse

@@ -1,0 +1,109 @@
+// Device-side helpers shared by the libattn kernels (gfx950 / CDNA4 only).
+//
+// Operand layouts of the two matrix-core instructions used here (C = A*B,
+// fp32 accumulate, lane l of a 64-wide wavefront, element e of 8):
+//   v_mfma_f32_32x32x16_{bf16,f16}:
+//     A[i = l%32][k = 8*(l/32)+e],  B[k = 8*(l/32)+e][j = l%32]
+//     C register r (16 per lane): row 8*(r/4) + 4*(l/32) + r%4, column l%32
+//   v_mfma_f32_16x16x32_{bf16,f16}:
+//     A[i = l%16][k = 8*(l/16)+e],  B[k = 8*(l/16)+e][j = l%16]
+//     C register r (4 per lane): row 4*(l/16) + r, column l%16
+// Any permutation of the contraction index k applied to both A and B leaves
+// C unchanged; the kernels use that freedom to make every lane's operand one
+// contiguous 16-byte read.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Element-type tags. Storage is raw 16-bit; arithmetic happens in the MFMA
+// (inputs) and in fp32 (everything else).
+struct BF16 {
+  static __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  // two fp32 -> packed pair, round to nearest even (v_cvt_pk_bf16_f32)
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+  }
+  static __device__ __forceinline__ float to_f32(uint16_t x) {
+    return __builtin_bit_cast(float, (uint32_t)x << 16);
+  }
+  // acc + lo + hi of a packed pair (v_dot2c_f32_bf16 against {1, 1}): sums the
+  // rounded values exactly as the matrix core sees them
+  static __device__ __forceinline__ float sum2(uint32_t pk, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), one, acc, false);
+  }
+};
+
+struct F16 {
+  static __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+  }
+  static __device__ __forceinline__ float to_f32(uint16_t x) {
+    return (float)__builtin_bit_cast(_Float16, x);
+  }
+  static __device__ __forceinline__ float sum2(uint32_t pk, float acc) {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk), one, acc, false);
+  }
+};
+
+// Max / sum of a value with the same lane in the other half of the wavefront
+// (lane l <-> lane l^32) through v_permlane32_swap: swap(x, x) returns the
+// lower half's values in r[0] and the upper half's in r[1] on every lane.
+__device__ __forceinline__ float half_swap_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                            __builtin_bit_cast(uint32_t, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                            __builtin_bit_cast(uint32_t, x), false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Byte-select helper (v_perm_b32): result byte i = sel byte i picks from {hi:lo}.
+__device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+// low 16 bits of a and low 16 bits of b -> {b.lo, a.lo}
+__device__ __forceinline__ uint32_t pack_lo16(uint32_t a, uint32_t b) { return perm_b32(b, a, 0x05040100u); }
+// high 16 bits of a and high 16 bits of b -> {b.hi, a.hi}
+__device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) { return perm_b32(b, a, 0x07060302u); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+}  // namespace attn

@@ -1,0 +1,53 @@
+// Internal interface between the C ABI (libattn.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace attn {
+
+// qmode: how the kernels read q so that the exponent factor c is always > 0.
+//   0: as stored (scale > 0), 1: sign flipped (scale < 0, exact in 16-bit),
+//   2: zero (scale == 0: every score is exactly 0).
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int* seq_lens;
+  int B, Hq, Hkv, Tq, Tk;
+  int G;      // Hq / Hkv
+  int nqt;    // number of query tiles (set by the launcher)
+  float c;    // |scale| * log2(e), or 1 when scale == 0
+  int qmode;
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* kc;
+  const void* vc;
+  const int* table;
+  const int* ctx;
+  void* o;
+  float* lse;
+  float* ws;  // per-split partials: [B][Hq][nsplit][D + 2] fp32
+  int B, Hq, Hkv, G, D;
+  int max_blocks;
+  int nsplit;  // maximum number of splits per sequence
+  float c;
+  int qmode;
+};
+
+constexpr int kDecodeBlock = 16;        // tokens per cache block
+constexpr int kSplitBlocks = 16;        // cache blocks per split (256 tokens)
+
+hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int D, bool causal, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, bool bf16, hipStream_t stream);
+
+inline size_t decode_workspace_bytes(int B, int Hq, int D, int max_blocks) {
+  const size_t nsplit = (size_t)(max_blocks + kSplitBlocks - 1) / kSplitBlocks;
+  return (size_t)B * Hq * nsplit * (size_t)(D + 2) * sizeof(float);
+}
+
+}  // namespace attn

@@ -1,0 +1,172 @@
+// C ABI of libattn: argument validation, kernel selection and launch on the
+// caller's stream. Nothing here allocates device memory or synchronises.
+#include "../../include/libattn.h"
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+attn_status fail(attn_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+attn_status fail(attn_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+attn_status ok() {
+  g_err[0] = '\0';
+  return ATTN_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// |scale| * log2(e) and how q must be read so that the factor is positive.
+void scale_mode(float scale, float* c, int* qmode) {
+  if (scale == 0.0f) {
+    *c = 1.0f;
+    *qmode = 2;
+  } else if (scale < 0.0f) {
+    *c = -scale * kLog2e;
+    *qmode = 1;
+  } else {
+    *c = scale * kLog2e;
+    *qmode = 0;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_str(attn_status s) {
+  switch (s) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_ERR_INVALID: return "ATTN_ERR_INVALID";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED";
+    case ATTN_ERR_HIP: return "ATTN_ERR_HIP";
+  }
+  return "ATTN_STATUS_UNKNOWN";
+}
+
+const char* attn_last_error(void) { return g_err; }
+
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                     int Tq, int Tk, int D, float scale, int causal, const int* seq_lens, attn_dtype dtype,
+                     hipStream_t stream) {
+  if (!q || !k || !v || !o) return fail(ATTN_ERR_INVALID, "attn_fwd: q, k, v and o must be non-null");
+  if (B < 1 || Hq < 1 || Hkv < 1 || Tq < 1 || Tk < 1 || D < 1)
+    return fail(ATTN_ERR_INVALID, "attn_fwd: sizes must be >= 1 (B=%d Hq=%d Hkv=%d Tq=%d Tk=%d D=%d)", B, Hq, Hkv,
+                Tq, Tk, D);
+  if (Hq % Hkv != 0) return fail(ATTN_ERR_INVALID, "attn_fwd: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: unknown dtype %d", (int)dtype);
+  if (D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: head size D=%d (supported: 64, 128)", D);
+  if (!isfinite(scale)) return fail(ATTN_ERR_INVALID, "attn_fwd: scale must be finite");
+  if (seq_lens && Tq != Tk)
+    return fail(ATTN_ERR_INVALID, "attn_fwd: seq_lens requires Tq == Tk (got %d, %d)", Tq, Tk);
+  const double nq = (double)B * Hq * Tq * D, nk = (double)B * Hkv * Tk * D;
+  if (nq >= 2147483648.0 || nk >= 2147483648.0)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: tensors must hold fewer than 2^31 elements");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(ATTN_ERR_INVALID, "attn_fwd: q, k, v and o must be 16-byte aligned");
+  if ((lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) || (seq_lens && (reinterpret_cast<uintptr_t>(seq_lens) & 3u)))
+    return fail(ATTN_ERR_INVALID, "attn_fwd: lse / seq_lens must be 4-byte aligned");
+
+  attn::PrefillArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.seq_lens = seq_lens;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Tq = Tq;
+  a.Tk = Tk;
+  a.G = Hq / Hkv;
+  a.nqt = 0;
+  scale_mode(scale, &a.c, &a.qmode);
+  hipError_t e = attn::launch_prefill(a, dtype == ATTN_BF16, D, causal != 0, stream);
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "attn_fwd: launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t attn_decode_workspace_bytes(int B, int Hq, int D, int max_blocks_per_seq, int block_size) {
+  if (B < 1 || Hq < 1 || max_blocks_per_seq < 1 || block_size != attn::kDecodeBlock || (D != 64 && D != 128))
+    return 0;
+  return attn::decode_workspace_bytes(B, Hq, D, max_blocks_per_seq);
+}
+
+attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_cache, const int* block_table,
+                              const int* ctx_lens, void* o, float* lse, int B, int Hq, int Hkv, int D,
+                              int block_size, int max_blocks_per_seq, int num_blocks, float scale,
+                              attn_dtype dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!q || !k_cache || !v_cache || !block_table || !ctx_lens || !o)
+    return fail(ATTN_ERR_INVALID, "attn_decode_paged: q, caches, block_table, ctx_lens and o must be non-null");
+  if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || max_blocks_per_seq < 1 || num_blocks < 1)
+    return fail(ATTN_ERR_INVALID, "attn_decode_paged: sizes must be >= 1");
+  if (Hq % Hkv != 0)
+    return fail(ATTN_ERR_INVALID, "attn_decode_paged: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged: unknown dtype %d", (int)dtype);
+  if (block_size != attn::kDecodeBlock)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged: block_size=%d (supported: 16)", block_size);
+  if (D != 64 && D != 128)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged: head size D=%d (supported: 64, 128)", D);
+  if (Hq / Hkv > 16)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged: group size Hq/Hkv=%d (supported: <= 16)", Hq / Hkv);
+  if (!isfinite(scale)) return fail(ATTN_ERR_INVALID, "attn_decode_paged: scale must be finite");
+  const double ncache = (double)num_blocks * Hkv * block_size * D;
+  if (ncache >= 9.0e18 || (double)B * max_blocks_per_seq >= 2147483648.0)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged: sizes too large");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+    return fail(ATTN_ERR_INVALID, "attn_decode_paged: q, caches and o must be 16-byte aligned");
+  const size_t need = attn::decode_workspace_bytes(B, Hq, D, max_blocks_per_seq);
+  const int nsplit = (max_blocks_per_seq + attn::kSplitBlocks - 1) / attn::kSplitBlocks;
+  if (nsplit > 1) {
+    if (!workspace) return fail(ATTN_ERR_INVALID, "attn_decode_paged: workspace is null (%zu bytes needed)", need);
+    if (workspace_bytes < need)
+      return fail(ATTN_ERR_INVALID, "attn_decode_paged: workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+      return fail(ATTN_ERR_INVALID, "attn_decode_paged: workspace must be 256-byte aligned");
+  }
+  if (nsplit > 65535 || Hkv > 65535 || B > 65535 || Hq > 65535)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged: grid too large (splits=%d Hkv=%d Hq=%d B=%d)", nsplit,
+                Hkv, Hq, B);
+
+  attn::DecodeArgs a;
+  a.q = q;
+  a.kc = k_cache;
+  a.vc = v_cache;
+  a.table = block_table;
+  a.ctx = ctx_lens;
+  a.o = o;
+  a.lse = lse;
+  a.ws = static_cast<float*>(workspace);
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = Hq / Hkv;
+  a.D = D;
+  a.max_blocks = max_blocks_per_seq;
+  a.nsplit = nsplit;
+  scale_mode(scale, &a.c, &a.qmode);
+  hipError_t e = attn::launch_decode(a, dtype == ATTN_BF16, stream);
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "attn_decode_paged: launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"
