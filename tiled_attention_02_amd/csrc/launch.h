@@ -21,6 +21,7 @@ struct PrefillArgs {
   int nqt;    // number of query tiles (set by the launcher)
   float c;    // |scale| * log2(e), or 1 when scale == 0
   int qmode;
+  int xcd_remap;  // set by the launcher: group kv-head siblings on one XCD
 };
 
 struct DecodeArgs {

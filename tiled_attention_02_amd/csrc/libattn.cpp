@@ -98,6 +98,7 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
   a.Tk = Tk;
   a.G = Hq / Hkv;
   a.nqt = 0;
+  a.xcd_remap = 0;
   scale_mode(scale, &a.c, &a.qmode);
   hipError_t e = attn::launch_prefill(a, dtype == ATTN_BF16, D, causal != 0, stream);
   if (e != hipSuccess) return fail(ATTN_ERR_HIP, "attn_fwd: launch failed: %s", hipGetErrorString(e));

@@ -11,17 +11,21 @@
 //
 // Work decomposition. One workgroup of BQ/32 wavefronts owns BQ consecutive
 // query rows of one (batch, query head); each wavefront owns 32 rows. The
-// workgroup streams the key/value rows of its kv head in tiles of BK keys:
-//   * K tile   -> LDS, row-major (row stride D+8 elements),
-//   * V tile   -> LDS, transposed to [D][BK] (row stride BK+8), keys permuted
-//                 inside each 16-key group as [0-3, 8-11, 4-7, 12-15] so that
-//                 every lane's operand of the P.V product is one 16-byte read.
-// Scores are computed transposed, S^T = K Q^T (keys on MFMA rows, the 32
-// queries of a wavefront on columns), so that a lane holds 16 keys of one
-// query per 32-key block: the row max and row sum are in-lane reductions plus
-// one exchange with lane l^32. The transposed scores are, after exp2 and
-// rounding, exactly the B operand of O^T += V^T P^T, so P never leaves the
-// registers. Q^T lives in registers for the whole key loop.
+// workgroup streams the key/value rows of its kv head in tiles of BK keys,
+// double-buffered in LDS: while tile j is consumed, tile j+1 travels from HBM
+// into registers and is written to the other buffer, one barrier per tile.
+// K and V tiles are stored row-major with a 16-byte-chunk XOR swizzle that
+// keeps every LDS access pattern below free of bank conflicts.
+//
+// Scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16: keys on
+// rows, the 32 queries of a wavefront on columns), so a lane holds 16 keys of
+// one query per 32-key block: row max and row sum are in-lane reductions plus
+// one exchange with lane l^32. After exp2 and rounding, the transposed scores
+// are exactly the B operand of O^T += V^T P^T, so P never leaves registers.
+// The V^T operand is read from the row-major V tile with ds_read_b64_tr_b16
+// (gfx950's transposing LDS read: within 16 lanes, lane j receives element
+// j + 16e of the concatenated 4-element chunks the lanes address). Q^T lives
+// in registers for the whole key loop.
 //
 // Online softmax (base 2, x = s * scale * log2 e): per query the running max
 // m, two running sums and the accumulator O^T. O is normalised by the sum of
@@ -38,7 +42,8 @@
 // only on tiles that need it (the causal diagonal, the ragged / Tk tail).
 // Value rows beyond the sequence are zero-filled in LDS so 0 * NaN cannot
 // reach O. Causal tiles entirely above the diagonal are skipped; causal
-// workgroups are issued heaviest (last query tile) first.
+// workgroups are issued heaviest (last query tile) first, and the G query
+// heads that share a kv head are placed on one XCD (one L2) next to each other.
 #include "attn_device.h"
 #include "launch.h"
 
@@ -46,33 +51,52 @@ namespace attn {
 
 constexpr float kLazyRescale = 8.0f;
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// 16-byte chunk slot of (row, chunk c) inside an LDS row: c ^ f(row). The
+// functions are chosen so that the K operand reads (16 rows, one chunk), the
+// transposing V reads (4 rows x 2 chunks per 16 lanes) and the row-major tile
+// writes all hit distinct banks.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 128) return ((row & 7) << 1) | ((row >> 3) & 1);
+  else return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
+}
+
 template <class T, int D, int BQ, int BK, bool CAUSAL>
-__global__ __launch_bounds__(BQ * 2) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(BQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   constexpr int WAVES = BQ / 32;
   constexpr int THREADS = WAVES * 64;
   constexpr int KS = D / 16;   // k-steps of S^T = K Q^T
   constexpr int DB = D / 32;   // 32-row blocks of O^T
   constexpr int KB = BK / 32;  // 32-key blocks of S^T
   constexpr int PS = BK / 16;  // k-steps of O^T += V^T P^T
-  constexpr int KLD = D + 8;   // K tile row stride (elements)
-  constexpr int VLD = BK + 8;  // V^T tile row stride (elements)
+  constexpr int RB = D * 2;    // bytes per tile row
   constexpr int C8 = D / 8;    // 16-byte chunks per row
-  constexpr int TASKS = (BK / 4) * C8;  // a task = 4 consecutive rows x one chunk
-  constexpr int TPT = (TASKS + THREADS - 1) / THREADS;
-  static_assert(BQ % 32 == 0 && BK % 32 == 0 && D % 32 == 0, "tile shape");
+  constexpr int CHUNKS = BK * C8;
+  constexpr int CPT = CHUNKS / THREADS;  // chunks per thread per tile (K and V each)
+  constexpr int TILE = BK * RB;          // bytes of one K or V tile
+  static_assert(BQ % 32 == 0 && BK % 32 == 0 && D % 32 == 0 && CHUNKS % THREADS == 0, "tile shape");
 
-  __shared__ __align__(16) uint16_t Ks[BK * KLD];
-  __shared__ __align__(16) uint16_t Vt[D * VLD];
+  // [buffer][K | V][tile]
+  __shared__ __align__(16) char smem[2 * 2 * TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int h = lane >> 5;   // half of the wavefront
   const int c32 = lane & 31;
+  const int g16 = lane >> 4;  // 16-lane group
+  const int i16 = lane & 15;
 
-  // ---- which tile: heaviest-first for causal; consecutive ids share a kv head
+  // ---- which tile: heaviest-first for causal; G consecutive ids share a kv head
+  int id = blockIdx.x;
+  if (a.xcd_remap) {  // members of a kv-head group land on one XCD (dispatch is round-robin over 8)
+    const int x = id & 7, slot = id >> 3;
+    id = ((slot / a.G) * 8 + x) * a.G + slot % a.G;
+  }
   const int per = a.Hq * a.B;
-  const int id = blockIdx.x;
   const int qt = CAUSAL ? (a.nqt - 1 - id / per) : (id / per);
   const int rem = id % per;
   const int hq = rem % a.Hq;
@@ -123,58 +147,41 @@ __global__ __launch_bounds__(BQ * 2) void prefill_kernel(PrefillArgs a) {
   float l_run = 0.f;   // sum of p in fp32 (for lse)
   float lr_run = 0.f;  // sum of p rounded to the 16-bit type (normalises O)
 
-  // ---- tile staging: global -> registers -> LDS
-  u32x4 kreg[TPT][4], vreg[TPT][4];
+  // ---- tile staging: global -> registers -> LDS (row-major, swizzled)
+  u32x4 kreg[CPT], vreg[CPT];
   auto gload = [&](int kt) {
     const int k0 = kt * BK;
 #pragma unroll
-    for (int i = 0; i < TPT; ++i) {
-      const int task = tid + i * THREADS;
-      if (TASKS % THREADS == 0 || task < TASKS) {
-        const int c = task % C8;
-        const int r0 = (task / C8) * 4;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = k0 + r0 + r;
-          if (key < Lk) {
-            kreg[i][r] = *reinterpret_cast<const u32x4*>(Kg + (size_t)key * D + c * 8);
-            vreg[i][r] = *reinterpret_cast<const u32x4*>(Vg + (size_t)key * D + c * 8);
-          } else {
-            kreg[i][r] = u32x4{0, 0, 0, 0};
-            vreg[i][r] = u32x4{0, 0, 0, 0};
-          }
-        }
+    for (int i = 0; i < CPT; ++i) {
+      const int ch = tid + i * THREADS;
+      const int key = k0 + ch / C8;
+      const int c = ch % C8;
+      if (key < Lk) {
+        kreg[i] = *reinterpret_cast<const u32x4*>(Kg + (size_t)key * D + c * 8);
+        vreg[i] = *reinterpret_cast<const u32x4*>(Vg + (size_t)key * D + c * 8);
+      } else {
+        kreg[i] = u32x4{0, 0, 0, 0};
+        vreg[i] = u32x4{0, 0, 0, 0};
       }
     }
   };
-  auto lds_store = [&]() {
+  auto lds_store = [&](int buf) {
+    char* kt_ = smem + buf * 2 * TILE;
+    char* vt_ = kt_ + TILE;
 #pragma unroll
-    for (int i = 0; i < TPT; ++i) {
-      const int task = tid + i * THREADS;
-      if (TASKS % THREADS == 0 || task < TASKS) {
-        const int c = task % C8;
-        const int r0 = (task / C8) * 4;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          *reinterpret_cast<u32x4*>(&Ks[(r0 + r) * KLD + c * 8]) = kreg[i][r];
-        // 4 rows x 8 columns -> 8 columns x 4 keys (transpose through v_perm)
-        const int g4 = (r0 & 15) >> 2;
-        const int pos = (r0 & ~15) + (((g4 & 1) << 3) | ((g4 >> 1) << 2));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {  // dword e holds columns 2e, 2e+1
-          const uint32_t x0 = vreg[i][0][e], x1 = vreg[i][1][e], x2 = vreg[i][2][e], x3 = vreg[i][3][e];
-          u32x2 lo = {pack_lo16(x0, x1), pack_lo16(x2, x3)};  // column 2e, keys r0..r0+3
-          u32x2 hi = {pack_hi16(x0, x1), pack_hi16(x2, x3)};  // column 2e+1
-          *reinterpret_cast<u32x2*>(&Vt[(c * 8 + 2 * e) * VLD + pos]) = lo;
-          *reinterpret_cast<u32x2*>(&Vt[(c * 8 + 2 * e + 1) * VLD + pos]) = hi;
-        }
-      }
+    for (int i = 0; i < CPT; ++i) {
+      const int ch = tid + i * THREADS;
+      const int r = ch / C8;
+      const int c = ch % C8;
+      const int o = r * RB + 16 * (c ^ swz<D>(r));
+      *reinterpret_cast<u32x4*>(kt_ + o) = kreg[i];
+      *reinterpret_cast<u32x4*>(vt_ + o) = vreg[i];
     }
   };
 
   if (nkt > 0) {
     gload(0);
-    lds_store();
+    lds_store(0);
   }
   __syncthreads();
 
@@ -183,7 +190,10 @@ __global__ __launch_bounds__(BQ * 2) void prefill_kernel(PrefillArgs a) {
 
   for (int kt = 0; kt < nkt; ++kt) {
     const int k0 = kt * BK;
+    const int buf = kt & 1;
     if (kt + 1 < nkt) gload(kt + 1);
+    const char* Ks = smem + buf * 2 * TILE;
+    const char* Vs = Ks + TILE;
 
     // skip tiles entirely above this wavefront's part of the diagonal
     const bool wave_work = wave_live && (!CAUSAL || k0 <= min(w_lo + 31, Lq - 1) + off);
@@ -193,10 +203,12 @@ __global__ __launch_bounds__(BQ * 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         sacc[kb] = f32x16{};
-        const uint16_t* krow = &Ks[(kb * 32 + c32) * KLD + 8 * h];
+        const int row = kb * 32 + c32;
+        const char* krow = Ks + row * RB;
+        const int sw = swz<D>(row);
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-          const u32x4 af = *reinterpret_cast<const u32x4*>(krow + 16 * s);
+          const u32x4 af = *reinterpret_cast<const u32x4*>(krow + 16 * ((2 * s + h) ^ sw));
           sacc[kb] = T::mfma32(af, qf[s], sacc[kb]);
         }
       }
@@ -231,7 +243,7 @@ __global__ __launch_bounds__(BQ * 2) void prefill_kernel(PrefillArgs a) {
         for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
       }
       const float msub = m_run == -__builtin_inff() ? 0.f : m_run;
-      // ---- p = 2^(s*c - m), row sum, pack to the P^T operand
+      // ---- p = 2^(s*c - m), row sums, pack to the P^T operand
       u32x4 pf[PS];
       float lsum = 0.f, lrsum = 0.f;
 #pragma unroll
@@ -246,29 +258,40 @@ __global__ __launch_bounds__(BQ * 2) void prefill_kernel(PrefillArgs a) {
           }
           const u32x4 pk = {T::pack2(p[0], p[1]), T::pack2(p[2], p[3]), T::pack2(p[4], p[5]),
                             T::pack2(p[6], p[7])};
-          // the row sum adds the rounded probabilities the P.V product uses
+          // the normaliser adds the rounded probabilities the P.V product uses
 #pragma unroll
           for (int e = 0; e < 4; ++e) lrsum = T::sum2(pk[e], lrsum);
           pf[kb * 2 + hf] = pk;
         }
       l_run += lsum;
       lr_run += lrsum;
-      // ---- O^T += V^T P^T
+      // ---- O^T += V^T P^T; the V^T operand comes from transposing LDS reads.
+      // k-step s covers keys 16s + 8r + 4h + (0..3) for element group r = 0, 1;
+      // lane i of 16-lane group g addresses row (those keys' base) + i/4 at
+      // columns 32db + 16(g%2) + 4(i%4) and receives column 32db + 16(g%2) + i.
+      const int vrow_l = 4 * h + (i16 >> 2);
+      const int vcol_l = 16 * (g16 & 1) + 4 * (i16 & 3);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const uint16_t* vrow = &Vt[(db * 32 + c32) * VLD + 8 * h];
+        const int col = 32 * db + vcol_l;
 #pragma unroll
         for (int s = 0; s < PS; ++s) {
-          const u32x4 af = *reinterpret_cast<const u32x4*>(vrow + 16 * s);
+          i16x4 part[2];
+#pragma unroll
+          for (int r = 0; r < 2; ++r) {
+            const int row = 16 * s + 8 * r + vrow_l;
+            const int o = row * RB + 16 * ((col >> 3) ^ swz<D>(row)) + 2 * (col & 7);
+            part[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vs + o));
+          }
+          const u32x2 p0 = __builtin_bit_cast(u32x2, part[0]);
+          const u32x2 p1 = __builtin_bit_cast(u32x2, part[1]);
+          const u32x4 af = {p0[0], p0[1], p1[0], p1[1]};
           oacc[db] = T::mfma32(af, pf[s], oacc[db]);
         }
       }
     }
+    if (kt + 1 < nkt) lds_store(buf ^ 1);
     __syncthreads();
-    if (kt + 1 < nkt) {
-      lds_store();
-      __syncthreads();
-    }
   }
 
   // ---- epilogue: O = O^T / l, lse = (m + log2 l) ln 2; padding rows -> 0, -inf
@@ -295,6 +318,7 @@ static hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
   x.nqt = (a.Tq + BQ - 1) / BQ;
   const long long blocks = (long long)x.nqt * a.Hq * a.B;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  x.xcd_remap = (blocks % (8LL * a.G) == 0) ? 1 : 0;
   hipLaunchKernelGGL((prefill_kernel<T, D, BQ, BK, CAUSAL>), dim3((unsigned)blocks), dim3(BQ * 2), 0, stream,
                      x);
   return hipGetLastError();
