@@ -9,13 +9,10 @@
 // section on Flash Attention's role); ragged batches spend no compute on
 // padding (ai-stack.site kernels update, "关键技术点" items 1-2).
 //
-// Work decomposition. One workgroup of BQ/32 wavefronts owns BQ consecutive
-// query rows of one (batch, query head); each wavefront owns 32 rows. The
-// workgroup streams the key/value rows of its kv head in tiles of BK keys,
-// double-buffered in LDS: while tile j is consumed, tile j+1 travels from HBM
-// into registers and is written to the other buffer, one barrier per tile.
-// K and V tiles are stored row-major with a 16-byte-chunk XOR swizzle that
-// keeps every LDS access pattern below free of bank conflicts.
+// Per wavefront: 32 consecutive query rows of one (batch, query head). The
+// workgroup streams the key/value rows of its kv head in tiles of BK keys
+// through LDS (row-major, with a 16-byte-chunk XOR swizzle that keeps every
+// LDS access below free of bank conflicts).
 //
 // Scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16: keys on
 // rows, the 32 queries of a wavefront on columns), so a lane holds 16 keys of
@@ -32,18 +29,25 @@
 // the probabilities after their rounding to the 16-bit input type, i.e. by the
 // very weights the P.V product applies, so O is a weighted mean of value rows
 // (a one-hot row returns its value row exactly); lse uses the fp32 sum of the
-// unrounded probabilities. The max only moves when a tile's max
-// exceeds it by more than kLazyRescale (in log2 units); otherwise p = 2^(x-m)
-// is at most 2^kLazyRescale, which fp32 and the 16-bit P hold without loss of
-// relative precision. O = O^T / l and lse = (m + log2 l) ln 2 are exact
-// rearrangements of the same sums.
+// unrounded probabilities. The max only moves when a tile's max exceeds it by
+// more than kLazyRescale (in log2 units); otherwise p = 2^(x-m) is at most
+// 2^kLazyRescale, which fp32 and the 16-bit P hold without loss of relative
+// precision. O = O^T / l and lse = (m + log2 l) ln 2 are exact rearrangements
+// of the same sums.
 //
 // Masking is a selection of -inf on the raw score (never an addition), and
 // only on tiles that need it (the causal diagonal, the ragged / Tk tail).
 // Value rows beyond the sequence are zero-filled in LDS so 0 * NaN cannot
-// reach O. Causal tiles entirely above the diagonal are skipped; causal
-// workgroups are issued heaviest (last query tile) first, and the G query
-// heads that share a kv head are placed on one XCD (one L2) next to each other.
+// reach O. Causal tiles entirely above a wavefront's diagonal are skipped;
+// causal workgroups are issued heaviest (last query tile) first, and the G
+// query heads that share a kv head are placed on one XCD (one L2) together.
+//
+// Schedule: 4 wavefronts x 32 rows (128 query rows) per workgroup, two
+// workgroups per CU (two wavefronts per SIMD, so one wavefront's MFMAs overlap
+// the other's softmax), K/V tiles double-buffered in LDS with one barrier per
+// tile: tile j+1 travels HBM -> registers while tile j is consumed, then goes
+// to the other LDS buffer. LDS operand reads are issued ahead of the MFMAs
+// that consume them (register double buffering).
 #include "attn_device.h"
 #include "launch.h"
 
@@ -64,33 +68,30 @@ __device__ __forceinline__ int swz(int row) {
   else return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
 }
 
-template <class T, int D, int BQ, int BK, bool CAUSAL>
-__global__ __launch_bounds__(BQ * 2, 2) void prefill_kernel(PrefillArgs a) {
-  constexpr int WAVES = BQ / 32;
-  constexpr int THREADS = WAVES * 64;
-  constexpr int KS = D / 16;   // k-steps of S^T = K Q^T
-  constexpr int DB = D / 32;   // 32-row blocks of O^T
-  constexpr int KB = BK / 32;  // 32-key blocks of S^T
-  constexpr int PS = BK / 16;  // k-steps of O^T += V^T P^T
-  constexpr int RB = D * 2;    // bytes per tile row
-  constexpr int C8 = D / 8;    // 16-byte chunks per row
-  constexpr int CHUNKS = BK * C8;
-  constexpr int CPT = CHUNKS / THREADS;  // chunks per thread per tile (K and V each)
-  constexpr int TILE = BK * RB;          // bytes of one K or V tile
-  static_assert(BQ % 32 == 0 && BK % 32 == 0 && D % 32 == 0 && CHUNKS % THREADS == 0, "tile shape");
+template <int D, int BK>
+struct Shape {
+  static constexpr int KS = D / 16;   // k-steps of S^T = K Q^T
+  static constexpr int DB = D / 32;   // 32-row blocks of O^T
+  static constexpr int KB = BK / 32;  // 32-key blocks of S^T
+  static constexpr int PS = BK / 16;  // k-steps of O^T += V^T P^T
+  static constexpr int RB = D * 2;    // bytes per tile row
+  static constexpr int C8 = D / 8;    // 16-byte chunks per row
+  static constexpr int TILE = BK * RB;
+};
 
-  // [buffer][K | V][tile]
-  __shared__ __align__(16) char smem[2 * 2 * TILE];
+// Which (batch, head, query tile) this workgroup owns, and its bounds.
+struct Geo {
+  int b, hq, kvh, Lq, Lk, off, q_lo, nkt;
+  const uint16_t* Qg;
+  const uint16_t* Kg;
+  const uint16_t* Vg;
+  uint16_t* Og;
+  float* Lg;
+};
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int h = lane >> 5;   // half of the wavefront
-  const int c32 = lane & 31;
-  const int g16 = lane >> 4;  // 16-lane group
-  const int i16 = lane & 15;
-
-  // ---- which tile: heaviest-first for causal; G consecutive ids share a kv head
+template <int D, int BQ, int BK, bool CAUSAL>
+__device__ __forceinline__ Geo make_geo(const PrefillArgs& a) {
+  Geo g;
   int id = blockIdx.x;
   if (a.xcd_remap) {  // members of a kv-head group land on one XCD (dispatch is round-robin over 8)
     const int x = id & 7, slot = id >> 3;
@@ -99,237 +100,343 @@ __global__ __launch_bounds__(BQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   const int per = a.Hq * a.B;
   const int qt = CAUSAL ? (a.nqt - 1 - id / per) : (id / per);
   const int rem = id % per;
-  const int hq = rem % a.Hq;
-  const int b = rem / a.Hq;
-  const int kvh = hq / a.G;
-
-  int Lq = a.Tq, Lk = a.Tk;
+  g.hq = rem % a.Hq;
+  g.b = rem / a.Hq;
+  g.kvh = g.hq / a.G;
+  g.Lq = a.Tq;
+  g.Lk = a.Tk;
   if (a.seq_lens) {
-    Lq = a.seq_lens[b];
-    Lk = Lq;
+    g.Lq = a.seq_lens[g.b];
+    g.Lk = g.Lq;
   }
-  const int off = Lk - Lq;  // bottom-right causal alignment
-  const int q_lo = qt * BQ;
-
-  const uint16_t* Qg = static_cast<const uint16_t*>(a.q) + (size_t)(b * a.Hq + hq) * a.Tq * D;
-  const uint16_t* Kg = static_cast<const uint16_t*>(a.k) + (size_t)(b * a.Hkv + kvh) * a.Tk * D;
-  const uint16_t* Vg = static_cast<const uint16_t*>(a.v) + (size_t)(b * a.Hkv + kvh) * a.Tk * D;
-  uint16_t* Og = static_cast<uint16_t*>(a.o) + (size_t)(b * a.Hq + hq) * a.Tq * D;
-  float* Lg = a.lse ? a.lse + (size_t)(b * a.Hq + hq) * a.Tq : nullptr;
-
-  // exclusive key bound of the whole tile
-  int kend = Lk;
-  if (CAUSAL) kend = min(Lk, min(q_lo + BQ, Lq) + off);
-  const int nkt = (q_lo < Lq && kend > 0) ? (kend + BK - 1) / BK : 0;
-
-  const int qrow = q_lo + w * 32 + c32;  // this lane's query row
-  const int w_lo = q_lo + w * 32;        // first row of this wavefront
-
-  // ---- Q^T fragments (B operand): lane holds Q[qrow][16s + 8h .. +8)
-  u32x4 qf[KS];
-  {
-    const bool live = qrow < Lq;
-    const uint32_t flip = a.qmode == 1 ? 0x80008000u : 0u;
-    const bool zero = a.qmode == 2 || !live;
-    const u32x4* src = reinterpret_cast<const u32x4*>(Qg + (size_t)(live ? qrow : 0) * D + 8 * h);
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      u32x4 x = src[2 * s];
-      x ^= flip;
-      qf[s] = zero ? u32x4{0, 0, 0, 0} : x;
-    }
-  }
-
-  f32x16 oacc[DB];
-#pragma unroll
-  for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
-  float m_run = -__builtin_inff();
-  float l_run = 0.f;   // sum of p in fp32 (for lse)
-  float lr_run = 0.f;  // sum of p rounded to the 16-bit type (normalises O)
-
-  // ---- tile staging: global -> registers -> LDS (row-major, swizzled)
-  u32x4 kreg[CPT], vreg[CPT];
-  auto gload = [&](int kt) {
-    const int k0 = kt * BK;
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int ch = tid + i * THREADS;
-      const int key = k0 + ch / C8;
-      const int c = ch % C8;
-      if (key < Lk) {
-        kreg[i] = *reinterpret_cast<const u32x4*>(Kg + (size_t)key * D + c * 8);
-        vreg[i] = *reinterpret_cast<const u32x4*>(Vg + (size_t)key * D + c * 8);
-      } else {
-        kreg[i] = u32x4{0, 0, 0, 0};
-        vreg[i] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto lds_store = [&](int buf) {
-    char* kt_ = smem + buf * 2 * TILE;
-    char* vt_ = kt_ + TILE;
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int ch = tid + i * THREADS;
-      const int r = ch / C8;
-      const int c = ch % C8;
-      const int o = r * RB + 16 * (c ^ swz<D>(r));
-      *reinterpret_cast<u32x4*>(kt_ + o) = kreg[i];
-      *reinterpret_cast<u32x4*>(vt_ + o) = vreg[i];
-    }
-  };
-
-  if (nkt > 0) {
-    gload(0);
-    lds_store(0);
-  }
-  __syncthreads();
-
-  const float cexp = a.c;  // scale * log2(e) > 0
-  const bool wave_live = w_lo < Lq;
-
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int k0 = kt * BK;
-    const int buf = kt & 1;
-    if (kt + 1 < nkt) gload(kt + 1);
-    const char* Ks = smem + buf * 2 * TILE;
-    const char* Vs = Ks + TILE;
-
-    // skip tiles entirely above this wavefront's part of the diagonal
-    const bool wave_work = wave_live && (!CAUSAL || k0 <= min(w_lo + 31, Lq - 1) + off);
-    if (wave_work) {
-      // ---- S^T = K Q^T
-      f32x16 sacc[KB];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        sacc[kb] = f32x16{};
-        const int row = kb * 32 + c32;
-        const char* krow = Ks + row * RB;
-        const int sw = swz<D>(row);
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const u32x4 af = *reinterpret_cast<const u32x4*>(krow + 16 * ((2 * s + h) ^ sw));
-          sacc[kb] = T::mfma32(af, qf[s], sacc[kb]);
-        }
-      }
-      // ---- mask (selection) where the tile crosses the diagonal or the tail
-      const bool need_mask = (k0 + BK > Lk) || (CAUSAL && k0 + BK - 1 > w_lo + off);
-      if (need_mask) {
-        const int lim = CAUSAL ? min(Lk - 1, qrow + off) : (Lk - 1);
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            sacc[kb][r] = key > lim ? -__builtin_inff() : sacc[kb][r];
-          }
-      }
-      // ---- tile max (raw scores; cexp > 0)
-      float mx = sacc[0][0];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-      mx = half_swap_max(mx) * cexp;  // -inf stays -inf (cexp > 0)
-      // ---- lazy rescale: move m only when the max grows by more than the margin
-      const bool grow = mx > m_run + kLazyRescale;
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float m_new = grow ? mx : m_run;
-        const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;  // m_run=-inf -> 0
-        m_run = m_new;
-        l_run *= alpha;
-        lr_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
-      }
-      const float msub = m_run == -__builtin_inff() ? 0.f : m_run;
-      // ---- p = 2^(s*c - m), row sums, pack to the P^T operand
-      u32x4 pf[PS];
-      float lsum = 0.f, lrsum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          float p[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            p[e] = fast_exp2(__builtin_fmaf(sacc[kb][8 * hf + e], cexp, -msub));
-            lsum += p[e];
-          }
-          const u32x4 pk = {T::pack2(p[0], p[1]), T::pack2(p[2], p[3]), T::pack2(p[4], p[5]),
-                            T::pack2(p[6], p[7])};
-          // the normaliser adds the rounded probabilities the P.V product uses
-#pragma unroll
-          for (int e = 0; e < 4; ++e) lrsum = T::sum2(pk[e], lrsum);
-          pf[kb * 2 + hf] = pk;
-        }
-      l_run += lsum;
-      lr_run += lrsum;
-      // ---- O^T += V^T P^T; the V^T operand comes from transposing LDS reads.
-      // k-step s covers keys 16s + 8r + 4h + (0..3) for element group r = 0, 1;
-      // lane i of 16-lane group g addresses row (those keys' base) + i/4 at
-      // columns 32db + 16(g%2) + 4(i%4) and receives column 32db + 16(g%2) + i.
-      const int vrow_l = 4 * h + (i16 >> 2);
-      const int vcol_l = 16 * (g16 & 1) + 4 * (i16 & 3);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int col = 32 * db + vcol_l;
-#pragma unroll
-        for (int s = 0; s < PS; ++s) {
-          i16x4 part[2];
-#pragma unroll
-          for (int r = 0; r < 2; ++r) {
-            const int row = 16 * s + 8 * r + vrow_l;
-            const int o = row * RB + 16 * ((col >> 3) ^ swz<D>(row)) + 2 * (col & 7);
-            part[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vs + o));
-          }
-          const u32x2 p0 = __builtin_bit_cast(u32x2, part[0]);
-          const u32x2 p1 = __builtin_bit_cast(u32x2, part[1]);
-          const u32x4 af = {p0[0], p0[1], p1[0], p1[1]};
-          oacc[db] = T::mfma32(af, pf[s], oacc[db]);
-        }
-      }
-    }
-    if (kt + 1 < nkt) lds_store(buf ^ 1);
-    __syncthreads();
-  }
-
-  // ---- epilogue: O = O^T / l, lse = (m + log2 l) ln 2; padding rows -> 0, -inf
-  const float l_tot = half_swap_sum(l_run);
-  const float lr_tot = half_swap_sum(lr_run);
-  if (qrow >= a.Tq) return;
-  const bool has = qrow < Lq && l_tot > 0.f;
-  const float inv = has ? 1.f / lr_tot : 0.f;
-  uint16_t* orow = Og + (size_t)qrow * D + 4 * h;
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      u32x2 pk = {T::pack2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv),
-                  T::pack2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
-      *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * g) = pk;
-    }
-  if (Lg && h == 0) Lg[qrow] = has ? (m_run + fast_log2(l_tot)) * kLn2 : -__builtin_inff();
+  g.off = g.Lk - g.Lq;  // bottom-right causal alignment
+  g.q_lo = qt * BQ;
+  g.Qg = static_cast<const uint16_t*>(a.q) + (size_t)(g.b * a.Hq + g.hq) * a.Tq * D;
+  g.Kg = static_cast<const uint16_t*>(a.k) + (size_t)(g.b * a.Hkv + g.kvh) * a.Tk * D;
+  g.Vg = static_cast<const uint16_t*>(a.v) + (size_t)(g.b * a.Hkv + g.kvh) * a.Tk * D;
+  g.Og = static_cast<uint16_t*>(a.o) + (size_t)(g.b * a.Hq + g.hq) * a.Tq * D;
+  g.Lg = a.lse ? a.lse + (size_t)(g.b * a.Hq + g.hq) * a.Tq : nullptr;
+  int kend = g.Lk;  // exclusive key bound of the whole tile
+  if (CAUSAL) kend = min(g.Lk, min(g.q_lo + BQ, g.Lq) + g.off);
+  g.nkt = (g.q_lo < g.Lq && kend > 0) ? (kend + BK - 1) / BK : 0;
+  return g;
 }
 
+// Per-wavefront accumulator state.
+template <int D>
+struct Acc {
+  u32x4 qf[D / 16];    // Q^T fragments (B operand): lane holds Q[qrow][16s + 8h .. +8)
+  f32x16 oacc[D / 32];
+  float m, l, lr;      // running max (log2 units), fp32 sum, sum of the rounded p
+};
+
+template <int D>
+__device__ __forceinline__ void load_q(Acc<D>& st, const Geo& g, int qmode, int qrow, int h) {
+  const bool live = qrow < g.Lq;
+  const uint32_t flip = qmode == 1 ? 0x80008000u : 0u;
+  const bool zero = qmode == 2 || !live;
+  const u32x4* src = reinterpret_cast<const u32x4*>(g.Qg + (size_t)(live ? qrow : 0) * D + 8 * h);
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    u32x4 x = src[2 * s];
+    x ^= flip;
+    st.qf[s] = zero ? u32x4{0, 0, 0, 0} : x;
+  }
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) st.oacc[i] = f32x16{};
+  st.m = -__builtin_inff();
+  st.l = 0.f;
+  st.lr = 0.f;
+}
+
+// Per-lane LDS read offsets (identical for every tile).
+template <int D, int BK>
+struct Offs {
+  int k[D / 16];
+  int v[D / 32][2];
+};
+
+template <int D, int BK>
+__device__ __forceinline__ void make_offs(Offs<D, BK>& o, int lane) {
+  using S = Shape<D, BK>;
+  const int h = lane >> 5, c32 = lane & 31, g16 = lane >> 4, i16 = lane & 15;
+  // K operand of k-step s: row kb*32 + c32, chunk (2s + h) ^ swz(row); swz(row)
+  // does not depend on kb because kb*32 is a multiple of 16.
+  const int sw = swz<D>(c32);
+#pragma unroll
+  for (int s = 0; s < S::KS; ++s) o.k[s] = c32 * S::RB + 16 * ((2 * s + h) ^ sw);
+  // V^T operand: k-step s covers keys 16s + 8r + 4h + (0..3) for element group
+  // r = 0, 1; lane i of 16-lane group g addresses row (those keys' base) + i/4
+  // at columns 32db + 16(g%2) + 4(i%4) and receives column 32db + 16(g%2) + i.
+  // The swizzle of row 16s + 8r + vr depends only on r and the lane (16s + 8r
+  // is a multiple of 8), so the offset is v[db][r] + 16s * RB.
+  const int vr = 4 * h + (i16 >> 2);
+  const int vc = 16 * (g16 & 1) + 4 * (i16 & 3);
+#pragma unroll
+  for (int db = 0; db < S::DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int row = 8 * r + vr;
+      const int col = 32 * db + vc;
+      o.v[db][r] = row * S::RB + 16 * ((col >> 3) ^ swz<D>(row)) + 2 * (col & 7);
+    }
+}
+
+// S^T = K Q^T for one tile in LDS. The K fragments of k-step s+2 are read
+// while the MFMAs of step s run (a three-deep register ring).
+template <class T, int D, int BK>
+__device__ __forceinline__ void tile_qk(f32x16 (&sacc)[BK / 32], const char* Ks, const Offs<D, BK>& o,
+                                        const Acc<D>& st) {
+  using S = Shape<D, BK>;
+  constexpr int DEPTH = 2;
+  u32x4 fr[DEPTH + 1][S::KB];
+#pragma unroll
+  for (int kb = 0; kb < S::KB; ++kb) sacc[kb] = f32x16{};
+#pragma unroll
+  for (int s = 0; s < DEPTH; ++s)
+#pragma unroll
+    for (int kb = 0; kb < S::KB; ++kb)
+      fr[s][kb] = *reinterpret_cast<const u32x4*>(Ks + kb * 32 * S::RB + o.k[s]);
+#pragma unroll
+  for (int s = 0; s < S::KS; ++s) {
+    if (s + DEPTH < S::KS) {
+#pragma unroll
+      for (int kb = 0; kb < S::KB; ++kb)
+        fr[(s + DEPTH) % (DEPTH + 1)][kb] = *reinterpret_cast<const u32x4*>(Ks + kb * 32 * S::RB + o.k[s + DEPTH]);
+    }
+#pragma unroll
+    for (int kb = 0; kb < S::KB; ++kb) sacc[kb] = T::mfma32(fr[s % (DEPTH + 1)][kb], st.qf[s], sacc[kb]);
+  }
+  // schedule: the reads of step s+DEPTH go out before the MFMAs of step s
+  __builtin_amdgcn_sched_group_barrier(0x100, DEPTH * S::KB, 0);
+#pragma unroll
+  for (int s = 0; s < S::KS; ++s) {
+    if (s + DEPTH < S::KS) __builtin_amdgcn_sched_group_barrier(0x100, S::KB, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, S::KB, 0);
+  }
+}
+
+// Two transposing reads give the 8-element V^T operand of one MFMA.
+template <int D, int BK>
+__device__ __forceinline__ u32x4 vt_frag(const char* Vs, const Offs<D, BK>& o, int db, int s) {
+  using S = Shape<D, BK>;
+  const i16x4 p0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vs + 16 * s * S::RB + o.v[db][0]));
+  const i16x4 p1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vs + 16 * s * S::RB + o.v[db][1]));
+  const u32x2 a0 = __builtin_bit_cast(u32x2, p0);
+  const u32x2 a1 = __builtin_bit_cast(u32x2, p1);
+  return u32x4{a0[0], a0[1], a1[0], a1[1]};
+}
+
+// O^T += V^T P^T for one tile in LDS; fragments of k-step s+1 are read while
+// the DB independent MFMAs of step s run.
+template <class T, int D, int BK>
+__device__ __forceinline__ void tile_pv(Acc<D>& st, const u32x4 (&pf)[BK / 16], const char* Vs,
+                                        const Offs<D, BK>& o) {
+  using S = Shape<D, BK>;
+  u32x4 fr[2][S::DB];
+#pragma unroll
+  for (int db = 0; db < S::DB; ++db) fr[0][db] = vt_frag<D, BK>(Vs, o, db, 0);
+#pragma unroll
+  for (int s = 0; s < S::PS; ++s) {
+    if (s + 1 < S::PS) {
+#pragma unroll
+      for (int db = 0; db < S::DB; ++db) fr[(s + 1) & 1][db] = vt_frag<D, BK>(Vs, o, db, s + 1);
+    }
+#pragma unroll
+    for (int db = 0; db < S::DB; ++db) st.oacc[db] = T::mfma32(fr[s & 1][db], pf[s], st.oacc[db]);
+  }
+}
+
+// Mask, online-softmax update and P^T operand for one tile of scores.
+template <class T, int D, int BK, bool CAUSAL>
+__device__ __forceinline__ void tile_softmax(f32x16 (&sacc)[BK / 32], u32x4 (&pf)[BK / 16], Acc<D>& st,
+                                             const Geo& g, int k0, int qrow, int w_lo, int h, float cexp) {
+  using S = Shape<D, BK>;
+  const bool need_mask = (k0 + BK > g.Lk) || (CAUSAL && k0 + BK - 1 > w_lo + g.off);
+  if (need_mask) {
+    const int lim = CAUSAL ? min(g.Lk - 1, qrow + g.off) : (g.Lk - 1);
+#pragma unroll
+    for (int kb = 0; kb < S::KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        sacc[kb][r] = key > lim ? -__builtin_inff() : sacc[kb][r];
+      }
+  }
+  // tile max (raw scores; cexp > 0)
+  float mx = sacc[0][0];
+#pragma unroll
+  for (int kb = 0; kb < S::KB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+  mx = half_swap_max(mx) * cexp;  // -inf stays -inf (cexp > 0)
+  // lazy rescale: move m only when the max grows by more than the margin
+  const bool grow = mx > st.m + kLazyRescale;
+  if (__builtin_amdgcn_ballot_w64(grow)) {
+    const float m_new = grow ? mx : st.m;
+    const float alpha = grow ? fast_exp2(st.m - m_new) : 1.f;  // m = -inf -> 0
+    st.m = m_new;
+    st.l *= alpha;
+    st.lr *= alpha;
+#pragma unroll
+    for (int i = 0; i < S::DB; ++i) st.oacc[i] *= alpha;
+  }
+  const float msub = st.m == -__builtin_inff() ? 0.f : st.m;
+  // p = 2^(s*c - m), row sums, pack to the P^T operand
+  float lsum = 0.f, lrsum = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < S::KB; ++kb)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = fast_exp2(__builtin_fmaf(sacc[kb][8 * hf + e], cexp, -msub));
+        lsum += p[e];
+      }
+      const u32x4 pk = {T::pack2(p[0], p[1]), T::pack2(p[2], p[3]), T::pack2(p[4], p[5]), T::pack2(p[6], p[7])};
+      // the normaliser adds the rounded probabilities the P.V product uses
+#pragma unroll
+      for (int e = 0; e < 4; ++e) lrsum = T::sum2(pk[e], lrsum);
+      pf[kb * 2 + hf] = pk;
+    }
+  st.l += lsum;
+  st.lr += lrsum;
+}
+
+// O = O^T / l, lse = (m + log2 l) ln 2; padding rows -> 0, -inf.
+template <class T, int D>
+__device__ __forceinline__ void epilogue(const Acc<D>& st, const Geo& g, int Tq, int qrow, int h) {
+  const float l_tot = half_swap_sum(st.l);
+  const float lr_tot = half_swap_sum(st.lr);
+  if (qrow >= Tq) return;
+  const bool has = qrow < g.Lq && l_tot > 0.f;
+  const float inv = has ? 1.f / lr_tot : 0.f;
+  uint16_t* orow = g.Og + (size_t)qrow * D + 4 * h;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      u32x2 pk = {T::pack2(st.oacc[db][4 * q4 + 0] * inv, st.oacc[db][4 * q4 + 1] * inv),
+                  T::pack2(st.oacc[db][4 * q4 + 2] * inv, st.oacc[db][4 * q4 + 3] * inv)};
+      *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * q4) = pk;
+    }
+  if (g.Lg && h == 0) g.Lg[qrow] = has ? (st.m + fast_log2(l_tot)) * kLn2 : -__builtin_inff();
+}
+
+// Global -> register -> LDS staging of K or V tiles (row-major, swizzled).
+// Thread tid stages chunks tid + i*THREADS: row ch / C8, 16-byte chunk ch % C8.
+template <int D, int BK, int THREADS>
+struct Stager {
+  using S = Shape<D, BK>;
+  static constexpr int CPT = BK * S::C8 / THREADS;
+  static constexpr int RPP = THREADS / S::C8;  // rows per pass
+  static_assert(CPT >= 1 && BK * S::C8 % THREADS == 0, "staging shape");
+  int row0;
+  int off[CPT];
+  u32x4 reg[CPT];
+  const uint16_t* src;
+
+  __device__ __forceinline__ void init(const uint16_t* base, int tid) {
+    row0 = tid / S::C8;
+    const int c = tid % S::C8;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int r = row0 + i * RPP;
+      off[i] = r * S::RB + 16 * (c ^ swz<D>(r));
+    }
+    src = base + (size_t)row0 * D + c * 8;
+  }
+  __device__ __forceinline__ void load(int kt, int Lk) {
+    const int k0 = kt * BK;
+    if (k0 + BK <= Lk) {  // full tile: plain loads
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) reg[i] = *reinterpret_cast<const u32x4*>(src + (size_t)(k0 + i * RPP) * D);
+    } else {  // tail tile: rows beyond the sequence are zero
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        reg[i] = u32x4{0, 0, 0, 0};
+        if (k0 + row0 + i * RPP < Lk) reg[i] = *reinterpret_cast<const u32x4*>(src + (size_t)(k0 + i * RPP) * D);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(char* tile) const {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) *reinterpret_cast<u32x4*>(tile + off[i]) = reg[i];
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Small grids: 4 wavefronts x 32 rows, double-buffered K/V tiles.
 template <class T, int D, int BQ, int BK, bool CAUSAL>
-static hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
+__global__ __launch_bounds__(BQ * 2, 2) void prefill_kernel(PrefillArgs a) {
+  using S = Shape<D, BK>;
+  constexpr int THREADS = (BQ / 32) * 64;
+  __shared__ __align__(16) char smem[2 * 2 * S::TILE];  // [buffer][K | V]
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5;
+  const Geo g = make_geo<D, BQ, BK, CAUSAL>(a);
+  const int w_lo = g.q_lo + w * 32;
+  const int qrow = w_lo + (lane & 31);
+  Acc<D> st;
+  load_q(st, g, a.qmode, qrow, h);
+  Offs<D, BK> o;
+  make_offs(o, lane);
+  Stager<D, BK, THREADS> ks, vs;
+  ks.init(g.Kg, tid);
+  vs.init(g.Vg, tid);
+
+  if (g.nkt > 0) {
+    ks.load(0, g.Lk);
+    vs.load(0, g.Lk);
+    ks.store(smem);
+    vs.store(smem + S::TILE);
+  }
+  __syncthreads();
+  const bool wave_live = w_lo < g.Lq;
+  for (int kt = 0; kt < g.nkt; ++kt) {
+    const int k0 = kt * BK;
+    const int buf = kt & 1;
+    if (kt + 1 < g.nkt) {
+      ks.load(kt + 1, g.Lk);
+      vs.load(kt + 1, g.Lk);
+    }
+    const char* Ks = smem + buf * 2 * S::TILE;
+    const char* Vs = Ks + S::TILE;
+    // skip tiles entirely above this wavefront's part of the diagonal
+    if (wave_live && (!CAUSAL || k0 <= min(w_lo + 31, g.Lq - 1) + g.off)) {
+      f32x16 sacc[S::KB];
+      u32x4 pf[S::PS];
+      tile_qk<T, D, BK>(sacc, Ks, o, st);
+      tile_softmax<T, D, BK, CAUSAL>(sacc, pf, st, g, k0, qrow, w_lo, h, a.c);
+      tile_pv<T, D, BK>(st, pf, Vs, o);
+    }
+    if (kt + 1 < g.nkt) {
+      char* nb = smem + (buf ^ 1) * 2 * S::TILE;
+      ks.store(nb);
+      vs.store(nb + S::TILE);
+    }
+    __syncthreads();
+  }
+  epilogue<T, D>(st, g, a.Tq, qrow, h);
+}
+
+// ---------------------------------------------------------------------------
+template <class T, int D, int BK, bool CAUSAL>
+static hipError_t launch_D(const PrefillArgs& a, hipStream_t stream) {
   PrefillArgs x = a;
-  x.nqt = (a.Tq + BQ - 1) / BQ;
+  x.nqt = (a.Tq + 127) / 128;
   const long long blocks = (long long)x.nqt * a.Hq * a.B;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   x.xcd_remap = (blocks % (8LL * a.G) == 0) ? 1 : 0;
-  hipLaunchKernelGGL((prefill_kernel<T, D, BQ, BK, CAUSAL>), dim3((unsigned)blocks), dim3(BQ * 2), 0, stream,
-                     x);
+  hipLaunchKernelGGL((prefill_kernel<T, D, 128, BK, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, stream, x);
   return hipGetLastError();
 }
 
 template <class T>
 static hipError_t launch_t(const PrefillArgs& a, int D, bool causal, hipStream_t stream) {
-  if (D == 128) {
-    return causal ? launch_one<T, 128, 128, 64, true>(a, stream) : launch_one<T, 128, 128, 64, false>(a, stream);
-  }
-  return causal ? launch_one<T, 64, 128, 128, true>(a, stream) : launch_one<T, 64, 128, 128, false>(a, stream);
+  if (D == 128) return causal ? launch_D<T, 128, 64, true>(a, stream) : launch_D<T, 128, 64, false>(a, stream);
+  return causal ? launch_D<T, 64, 128, true>(a, stream) : launch_D<T, 64, 128, false>(a, stream);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int D, bool causal, hipStream_t stream) {
