@@ -100,11 +100,12 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
  *  lse         : [B, Hq] fp32 natural-log log-sum-exp; may be NULL.
  *  block_size == 16, D in {64, 128}, Hq % Hkv == 0, Hq / Hkv <= 16.
  *  workspace   : device scratch of at least attn_decode_workspace_bytes(...)
- *                bytes, 256-byte aligned, owned by the caller; it holds the
- *                per-split partial results (the key range of a long context is
- *                split across workgroups and merged in a second pass).
- *                Contents on entry are ignored; calls that share a workspace
- *                must be ordered on one stream.
+ *                bytes, 256-byte aligned, owned by the caller; contents on
+ *                entry are ignored. A long context is split into ranges of 256
+ *                tokens handled by different workgroups; the workspace holds
+ *                their partial results until a second kernel merges them.
+ *                Calls that share a workspace must be ordered on one stream.
+ *                May be NULL when max_blocks_per_seq <= 16 (one range only).
  */
 attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                               const int* block_table, const int* ctx_lens, void* o, float* lse,
@@ -114,7 +115,7 @@ attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_
                               hipStream_t stream);
 
 /* Workspace bytes attn_decode_paged needs for these sizes (0 if they are invalid). */
-size_t attn_decode_workspace_bytes(int B, int Hq, int D, int max_blocks_per_seq, int block_size);
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_blocks_per_seq, int block_size);
 
 /* Static, human-readable name of a status code. */
 const char* attn_status_str(attn_status s);

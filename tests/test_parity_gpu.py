@@ -279,3 +279,28 @@ def test_decode_deterministic(ta):
     o1, l1 = _run_decode(ta, x, W.QWEN)
     o2, l2 = _run_decode(ta, x, W.QWEN)
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_decode_explicit_workspace_reused_across_shapes(ta):
+    """One caller-owned workspace, never cleared, reused by calls of different
+    shapes (its contents on entry are ignored); every call matches the oracle."""
+    import torch
+    cases = [W.DecodeCase("ws-a", B=4, Hq=12, Hkv=2, D=128, dtype="bf16", ctx_lo=600, ctx_hi=2000, seed=41),
+             W.DecodeCase("ws-b", B=24, Hq=8, Hkv=4, D=64, dtype="fp16", ctx_lo=300, ctx_hi=3000, seed=42),
+             W.DecodeCase("ws-c", B=3, Hq=16, Hkv=1, D=128, dtype="bf16", ctx_lo=1000, ctx_hi=4000, seed=43),
+             W.DecodeCase("ws-b2", B=24, Hq=8, Hkv=4, D=64, dtype="fp16", ctx_lo=300, ctx_hi=3000, seed=44)]
+    size = max(ta.attn_decode_workspace_bytes(c.B, c.Hq, c.Hkv, c.D, (c.ctx_hi + 15) // 16) for c in cases)
+    ws = torch.full((size,), 0x7f, dtype=torch.uint8, device="cuda")  # garbage on entry
+    for c in cases:
+        x = W.decode_inputs(c, nan_fill=True)
+        _note(f"[case] workspace {c.name} B={c.B} Hkv={c.Hkv} maxb={x['block_table'].shape[1]}")
+        q = _dev(x["q"], c.dtype)
+        kc = _dev(x["k_cache"], c.dtype)
+        vc = _dev(x["v_cache"], c.dtype)
+        bt = torch.from_numpy(x["block_table"]).cuda()
+        cl = torch.from_numpy(x["ctx_lens"]).cuda()
+        assert x["block_table"].shape[1] > 16  # several 256-token ranges per sequence
+        o, lse = ta.attn_decode_paged(q, kc, vc, bt, cl, scale=c.scale, workspace=ws)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = O.decode_paged(x["q"], x["k_cache"], x["v_cache"], x["block_table"], x["ctx_lens"], c.scale)
+        _compare(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, c.dtype, what=c.name)

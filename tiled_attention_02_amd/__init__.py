@@ -13,7 +13,7 @@ import math
 import os
 
 __all__ = ["attn_fwd", "attn_decode_paged", "attn_decode_workspace_bytes", "attn_status_str",
-           "attn_last_error", "AttnError", "lib", "LIB_PATH", "EXPORTS", "BLOCK_SIZE"]
+           "attn_last_error", "AttnError", "lib", "LIB_PATH", "EXPORTS", "BLOCK_SIZE", "decode_workspace"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
 EXPORTS = ("attn_fwd", "attn_decode_paged", "attn_decode_workspace_bytes", "attn_status_str", "attn_last_error")
@@ -45,7 +45,7 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd.restype = i
     L.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, sz, vp]
     L.attn_decode_paged.restype = i
-    L.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i]
+    L.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
     L.attn_decode_workspace_bytes.restype = sz
     L.attn_status_str.argtypes = [i]
     L.attn_status_str.restype = ctypes.c_char_p
@@ -125,8 +125,23 @@ def attn_fwd(q, k, v, scale: float | None = None, causal: bool = False, seq_lens
     return out, lse
 
 
-def attn_decode_workspace_bytes(B: int, Hq: int, D: int, max_blocks_per_seq: int, block_size: int = BLOCK_SIZE):
-    return int(lib().attn_decode_workspace_bytes(B, Hq, D, max_blocks_per_seq, block_size))
+def attn_decode_workspace_bytes(B: int, Hq: int, Hkv: int, D: int, max_blocks_per_seq: int,
+                                block_size: int = BLOCK_SIZE):
+    return int(lib().attn_decode_workspace_bytes(B, Hq, Hkv, D, max_blocks_per_seq, block_size))
+
+
+_workspaces = {}
+
+
+def decode_workspace(device, nbytes: int):
+    """A decode workspace of at least nbytes on device, kept per (device, stream) and reused."""
+    import torch
+    key = (str(device), torch.cuda.current_stream(device).cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
 
 
 def attn_decode_paged(q, k_cache, v_cache, block_table, ctx_lens, scale: float | None = None, out=None,
@@ -152,9 +167,9 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, ctx_lens, scale: float |
         out = torch.empty_like(q)
     if need_lse and lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    need = attn_decode_workspace_bytes(B, Hq, D, maxb, bs)
+    need = attn_decode_workspace_bytes(B, Hq, Hkv, D, maxb, bs)
     if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+        workspace = decode_workspace(q.device, need)
     st = lib().attn_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(ctx_lens),
                                  _ptr(out), _ptr(lse), B, Hq, Hkv, D, bs, maxb, NB, ctypes.c_float(scale), dt,
                                  _ptr(workspace), workspace.numel() * workspace.element_size(),

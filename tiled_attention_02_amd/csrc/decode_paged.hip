@@ -27,8 +27,8 @@
 // n of product n is d = 8c + n (for D = 128).
 // Every (block, kv head) of K and V is 16*D contiguous elements, read once.
 // The 4 wavefronts merge through LDS and write one partial (O normalised, log2
-// of its sum) per (sequence, query head, split); decode_combine_kernel merges
-// the splits. A sequence with a single split writes its output directly.
+// of its sum) per (sequence, query head, split); a second, light kernel merges
+// the partials. A sequence with a single split writes its output directly.
 #include "attn_device.h"
 #include "launch.h"
 
@@ -39,7 +39,6 @@ constexpr float kDecodeLazy = 8.0f;
 template <class T, int D>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   constexpr int KS = D / 32;   // k-steps of S^T (32 columns of D each)
-  constexpr int QW = D / 4;    // contiguous columns of q / k per lane group
   constexpr int VC = D / 16;   // columns of V per lane (= number of P.V products)
   constexpr int NPAIR = 2;     // block pairs per wavefront
   static_assert(D == 128 || D == 64, "head size");
@@ -52,19 +51,30 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   const int split = blockIdx.x;
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar table loads
+  const int g = lane >> 4;
+  const int c = lane & 15;
+  const int G = a.G;
+  const int blk0 = split * kSplitBlocks + 4 * w;
+  const int* trow = a.table + (size_t)b * a.max_blocks;
+
+  // The block-table entries of this wavefront's 4 blocks are read together with
+  // the context length (scalar loads, one round trip); entries at or beyond the
+  // sequence's end are read only if they exist in the table and never used.
+  int phys[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) phys[i] = trow[min(blk0 + i, a.max_blocks - 1)];
+  // materialise the four entries here (one wait for all) rather than letting
+  // the compiler sink each load into the branch that uses it
+  asm volatile("" ::"s"(phys[0]), "s"(phys[1]), "s"(phys[2]), "s"(phys[3]));
   const int ctx = a.ctx[b];
   const int nblk = (ctx + kDecodeBlock - 1) / kDecodeBlock;
   const int nsp = (nblk + kSplitBlocks - 1) / kSplitBlocks;
   if (split >= nsp) return;  // uniform across the workgroup
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int g = lane >> 4;
-  const int c = lane & 15;
-  const int G = a.G;
-
-  // ---- q^T operand: head c, columns QW*g + 8s .. +8
+  // ---- q^T operand: head c, columns 32s + 8g .. +8 (step s, lane group g)
   u32x4 qf[KS];
   {
     const bool live = c < G && a.qmode != 2;
@@ -72,20 +82,25 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + kvh * G + (live ? c : 0)) * D;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      u32x4 x = *reinterpret_cast<const u32x4*>(qp + QW * g + 8 * s);
+      u32x4 x = *reinterpret_cast<const u32x4*>(qp + 32 * s + 8 * g);
       x ^= flip;
       qf[s] = live ? x : u32x4{0, 0, 0, 0};
     }
   }
 
-  const int* trow = a.table + (size_t)b * a.max_blocks;
-  const size_t head_stride = (size_t)kDecodeBlock * D;                 // one (block, kv head)
+  const size_t head_stride = (size_t)kDecodeBlock * D;  // one (block, kv head)
   const size_t block_stride = (size_t)a.Hkv * head_stride;
   const uint16_t* kbase = static_cast<const uint16_t*>(a.kc) + kvh * head_stride;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.vc) + kvh * head_stride;
 
-  // ---- issue every load of this wavefront's blocks up front
-  const int blk0 = split * kSplitBlocks + 4 * w;
+  // ---- issue every load of this wavefront's blocks at once (blocks inside the
+  // sequence only: a wave-uniform test). A K load instruction reads 64
+  // contiguous bytes of each of 16 token rows, so each 128-byte line is
+  // requested by two consecutive instructions: these loads keep the normal
+  // cache policy so the second one hits. A V load instruction reads 4 whole
+  // rows, so V is streamed with non-temporal loads. Slots at or beyond ctx in the last
+  // block may hold anything (NaN included): they are loaded (the block exists)
+  // and their V rows replaced by zeros, so p = 0 cannot meet 0 * NaN.
   u32x4 kreg[NPAIR][2][KS];
   typedef uint32_t vchunk __attribute__((ext_vector_type(VC / 2)));
   vchunk vreg[NPAIR][8];
@@ -95,19 +110,14 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     for (int j = 0; j < 2; ++j) {
       const int blk = blk0 + 2 * p + j;
       if (blk < nblk) {
-        const size_t phys = (size_t)trow[blk];
-        const uint16_t* kb = kbase + phys * block_stride;
-        const uint16_t* vb = vbase + phys * block_stride;
+        const uint16_t* kb = kbase + (size_t)phys[2 * p + j] * block_stride;
+        const uint16_t* vb = vbase + (size_t)phys[2 * p + j] * block_stride;
 #pragma unroll
         for (int s = 0; s < KS; ++s)
-          kreg[p][j][s] = *reinterpret_cast<const u32x4*>(kb + c * D + QW * g + 8 * s);
-        // slots at or beyond ctx may hold anything (NaN included): their V rows are
-        // zeroed so that p = 0 cannot meet 0 * NaN in the product
+          kreg[p][j][s] = *reinterpret_cast<const u32x4*>(kb + c * D + 32 * s + 8 * g);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          vreg[p][4 * j + e] = (blk * kDecodeBlock + 4 * g + e < ctx)
-                                   ? *reinterpret_cast<const vchunk*>(vb + (4 * g + e) * D + VC * c)
-                                   : vchunk{};
+          vreg[p][4 * j + e] = __builtin_nontemporal_load(reinterpret_cast<const vchunk*>(vb + (4 * g + e) * D + VC * c));
       } else {
 #pragma unroll
         for (int s = 0; s < KS; ++s) kreg[p][j][s] = u32x4{0, 0, 0, 0};
@@ -115,6 +125,15 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         for (int e = 0; e < 4; ++e) vreg[p][4 * j + e] = vchunk{};
       }
     }
+  if ((blk0 + 4) * kDecodeBlock > ctx) {  // this wavefront holds the sequence's tail
+#pragma unroll
+    for (int p = 0; p < NPAIR; ++p)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int t = (blk0 + 2 * p + (e >> 2)) * kDecodeBlock + 4 * g + (e & 3);
+        vreg[p][e] = t < ctx ? vreg[p][e] : vchunk{};
+      }
+  }
 
   f32x4 oacc[VC];
 #pragma unroll
@@ -235,7 +254,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   }
 }
 
-// Second pass: merge the per-split partials of one (sequence, query head).
+// Second pass (the reduction of the split-K decomposition): merge the partials
+// of a sequence's splits. One workgroup of D threads per (query head,
+// sequence); thread d produces output column d. The partials are combined
+// with a running maximum, 8 splits per step so that 16 loads are in flight.
 template <class T, int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
   const int hq = blockIdx.x;
@@ -243,33 +265,44 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
   const int ctx = a.ctx[b];
   const int nblk = (ctx + kDecodeBlock - 1) / kDecodeBlock;
   const int nsp = (nblk + kSplitBlocks - 1) / kSplitBlocks;
-  if (nsp <= 1) return;  // written by the split kernel
+  if (nsp == 1) return;  // the first pass wrote this head's output
   const int d = threadIdx.x;
   const float* wp = a.ws + ((size_t)b * a.Hq + hq) * a.nsplit * (D + 2);
-  float M = -__builtin_inff();
-  for (int s = 0; s < nsp; ++s) M = fmaxf(M, wp[s * (D + 2) + D]);
-  float W = 0.f, acc = 0.f;
-  for (int s = 0; s < nsp; ++s) {
-    const float wt = fast_exp2(wp[s * (D + 2) + D] - M);
-    W += wt;
-    acc += wt * wp[s * (D + 2) + d];
+  float m = -__builtin_inff(), W = 0.f, acc = 0.f;
+  for (int s0 = 0; s0 < nsp; s0 += 8) {
+    float ls[8], part[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int sp = min(s0 + u, nsp - 1);  // valid address; weight 0 below
+      ls[u] = wp[(size_t)sp * (D + 2) + D];
+      part[u] = wp[(size_t)sp * (D + 2) + d];
+    }
+    float mc = m;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) mc = s0 + u < nsp ? fmaxf(mc, ls[u]) : mc;
+    const float r = fast_exp2(m - mc);  // 0 on the first step (m = -inf, W = acc = 0)
+    W *= r;
+    acc *= r;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float wt = s0 + u < nsp ? fast_exp2(ls[u] - mc) : 0.f;
+      W += wt;
+      acc += wt * part[u];
+    }
+    m = mc;
   }
-  const float val = acc / W;
   uint16_t* op = static_cast<uint16_t*>(a.o);
-  op[((size_t)b * a.Hq + hq) * D + d] = (uint16_t)(T::pack2(val, 0.f) & 0xffffu);
-  if (d == 0 && a.lse) a.lse[(size_t)b * a.Hq + hq] = (M + fast_log2(W)) * kLn2;
+  op[((size_t)b * a.Hq + hq) * D + d] = (uint16_t)(T::pack2(acc / W, 0.f) & 0xffffu);
+  if (d == 0 && a.lse) a.lse[(size_t)b * a.Hq + hq] = (m + fast_log2(W)) * kLn2;
 }
 
 template <class T, int D>
 static hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3(a.nsplit, a.Hkv, a.B), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (a.nsplit > 1) {
-    hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(a.Hq, a.B), dim3(D), 0, stream, a);
-    e = hipGetLastError();
-  }
-  return e;
+  if (e != hipSuccess || a.nsplit == 1) return e;
+  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(a.Hq, a.B), dim3(D), 0, stream, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeArgs& a, bool bf16, hipStream_t stream) {

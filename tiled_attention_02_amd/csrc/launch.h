@@ -32,7 +32,7 @@ struct DecodeArgs {
   const int* ctx;
   void* o;
   float* lse;
-  float* ws;  // per-split partials: [B][Hq][nsplit][D + 2] fp32
+  float* ws;   // per-split partials: [B][Hq][nsplit][D + 2] fp32
   int B, Hq, Hkv, G, D;
   int max_blocks;
   int nsplit;  // maximum number of splits per sequence
@@ -46,7 +46,10 @@ constexpr int kSplitBlocks = 16;        // cache blocks per split (256 tokens)
 hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int D, bool causal, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, bool bf16, hipStream_t stream);
 
-inline size_t decode_workspace_bytes(int B, int Hq, int D, int max_blocks) {
+// Workspace: the per-split partials (Hkv is part of the signature so that a
+// layout that depends on it stays a library-internal change).
+inline size_t decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_blocks) {
+  (void)Hkv;
   const size_t nsplit = (size_t)(max_blocks + kSplitBlocks - 1) / kSplitBlocks;
   return (size_t)B * Hq * nsplit * (size_t)(D + 2) * sizeof(float);
 }

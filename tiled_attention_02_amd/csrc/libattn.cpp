@@ -106,10 +106,11 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
   return ok();
 }
 
-size_t attn_decode_workspace_bytes(int B, int Hq, int D, int max_blocks_per_seq, int block_size) {
-  if (B < 1 || Hq < 1 || max_blocks_per_seq < 1 || block_size != attn::kDecodeBlock || (D != 64 && D != 128))
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_blocks_per_seq, int block_size) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_blocks_per_seq < 1 || block_size != attn::kDecodeBlock ||
+      (D != 64 && D != 128))
     return 0;
-  return attn::decode_workspace_bytes(B, Hq, D, max_blocks_per_seq);
+  return attn::decode_workspace_bytes(B, Hq, Hkv, D, max_blocks_per_seq);
 }
 
 attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_cache, const int* block_table,
@@ -136,7 +137,7 @@ attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_
     return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged: sizes too large");
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
     return fail(ATTN_ERR_INVALID, "attn_decode_paged: q, caches and o must be 16-byte aligned");
-  const size_t need = attn::decode_workspace_bytes(B, Hq, D, max_blocks_per_seq);
+  const size_t need = attn::decode_workspace_bytes(B, Hq, Hkv, D, max_blocks_per_seq);
   const int nsplit = (max_blocks_per_seq + attn::kSplitBlocks - 1) / attn::kSplitBlocks;
   if (nsplit > 1) {
     if (!workspace) return fail(ATTN_ERR_INVALID, "attn_decode_paged: workspace is null (%zu bytes needed)", need);
