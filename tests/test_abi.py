@@ -86,8 +86,9 @@ def test_decode_rejects_before_launch(L, kw, code):
 
 def test_workspace_size(L):
     import tiled_attention_02_amd as ta
-    # 256 blocks of 16 tokens -> 16 splits of 256 tokens, each partial holding D values + log-sum
-    assert ta.attn_decode_workspace_bytes(64, 12, 2, 128, 256) == 64 * 12 * 16 * 130 * 4
+    # 256 blocks of 16 tokens -> 16 splits of 256 tokens, each partial holding D values + log-sum,
+    # padded to a 16-byte multiple
+    assert ta.attn_decode_workspace_bytes(64, 12, 2, 128, 256) == 64 * 12 * 16 * 132 * 4
     assert ta.attn_decode_workspace_bytes(64, 12, 2, 128, 256, 8) == 0
     assert ta.attn_decode_workspace_bytes(64, 12, 2, 96, 256) == 0
     assert ta.attn_decode_workspace_bytes(64, 12, 5, 128, 256) == 0

@@ -12,10 +12,10 @@
 // 加速推理，Triton時代要來？", section "Triton SplitK GEMM 內核", applied to the
 // key axis; the merge is the softmax-statistics update of blockwise attention.
 //
-// Decomposition: one workgroup (4 wavefronts) per (split of 256 tokens, kv
-// head, sequence). Wavefront w takes cache blocks 4w .. 4w+3 of the split, two
-// blocks (32 tokens) per step, and serves all G = Hq/Hkv query heads of the kv
-// head from one read of each key/value block:
+// Decomposition: one wavefront per (split of 256 tokens = 16 cache blocks,
+// kv head, sequence). It streams its blocks two at a time (32 tokens per
+// step) with the next two pairs' loads in flight, and serves all
+// G = Hq/Hkv query heads of the kv head from one read of each block:
 //   S^T = K Q^T       v_mfma_f32_16x16x32: rows = 16 tokens of a block,
 //                     columns = query heads (G <= 16, the rest zero).
 //   O  += P V         v_mfma_f32_16x16x32: rows = heads, columns = 16 of D,
@@ -23,12 +23,13 @@
 // The transposed scores of the two blocks are already the A operand (P) of
 // the second product. The V operand needs 8 tokens at one column per lane:
 // lane (g = l/16, c = l%16) loads 16-byte rows of its 8 tokens at columns
-// [8c, 8c+8) and transposes them in registers (v_perm), so output column
-// n of product n is d = 8c + n (for D = 128).
+// [VC*c, VC*c + VC) (VC = D/16) and transposes them in registers (v_perm), so
+// product n yields column d = VC*c + n.
 // Every (block, kv head) of K and V is 16*D contiguous elements, read once.
-// The 4 wavefronts merge through LDS and write one partial (O normalised, log2
-// of its sum) per (sequence, query head, split); a second, light kernel merges
-// the partials. A sequence with a single split writes its output directly.
+// The split's partial (O normalised, log2 of its sum) comes straight from
+// the wavefront's registers: no LDS and no barrier. A second, light kernel
+// merges the partials; a sequence with a single split writes its output
+// directly.
 #include "attn_device.h"
 #include "launch.h"
 
@@ -36,45 +37,170 @@ namespace attn {
 
 constexpr float kDecodeLazy = 8.0f;
 
-template <class T, int D>
-__global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
-  constexpr int KS = D / 32;   // k-steps of S^T (32 columns of D each)
-  constexpr int VC = D / 16;   // columns of V per lane (= number of P.V products)
-  constexpr int NPAIR = 2;     // block pairs per wavefront
-  static_assert(D == 128 || D == 64, "head size");
+// Registers of one pair of cache blocks: K as the A operand of S^T (lane
+// (g, c): token c, columns 32s + 8g .. +8 of step s), V as 16-byte rows
+// (lane (g, c): tokens 4g + e of each block, columns VC*c .. +VC).
+template <int D>
+struct PairRegs {
+  static constexpr int KS = D / 32;
+  typedef uint32_t vchunk __attribute__((ext_vector_type(D / 32)));
+  u32x4 k[2][KS];
+  vchunk v[8];
+};
 
-  __shared__ float s_o[4][16][D];
-  __shared__ float s_m[4][16];
-  __shared__ float s_l[4][16];
-  __shared__ float s_lr[4][16];
+// A K load instruction reads 64 contiguous bytes of each of 16 token rows, so
+// each 128-byte line is requested by two consecutive instructions: K keeps the
+// normal cache policy so that the second one hits. A V load instruction reads
+// whole rows, so V is streamed with non-temporal loads. The second block of
+// the pair may lie beyond the sequence's last block (live1 == false): it then
+// re-reads the first block (a cache hit) instead of branching, since every
+// token there is >= ctx and is masked (scores) or zeroed (V rows) anyway;
+// loads on both sides of a branch would cost register copies that wait for
+// the loads in flight.
+template <int D>
+__device__ __forceinline__ void load_pair(PairRegs<D>& P, const uint16_t* kbase, const uint16_t* vbase,
+                                          size_t block_stride, int ph0, int ph1, bool live1, int g, int c) {
+  typedef typename PairRegs<D>::vchunk vchunk;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const size_t off = (size_t)(j && live1 ? ph1 : ph0) * block_stride;
+    const uint16_t* kb = kbase + off;
+    const uint16_t* vb = vbase + off;
+#pragma unroll
+    for (int s = 0; s < PairRegs<D>::KS; ++s)
+      P.k[j][s] = *reinterpret_cast<const u32x4*>(kb + c * D + 32 * s + 8 * g);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      P.v[4 * j + e] = __builtin_nontemporal_load(reinterpret_cast<const vchunk*>(vb + (4 * g + e) * D + (D / 16) * c));
+  }
+}
+
+// Online-softmax state of one wavefront: per lane, head c's running max (log2
+// units), the fp32 sum of p and the sum of the rounded p over the lane's
+// tokens; the accumulator rows are heads 4g + r, columns VC*c + n.
+template <int D>
+struct WaveState {
+  f32x4 o[D / 16];
+  float m, l, lr;
+};
+
+// One step: the 32 tokens starting at t0. In the sequence's last pair (TAIL)
+// tokens >= ctx are masked and their V rows zeroed, since unused cache slots
+// may hold anything, NaN included.
+template <class T, int D, bool TAIL>
+__device__ __forceinline__ void pair_step(WaveState<D>& st, PairRegs<D>& P, const u32x4 (&qf)[D / 32], int t0,
+                                          int ctx, float cexp, int g) {
+  constexpr int KS = D / 32;
+  constexpr int VC = D / 16;
+  typedef typename PairRegs<D>::vchunk vchunk;
+  f32x4 sacc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    sacc[j] = f32x4{};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) sacc[j] = T::mfma16(P.k[j][s], qf[s], sacc[j]);
+  }
+  if constexpr (TAIL) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        sacc[j][r] = (t0 + 16 * j + 4 * g + r) >= ctx ? -__builtin_inff() : sacc[j][r];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      P.v[e] = (t0 + 16 * (e >> 2) + 4 * g + (e & 3)) < ctx ? P.v[e] : vchunk{};
+  }
+  float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
+                   fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = half_swap_max(mx) * cexp;
+  const bool grow = mx > st.m + kDecodeLazy;
+  if (__builtin_amdgcn_ballot_w64(grow)) {
+    const float m_new = grow ? mx : st.m;
+    const float alpha = grow ? fast_exp2(st.m - m_new) : 1.f;
+    st.m = m_new;
+    st.l *= alpha;
+    st.lr *= alpha;
+    // output rows are heads 4g + r: fetch their factors from lane 4g + r
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float ar = __shfl(alpha, 4 * g + r);
+#pragma unroll
+      for (int n = 0; n < VC; ++n) st.o[n][r] *= ar;
+    }
+  }
+  const float msub = st.m == -__builtin_inff() ? 0.f : st.m;
+  float pv[8];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pv[4 * j + r] = fast_exp2(__builtin_fmaf(sacc[j][r], cexp, -msub));
+      st.l += pv[4 * j + r];
+    }
+  const u32x4 pf = {T::pack2(pv[0], pv[1]), T::pack2(pv[2], pv[3]), T::pack2(pv[4], pv[5]),
+                    T::pack2(pv[6], pv[7])};
+  // the running sum adds the rounded probabilities that the P.V product applies
+#pragma unroll
+  for (int e = 0; e < 4; ++e) st.lr = T::sum2(pf[e], st.lr);
+  // V operand of product n: element e = V[token e][VC*c + n]
+#pragma unroll
+  for (int n = 0; n < VC; ++n) {
+    const int dw = n >> 1;
+    u32x4 vf;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t x0 = P.v[2 * k][dw], x1 = P.v[2 * k + 1][dw];
+      vf[k] = (n & 1) ? pack_hi16(x0, x1) : pack_lo16(x0, x1);
+    }
+    st.o[n] = T::mfma16(pf, vf, st.o[n]);
+  }
+}
+
+template <class T, int D>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_split_kernel(DecodeArgs a) {
+  constexpr int KS = D / 32;
+  constexpr int VC = D / 16;
+  constexpr int NP = kSplitBlocks / 2;  // block pairs per split
+  static_assert(D == 128 || D == 64, "head size");
 
   const int split = blockIdx.x;
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar table loads
+  const int lane = threadIdx.x;
   const int g = lane >> 4;
   const int c = lane & 15;
   const int G = a.G;
-  const int blk0 = split * kSplitBlocks + 4 * w;
+  const int blk0 = split * kSplitBlocks;
   const int* trow = a.table + (size_t)b * a.max_blocks;
 
-  // The block-table entries of this wavefront's 4 blocks are read together with
-  // the context length (scalar loads, one round trip); entries at or beyond the
-  // sequence's end are read only if they exist in the table and never used.
-  int phys[4];
+  // The split's 16 block-table entries are read together with the context
+  // length (scalar loads, one round trip); entries at or beyond the sequence's
+  // end are read only if they exist in the table and never used.
+  int phys[kSplitBlocks];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) phys[i] = trow[min(blk0 + i, a.max_blocks - 1)];
-  // materialise the four entries here (one wait for all) rather than letting
-  // the compiler sink each load into the branch that uses it
-  asm volatile("" ::"s"(phys[0]), "s"(phys[1]), "s"(phys[2]), "s"(phys[3]));
+  for (int i = 0; i < kSplitBlocks; ++i) phys[i] = trow[min(blk0 + i, a.max_blocks - 1)];
+  // materialise the entries here (one wait for all) rather than letting the
+  // compiler sink each load into the branch that uses it
+  asm volatile("" ::"s"(phys[0]), "s"(phys[1]), "s"(phys[2]), "s"(phys[3]), "s"(phys[4]), "s"(phys[5]),
+               "s"(phys[6]), "s"(phys[7]));
+  asm volatile("" ::"s"(phys[8]), "s"(phys[9]), "s"(phys[10]), "s"(phys[11]), "s"(phys[12]), "s"(phys[13]),
+               "s"(phys[14]), "s"(phys[15]));
   const int ctx = a.ctx[b];
   const int nblk = (ctx + kDecodeBlock - 1) / kDecodeBlock;
   const int nsp = (nblk + kSplitBlocks - 1) / kSplitBlocks;
-  if (split >= nsp) return;  // uniform across the workgroup
+  if (split >= nsp) return;
+  const int nb = min(kSplitBlocks, nblk - blk0);  // blocks of this split, >= 1
+  const int np = (nb + 1) >> 1;
 
-  // ---- q^T operand: head c, columns 32s + 8g .. +8 (step s, lane group g)
+  const size_t head_stride = (size_t)kDecodeBlock * D;  // one (block, kv head)
+  const size_t block_stride = (size_t)a.Hkv * head_stride;
+  const uint16_t* kbase = static_cast<const uint16_t*>(a.kc) + kvh * head_stride;
+  const uint16_t* vbase = static_cast<const uint16_t*>(a.vc) + kvh * head_stride;
+
+  // ---- q^T operand: head c, columns 32s + 8g .. +8 (step s, lane group g);
+  // loaded first: the memory counter is in order, so the first step then waits
+  // only for q and its own pair
   u32x4 qf[KS];
   {
     const bool live = c < G && a.qmode != 2;
@@ -88,168 +214,82 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     }
   }
 
-  const size_t head_stride = (size_t)kDecodeBlock * D;  // one (block, kv head)
-  const size_t block_stride = (size_t)a.Hkv * head_stride;
-  const uint16_t* kbase = static_cast<const uint16_t*>(a.kc) + kvh * head_stride;
-  const uint16_t* vbase = static_cast<const uint16_t*>(a.vc) + kvh * head_stride;
+  // Pair q's table entries; a pair beyond the split (q >= np) re-reads pair 0
+  // (cache hits) so that every load is unconditional: the hardware counts
+  // loads in order, and paths with different numbers of loads in flight would
+  // make the waits before the MFMAs conservative.
+  auto ph = [&](int q, int j) { return q < np ? phys[2 * q + j] : phys[0]; };
+  // The scheduling barriers keep the load groups in this order (the scheduler
+  // would otherwise interleave them and the first step would wait for all).
+  PairRegs<D> P0, P1;
+  __builtin_amdgcn_sched_barrier(0);
+  load_pair<D>(P0, kbase, vbase, block_stride, phys[0], phys[1], nb > 1, g, c);
+  __builtin_amdgcn_sched_barrier(0);
+  load_pair<D>(P1, kbase, vbase, block_stride, ph(1, 0), ph(1, 1), 3 < nb, g, c);
+  __builtin_amdgcn_sched_barrier(0);
 
-  // ---- issue every load of this wavefront's blocks at once (blocks inside the
-  // sequence only: a wave-uniform test). A K load instruction reads 64
-  // contiguous bytes of each of 16 token rows, so each 128-byte line is
-  // requested by two consecutive instructions: these loads keep the normal
-  // cache policy so the second one hits. A V load instruction reads 4 whole
-  // rows, so V is streamed with non-temporal loads. Slots at or beyond ctx in the last
-  // block may hold anything (NaN included): they are loaded (the block exists)
-  // and their V rows replaced by zeros, so p = 0 cannot meet 0 * NaN.
-  u32x4 kreg[NPAIR][2][KS];
-  typedef uint32_t vchunk __attribute__((ext_vector_type(VC / 2)));
-  vchunk vreg[NPAIR][8];
+  WaveState<D> st;
 #pragma unroll
-  for (int p = 0; p < NPAIR; ++p)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int blk = blk0 + 2 * p + j;
-      if (blk < nblk) {
-        const uint16_t* kb = kbase + (size_t)phys[2 * p + j] * block_stride;
-        const uint16_t* vb = vbase + (size_t)phys[2 * p + j] * block_stride;
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-          kreg[p][j][s] = *reinterpret_cast<const u32x4*>(kb + c * D + 32 * s + 8 * g);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          vreg[p][4 * j + e] = __builtin_nontemporal_load(reinterpret_cast<const vchunk*>(vb + (4 * g + e) * D + VC * c));
-      } else {
-#pragma unroll
-        for (int s = 0; s < KS; ++s) kreg[p][j][s] = u32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vreg[p][4 * j + e] = vchunk{};
-      }
-    }
-  if ((blk0 + 4) * kDecodeBlock > ctx) {  // this wavefront holds the sequence's tail
-#pragma unroll
-    for (int p = 0; p < NPAIR; ++p)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int t = (blk0 + 2 * p + (e >> 2)) * kDecodeBlock + 4 * g + (e & 3);
-        vreg[p][e] = t < ctx ? vreg[p][e] : vchunk{};
-      }
-  }
-
-  f32x4 oacc[VC];
-#pragma unroll
-  for (int n = 0; n < VC; ++n) oacc[n] = f32x4{};
-  float m_run = -__builtin_inff();
-  float l_run = 0.f;   // fp32 sum of p (lse)
-  float lr_run = 0.f;  // sum of the rounded p (normalises O)
-  const float cexp = a.c;
+  for (int n = 0; n < VC; ++n) st.o[n] = f32x4{};
+  st.m = -__builtin_inff();
+  st.l = 0.f;
+  st.lr = 0.f;
 
 #pragma unroll
-  for (int p = 0; p < NPAIR; ++p) {
-    const int t0 = (blk0 + 2 * p) * kDecodeBlock;  // first token of the pair
-    if (t0 >= ctx) break;                         // uniform across the wavefront
-    f32x4 sacc[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      sacc[j] = f32x4{};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) sacc[j] = T::mfma16(kreg[p][j][s], qf[s], sacc[j]);
-    }
-    if (t0 + 32 > ctx) {  // tail: hide tokens at or beyond ctx
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          sacc[j][r] = (t0 + 16 * j + 4 * g + r) >= ctx ? -__builtin_inff() : sacc[j][r];
-    }
-    float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
-                     fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = half_swap_max(mx) * cexp;
-    const bool grow = mx > m_run + kDecodeLazy;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-      const float m_new = grow ? mx : m_run;
-      const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
-      m_run = m_new;
-      l_run *= alpha;
-      lr_run *= alpha;
-      // output rows are heads 4g + r: fetch their factors from lane 4g + r
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float ar = __shfl(alpha, 4 * g + r);
-#pragma unroll
-        for (int n = 0; n < VC; ++n) oacc[n][r] *= ar;
-      }
-    }
-    const float msub = m_run == -__builtin_inff() ? 0.f : m_run;
-    float pv[8];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pv[4 * j + r] = fast_exp2(__builtin_fmaf(sacc[j][r], cexp, -msub));
-        l_run += pv[4 * j + r];
-      }
-    const u32x4 pf = {T::pack2(pv[0], pv[1]), T::pack2(pv[2], pv[3]), T::pack2(pv[4], pv[5]),
-                      T::pack2(pv[6], pv[7])};
-    // the running sum adds the rounded probabilities that the P.V product applies
-#pragma unroll
-    for (int e = 0; e < 4; ++e) lr_run = T::sum2(pf[e], lr_run);
-    // V operand of product n: element e = V[token e][VC*c + n]
-#pragma unroll
-    for (int n = 0; n < VC; ++n) {
-      const int dw = n >> 1;
-      u32x4 vf;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t x0 = vreg[p][2 * k][dw], x1 = vreg[p][2 * k + 1][dw];
-        vf[k] = (n & 1) ? pack_hi16(x0, x1) : pack_lo16(x0, x1);
-      }
-      oacc[n] = T::mfma16(pf, vf, oacc[n]);
+  for (int p = 0; p < NP; ++p) {
+    if (p >= np) break;  // wave-uniform
+    PairRegs<D>& P = (p & 1) ? P1 : P0;
+    const int t0 = (blk0 + 2 * p) * kDecodeBlock;
+    if (t0 + 32 > ctx)
+      pair_step<T, D, true>(st, P, qf, t0, ctx, a.c, g);
+    else
+      pair_step<T, D, false>(st, P, qf, t0, ctx, a.c, g);
+    if (p + 2 < NP) {
+      const int q = p + 2 < NP ? p + 2 : 0;  // in range also where the branch is dead
+      load_pair<D>(P, kbase, vbase, block_stride, ph(q, 0), ph(q, 1), 2 * q + 1 < nb, g, c);
     }
   }
 
-  // ---- wavefront totals per head, then merge the 4 wavefronts through LDS
-  float l_head = l_run + __shfl_xor(l_run, 16);
+  // ---- per-head totals (lane c: head c), then the split's result per head
+  float l_head = st.l + __shfl_xor(st.l, 16);
   l_head = half_swap_sum(l_head);
-  float lr_head = lr_run + __shfl_xor(lr_run, 16);
+  float lr_head = st.lr + __shfl_xor(st.lr, 16);
   lr_head = half_swap_sum(lr_head);
-  if (g == 0) {
-    s_m[w][c] = m_run;
-    s_l[w][c] = l_head;
-    s_lr[w][c] = lr_head;
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int n = 0; n < VC; ++n) s_o[w][4 * g + r][VC * c + n] = oacc[n][r];
-  __syncthreads();
-
   const bool single = nsp == 1;
-  for (int idx = tid; idx < G * D; idx += 256) {
-    const int hh = idx / D;
-    const int d = idx % D;
-    float M = -__builtin_inff();
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, s_m[ww][hh]);
-    float L = 0.f, LR = 0.f, acc = 0.f;
+  for (int r = 0; r < 4; ++r) {
+    const int h = 4 * g + r;
+    const float inv = 1.f / __shfl(lr_head, h);  // > 0: the split holds a visible token
+    if (h < G) {
+      const int hq = kvh * G + h;
+      float val[VC];
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
-      const float wt = s_m[ww][hh] == -__builtin_inff() ? 0.f : fast_exp2(s_m[ww][hh] - M);
-      L += s_l[ww][hh] * wt;
-      LR += s_lr[ww][hh] * wt;
-      acc += s_o[ww][hh][d] * wt;
+      for (int n = 0; n < VC; ++n) val[n] = st.o[n][r] * inv;
+      if (single) {
+        uint32_t pk[VC / 2];
+#pragma unroll
+        for (int n = 0; n < VC / 2; ++n) pk[n] = T::pack2(val[2 * n], val[2 * n + 1]);
+        uint16_t* op = static_cast<uint16_t*>(a.o) + ((size_t)b * a.Hq + hq) * D + VC * c;
+        if constexpr (VC == 8) {
+          *reinterpret_cast<u32x4*>(op) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+        } else {
+          *reinterpret_cast<u32x2*>(op) = u32x2{pk[0], pk[1]};
+        }
+      } else {
+        float* wp = a.ws + (((size_t)b * a.Hq + hq) * a.nsplit + split) * (D + 4) + VC * c;
+#pragma unroll
+        for (int n = 0; n < VC; n += 4)
+          *reinterpret_cast<f32x4*>(wp + n) = f32x4{val[n], val[n + 1], val[n + 2], val[n + 3]};
+      }
     }
-    const float val = acc / LR;  // LR > 0: the split holds at least one visible token
-    const int hq = kvh * G + hh;
+  }
+  if (g == 0 && c < G) {  // lane c holds head c's statistics
+    const int hq = kvh * G + c;
+    const float lse2 = st.m + fast_log2(l_head);
     if (single) {
-      const size_t oi = ((size_t)b * a.Hq + hq) * D + d;
-      uint16_t* op = static_cast<uint16_t*>(a.o);
-      op[oi] = (uint16_t)(T::pack2(val, 0.f) & 0xffffu);
-      if (d == 0 && a.lse) a.lse[(size_t)b * a.Hq + hq] = (M + fast_log2(L)) * kLn2;
+      if (a.lse) a.lse[(size_t)b * a.Hq + hq] = lse2 * kLn2;
     } else {
-      float* wp = a.ws + (((size_t)b * a.Hq + hq) * a.nsplit + split) * (D + 2);
-      wp[d] = val;
-      if (d == 0) wp[D] = M + fast_log2(L);
+      a.ws[(((size_t)b * a.Hq + hq) * a.nsplit + split) * (D + 4) + D] = lse2;
     }
   }
 }
@@ -267,15 +307,15 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
   const int nsp = (nblk + kSplitBlocks - 1) / kSplitBlocks;
   if (nsp == 1) return;  // the first pass wrote this head's output
   const int d = threadIdx.x;
-  const float* wp = a.ws + ((size_t)b * a.Hq + hq) * a.nsplit * (D + 2);
+  const float* wp = a.ws + ((size_t)b * a.Hq + hq) * a.nsplit * (D + 4);
   float m = -__builtin_inff(), W = 0.f, acc = 0.f;
   for (int s0 = 0; s0 < nsp; s0 += 8) {
     float ls[8], part[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int sp = min(s0 + u, nsp - 1);  // valid address; weight 0 below
-      ls[u] = wp[(size_t)sp * (D + 2) + D];
-      part[u] = wp[(size_t)sp * (D + 2) + d];
+      ls[u] = wp[(size_t)sp * (D + 4) + D];
+      part[u] = wp[(size_t)sp * (D + 4) + d];
     }
     float mc = m;
 #pragma unroll
@@ -298,7 +338,7 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
 
 template <class T, int D>
 static hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3(a.nsplit, a.Hkv, a.B), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3(a.nsplit, a.Hkv, a.B), dim3(64), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(a.Hq, a.B), dim3(D), 0, stream, a);

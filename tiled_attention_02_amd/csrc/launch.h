@@ -32,7 +32,7 @@ struct DecodeArgs {
   const int* ctx;
   void* o;
   float* lse;
-  float* ws;   // per-split partials: [B][Hq][nsplit][D + 2] fp32
+  float* ws;   // per-split partials: [B][Hq][nsplit][D + 4] fp32 (O, then log2-sum-exp, pad)
   int B, Hq, Hkv, G, D;
   int max_blocks;
   int nsplit;  // maximum number of splits per sequence
@@ -51,7 +51,7 @@ hipError_t launch_decode(const DecodeArgs& a, bool bf16, hipStream_t stream);
 inline size_t decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_blocks) {
   (void)Hkv;
   const size_t nsplit = (size_t)(max_blocks + kSplitBlocks - 1) / kSplitBlocks;
-  return (size_t)B * Hq * nsplit * (size_t)(D + 2) * sizeof(float);
+  return (size_t)B * Hq * nsplit * (size_t)(D + 4) * sizeof(float);
 }
 
 }  // namespace attn
