@@ -326,45 +326,87 @@ __device__ __forceinline__ void epilogue(const Acc<D>& st, const Geo& g, int Tq,
 
 // Global -> register -> LDS staging of K or V tiles (row-major, swizzled).
 // Thread tid stages chunks tid + i*THREADS: row ch / C8, 16-byte chunk ch % C8.
+// The tile is read with buffer loads whose descriptor starts at the tile's
+// first row and covers only the rows below the sequence length: the hardware
+// returns zeros for the rest (no branch, and no access beyond the tensor).
+// The per-lane offset is loop invariant and the per-pass row step is a scalar
+// offset, so no vector address arithmetic is spent per load.
+constexpr int kBufferDword3 = 0x00020000;  // raw (untyped) buffer, 32-bit data
+
 template <int D, int BK, int THREADS>
 struct Stager {
   using S = Shape<D, BK>;
   static constexpr int CPT = BK * S::C8 / THREADS;
   static constexpr int RPP = THREADS / S::C8;  // rows per pass
   static_assert(CPT >= 1 && BK * S::C8 % THREADS == 0, "staging shape");
-  int row0;
+  int voff;
   int off[CPT];
   u32x4 reg[CPT];
-  const uint16_t* src;
+  const uint16_t* base;
 
-  __device__ __forceinline__ void init(const uint16_t* base, int tid) {
-    row0 = tid / S::C8;
+  __device__ __forceinline__ void init(const uint16_t* b, int tid) {
+    const int row0 = tid / S::C8;
     const int c = tid % S::C8;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int r = row0 + i * RPP;
       off[i] = r * S::RB + 16 * (c ^ swz<D>(r));
     }
-    src = base + (size_t)row0 * D + c * 8;
+    voff = row0 * S::RB + 16 * c;
+    base = b;
   }
   __device__ __forceinline__ void load(int kt, int Lk) {
     const int k0 = kt * BK;
-    if (k0 + BK <= Lk) {  // full tile: plain loads
+    // uniform by construction; readfirstlane tells the compiler so (a
+    // descriptor in vector registers would need a loop per load)
+    const int rows = __builtin_amdgcn_readfirstlane(min(max(Lk - k0, 0), BK));
+    const uint64_t p = reinterpret_cast<uint64_t>(base + (size_t)k0 * D);
+    const uint64_t pu = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(p >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(pu), (short)0, rows * S::RB, kBufferDword3);
 #pragma unroll
-      for (int i = 0; i < CPT; ++i) reg[i] = *reinterpret_cast<const u32x4*>(src + (size_t)(k0 + i * RPP) * D);
-    } else {  // tail tile: rows beyond the sequence are zero
-#pragma unroll
-      for (int i = 0; i < CPT; ++i) {
-        reg[i] = u32x4{0, 0, 0, 0};
-        if (k0 + row0 + i * RPP < Lk) reg[i] = *reinterpret_cast<const u32x4*>(src + (size_t)(k0 + i * RPP) * D);
-      }
-    }
+    for (int i = 0; i < CPT; ++i)
+      reg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, i * RPP * S::RB, 0));
   }
   __device__ __forceinline__ void store(char* tile) const {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) *reinterpret_cast<u32x4*>(tile + off[i]) = reg[i];
   }
 };
+
+// One key tile: prefetch tile kt+1 into registers, consume tile kt from LDS
+// buffer BUF, stage tile kt+1 into the other buffer, barrier. BUF is a
+// template parameter so that every LDS address is a per-lane offset plus an
+// immediate.
+template <class T, int D, int BK, bool CAUSAL, int BUF, int THREADS>
+__device__ __forceinline__ void tile_step(int kt, char* smem, Stager<D, BK, THREADS>& ks,
+                                          Stager<D, BK, THREADS>& vs, Acc<D>& st, const Offs<D, BK>& o,
+                                          const Geo& g, bool wave_live, int w_lo, int qrow, int h, float cexp) {
+  using S = Shape<D, BK>;
+  const int k0 = kt * BK;
+  const bool more = kt + 1 < g.nkt;
+  if (more) {
+    ks.load(kt + 1, g.Lk);
+    vs.load(kt + 1, g.Lk);
+  }
+  const char* Ks = smem + BUF * 2 * S::TILE;
+  const char* Vs = Ks + S::TILE;
+  // skip tiles entirely above this wavefront's part of the diagonal
+  if (wave_live && (!CAUSAL || k0 <= min(w_lo + 31, g.Lq - 1) + g.off)) {
+    f32x16 sacc[S::KB];
+    u32x4 pf[S::PS];
+    tile_qk<T, D, BK>(sacc, Ks, o, st);
+    tile_softmax<T, D, BK, CAUSAL>(sacc, pf, st, g, k0, qrow, w_lo, h, cexp);
+    tile_pv<T, D, BK>(st, pf, Vs, o);
+  }
+  if (more) {
+    char* nb = smem + (BUF ^ 1) * 2 * S::TILE;
+    ks.store(nb);
+    vs.store(nb + S::TILE);
+  }
+  __syncthreads();
+}
 
 // ---------------------------------------------------------------------------
 // Small grids: 4 wavefronts x 32 rows, double-buffered K/V tiles.
@@ -394,29 +436,9 @@ __global__ __launch_bounds__(BQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   }
   __syncthreads();
   const bool wave_live = w_lo < g.Lq;
-  for (int kt = 0; kt < g.nkt; ++kt) {
-    const int k0 = kt * BK;
-    const int buf = kt & 1;
-    if (kt + 1 < g.nkt) {
-      ks.load(kt + 1, g.Lk);
-      vs.load(kt + 1, g.Lk);
-    }
-    const char* Ks = smem + buf * 2 * S::TILE;
-    const char* Vs = Ks + S::TILE;
-    // skip tiles entirely above this wavefront's part of the diagonal
-    if (wave_live && (!CAUSAL || k0 <= min(w_lo + 31, g.Lq - 1) + g.off)) {
-      f32x16 sacc[S::KB];
-      u32x4 pf[S::PS];
-      tile_qk<T, D, BK>(sacc, Ks, o, st);
-      tile_softmax<T, D, BK, CAUSAL>(sacc, pf, st, g, k0, qrow, w_lo, h, a.c);
-      tile_pv<T, D, BK>(st, pf, Vs, o);
-    }
-    if (kt + 1 < g.nkt) {
-      char* nb = smem + (buf ^ 1) * 2 * S::TILE;
-      ks.store(nb);
-      vs.store(nb + S::TILE);
-    }
-    __syncthreads();
+  for (int kt = 0; kt < g.nkt; kt += 2) {
+    tile_step<T, D, BK, CAUSAL, 0>(kt, smem, ks, vs, st, o, g, wave_live, w_lo, qrow, h, a.c);
+    if (kt + 1 < g.nkt) tile_step<T, D, BK, CAUSAL, 1>(kt + 1, smem, ks, vs, st, o, g, wave_live, w_lo, qrow, h, a.c);
   }
   epilogue<T, D>(st, g, a.Tq, qrow, h);
 }
