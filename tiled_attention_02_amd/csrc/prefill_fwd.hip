@@ -58,14 +58,16 @@ constexpr float kLazyRescale = 8.0f;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-// 16-byte chunk slot of (row, chunk c) inside an LDS row: c ^ f(row). The
-// functions are chosen so that the K operand reads (16 rows, one chunk), the
-// transposing V reads (4 rows x 2 chunks per 16 lanes) and the row-major tile
-// writes all hit distinct banks.
+// 16-byte chunk slot of (row, chunk c) inside an LDS row: c ^ f(row). LDS
+// serves 256 bytes per cycle: 16 lanes of a 16-byte access, 32 lanes of an
+// 8-byte one. The functions make every such lane group hit distinct banks for
+// the K operand reads (16 consecutive rows, one chunk), the transposing V
+// reads (32 lanes: 4 consecutive rows x 4 chunks) and the row-major tile
+// writes. f depends only on row bits 0-3, which the offset hoisting relies on.
 template <int D>
 __device__ __forceinline__ int swz(int row) {
-  if constexpr (D == 128) return ((row & 7) << 1) | ((row >> 3) & 1);
-  else return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
+  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  else return ((row >> 3) & 1) | (((row >> 2) & 1) << 1) | (((row >> 1) & 1) << 2);
 }
 
 template <int D, int BK>
