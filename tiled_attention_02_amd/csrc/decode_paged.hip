@@ -28,8 +28,8 @@
 // Every (block, kv head) of K and V is 16*D contiguous elements, read once.
 // The split's partial (O normalised, log2 of its sum) comes straight from
 // the wavefront's registers: no LDS and no barrier. A second, light kernel
-// merges the partials; a sequence with a single split writes its output
-// directly.
+// merges the partials; when the whole batch fits in one split the first
+// kernel writes the output directly.
 #include "attn_device.h"
 #include "launch.h"
 
@@ -189,7 +189,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   const int ctx = a.ctx[b];
   const int nblk = (ctx + kDecodeBlock - 1) / kDecodeBlock;
   const int nsp = (nblk + kSplitBlocks - 1) / kSplitBlocks;
-  if (split >= nsp) return;
+  if (split >= nsp) {
+    // a split past the sequence's end publishes an empty partial (log2-sum-exp
+    // = -inf, weight 0) so that the merge needs no context length
+    if (a.nsplit > 1 && lane < G)
+      a.ws[(((size_t)b * a.Hq + kvh * G + lane) * a.nsplit + split) * (D + 4) + D] = -__builtin_inff();
+    return;
+  }
   const int nb = min(kSplitBlocks, nblk - blk0);  // blocks of this split, >= 1
   const int np = (nb + 1) >> 1;
 
@@ -255,7 +261,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   l_head = half_swap_sum(l_head);
   float lr_head = st.lr + __shfl_xor(st.lr, 16);
   lr_head = half_swap_sum(lr_head);
-  const bool single = nsp == 1;
+  const bool single = a.nsplit == 1;  // the whole grid has one split: no merge pass
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int h = 4 * g + r;
@@ -296,38 +302,36 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 
 // Second pass (the reduction of the split-K decomposition): merge the partials
 // of a sequence's splits. One workgroup of D threads per (query head,
-// sequence); thread d produces output column d. The partials are combined
-// with a running maximum, 8 splits per step so that 16 loads are in flight.
+// sequence); thread d produces output column d. Every split slot holds a
+// partial (splits past the sequence's end hold log2-sum-exp = -inf, and their
+// values are never used), so all slots are read in one round, 16 at a time.
 template <class T, int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
   const int hq = blockIdx.x;
   const int b = blockIdx.y;
-  const int ctx = a.ctx[b];
-  const int nblk = (ctx + kDecodeBlock - 1) / kDecodeBlock;
-  const int nsp = (nblk + kSplitBlocks - 1) / kSplitBlocks;
-  if (nsp == 1) return;  // the first pass wrote this head's output
   const int d = threadIdx.x;
   const float* wp = a.ws + ((size_t)b * a.Hq + hq) * a.nsplit * (D + 4);
   float m = -__builtin_inff(), W = 0.f, acc = 0.f;
-  for (int s0 = 0; s0 < nsp; s0 += 8) {
-    float ls[8], part[8];
+  for (int s0 = 0; s0 < a.nsplit; s0 += 16) {
+    float ls[16], part[16];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int sp = min(s0 + u, nsp - 1);  // valid address; weight 0 below
+    for (int u = 0; u < 16; ++u) {
+      const int sp = min(s0 + u, a.nsplit - 1);  // valid address; weight 0 below
       ls[u] = wp[(size_t)sp * (D + 4) + D];
       part[u] = wp[(size_t)sp * (D + 4) + d];
     }
     float mc = m;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) mc = s0 + u < nsp ? fmaxf(mc, ls[u]) : mc;
-    const float r = fast_exp2(m - mc);  // 0 on the first step (m = -inf, W = acc = 0)
+    for (int u = 0; u < 16; ++u) mc = s0 + u < a.nsplit ? fmaxf(mc, ls[u]) : mc;
+    const float r = mc == -__builtin_inff() ? 0.f : fast_exp2(m - mc);  // 0 while nothing is merged
     W *= r;
     acc *= r;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float wt = s0 + u < nsp ? fast_exp2(ls[u] - mc) : 0.f;
+    for (int u = 0; u < 16; ++u) {
+      const bool live = s0 + u < a.nsplit && ls[u] != -__builtin_inff();
+      const float wt = live ? fast_exp2(ls[u] - mc) : 0.f;
       W += wt;
-      acc += wt * part[u];
+      acc += live ? wt * part[u] : 0.f;  // an empty slot's values are never read into O
     }
     m = mc;
   }

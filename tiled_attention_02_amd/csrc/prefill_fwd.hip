@@ -398,9 +398,16 @@ __device__ __forceinline__ void tile_step(int kt, char* smem, Stager<D, BK, THRE
   if (wave_live && (!CAUSAL || k0 <= min(w_lo + 31, g.Lq - 1) + g.off)) {
     f32x16 sacc[S::KB];
     u32x4 pf[S::PS];
+    // Wave priority: the MFMA sections run at a higher priority than the
+    // softmax, so when both wavefronts of a SIMD are ready the matrix pipe is
+    // re-fed first and the other wavefront's VALU work fills its gaps.
+    __builtin_amdgcn_s_setprio(2);
     tile_qk<T, D, BK>(sacc, Ks, o, st);
+    __builtin_amdgcn_s_setprio(0);
     tile_softmax<T, D, BK, CAUSAL>(sacc, pf, st, g, k0, qrow, w_lo, h, cexp);
+    __builtin_amdgcn_s_setprio(2);
     tile_pv<T, D, BK>(st, pf, Vs, o);
+    __builtin_amdgcn_s_setprio(1);
   }
   if (more) {
     char* nb = smem + (BUF ^ 1) * 2 * S::TILE;
