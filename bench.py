@@ -10,6 +10,8 @@ Each call is timed with HIP events on the stream it runs on. Before each call
 the 256 MB Infinity Cache and the L2s, so the timed call reads its inputs from
 HBM; a read pass leaves clean lines behind, whereas a write pass would leave a
 gigabyte of dirty lines whose write-back would land inside the timed region.
+"context" holds figures reported beside the headline ones: the Llama3-8B-shaped
+512-token prefill (launch-dominated) and the rate of a plain streaming read.
 
 Prints ONE JSON line. value = prefill TFLOP/s (algorithmic flops: 4*D per
 unmasked query/key pair); the decode figure (algorithmic HBM bytes: K and V of
@@ -78,15 +80,20 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def _oracle_threads():
+    """Threads the oracle's numpy calls use (BLAS pool size), else the usable cores."""
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
 def cpu_baseline_prefill(x, case, budget_heads=32, row_stride=8):
     """Time the float64 oracle on a bounded sample of the prefill workload."""
     import numpy as np
     from oracle import oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
+    threads = _oracle_threads()
     heads = list(range(0, case.Hq, max(1, case.Hq // budget_heads)))[:budget_heads]
     rows = np.arange(0, case.T, row_stride)
     picks = np.array([(0, h, i) for h in heads for i in rows])
@@ -100,17 +107,83 @@ def cpu_baseline_prefill(x, case, budget_heads=32, row_stride=8):
                       f"algorithmic flops of the sampled rows / wall time"}
 
 
-def cpu_baseline_decode(x, case, nseq=64):
+def cpu_baseline_decode(x, case, nseq=64, min_seconds=5.0):
     import numpy as np
     import workloads as W
     from oracle import oracle as O
     sl = slice(0, nseq)
+    reps = 0
     t0 = time.perf_counter()
-    O.decode_paged(x["q"][sl], x["k_cache"], x["v_cache"], x["block_table"][sl], x["ctx_lens"][sl], case.scale)
-    dt = time.perf_counter() - t0
-    nbytes = W.decode_bytes(x["ctx_lens"][sl], case.Hq, case.Hkv, case.D)
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "kind": "oracle",
-            "sample": f"float64 oracle on {nseq} of {case.B} sequences; {dt:.2f} s wall"}
+    while True:  # the whole batch takes well under a second: repeat it for a stable figure
+        O.decode_paged(x["q"][sl], x["k_cache"], x["v_cache"], x["block_table"][sl], x["ctx_lens"][sl], case.scale)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    nbytes = W.decode_bytes(x["ctx_lens"][sl], case.Hq, case.Hkv, case.D) * reps
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": _oracle_threads(), "kind": "oracle",
+            "sample": f"float64 oracle on the whole batch ({nseq} sequences), repeated {reps} times; "
+                      f"{dt:.1f} s wall"}
+
+
+def context_measurements(ta, W, torch, np, dev, flush_rows, flush_dst, evict):
+    """Figures reported beside the headline numbers (not part of `value`).
+
+    * Llama3-8B-shaped prefill (B=2, Hq=32, Hkv=8, T=512, D=128, causal bf16):
+      4.3 GFLOP, about 2 us of the whole GPU, so its time is set by launch and
+      tail effects; timed per call (after the cache eviction) and as the mean
+      of 50 back-to-back calls.
+    * a plain streaming read: the 1 GiB eviction pass itself (torch.sum over
+      rows of 4096 float32), i.e. the HBM read rate a simple kernel attains here.
+    """
+    lc = W.LLAMA
+    xl = W.prefill_inputs(lc)
+    bf = torch.bfloat16
+    q = torch.from_numpy(xl["q"]).to(bf).to(dev)
+    k = torch.from_numpy(xl["k"]).to(bf).to(dev)
+    v = torch.from_numpy(xl["v"]).to(bf).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    flops = W.prefill_flops(lc.B, lc.Hq, lc.T, lc.T, lc.D, True)
+    call = lambda: ta.attn_fwd(q, k, v, scale=lc.scale, causal=True, out=o, lse=lse)  # noqa: E731
+    for _ in range(3):
+        call()
+    per = []
+    for _ in range(20):
+        evict()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call()
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(50):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    b2b = e0.elapsed_time(e1) / 50
+    med = float(np.median(per))
+    rd = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.sum(flush_rows, dim=1, out=flush_dst)
+        e1.record()
+        torch.cuda.synchronize()
+        rd.append(e0.elapsed_time(e1))
+    nbytes = flush_rows.numel() * 4
+    return {
+        "llama3_8b_shaped_prefill": {
+            "workload": "causal bf16 B=2 Hq=32 Hkv=8 T=512 D=128", "gflop_per_call": round(flops / 1e9, 3),
+            "us_per_call_median": round(med * 1e3, 2),
+            "tflops_per_call": round(flops / (med * 1e-3) / 1e12, 1),
+            "us_per_call_back_to_back": round(b2b * 1e3, 2),
+            "tflops_back_to_back": round(flops / (b2b * 1e-3) / 1e12, 1)},
+        "streaming_read_gbs": {"value": round(nbytes / (float(np.median(rd)) * 1e-3) / 1e9, 1),
+                               "what": "torch.sum over a 1 GiB float32 buffer in rows of 4096 (the eviction pass), median of 5"},
+    }
 
 
 def main():
@@ -162,8 +235,9 @@ def main():
     dlse = torch.empty(dq.shape[:2], dtype=torch.float32, device=dev)
     ws = torch.empty(max(256, ta.attn_decode_workspace_bytes(dc.B, dc.Hq, dc.Hkv, dc.D, bt.shape[1])),
                      dtype=torch.uint8, device=dev)
-    flush_src = torch.ones((1 << 20, 1024), dtype=torch.uint8, device=dev)  # 1 GiB
-    flush_dst = torch.empty(1024, dtype=torch.uint8, device=dev)
+    flush_src = torch.ones((1 << 18, 1024), dtype=torch.float32, device=dev)  # 1 GiB
+    flush_rows = flush_src.view(-1, 4096)
+    flush_dst = torch.empty(flush_rows.shape[0], dtype=torch.float32, device=dev)
 
     pflops = W.prefill_flops(pc.B, pc.Hq, pc.T, pc.T, pc.D, True)
     dbytes = W.decode_bytes(xd["ctx_lens"], dc.Hq, dc.Hkv, dc.D)
@@ -174,7 +248,7 @@ def main():
         # read-only pass over 1 GiB: pushes the inputs out of every cache level
         # without leaving dirty lines to write back during the timed call
         if not args.no_flush:
-            torch.amax(flush_src, dim=0, out=flush_dst)
+            torch.sum(flush_rows, dim=1, out=flush_dst)
 
     def step(evs):
         if run_p:
@@ -240,6 +314,7 @@ def main():
                                 "kernels": "decode_split_kernel + decode_combine_kernel",
                                 "algorithmic_bytes_per_call": dbytes}},
     }
+    out["context"] = context_measurements(ta, W, torch, np, dev, flush_rows, flush_dst, evict)
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline: float64 oracle on a sample of the prefill workload")
         out["cpu_baseline"] = cpu_baseline_prefill(xp, pc)
