@@ -45,8 +45,8 @@
 // Schedule: 4 wavefronts x 32 rows (128 query rows) per workgroup, two
 // workgroups per CU (two wavefronts per SIMD, so one wavefront's MFMAs overlap
 // the other's softmax), K/V tiles double-buffered in LDS with one barrier per
-// tile: tile j+1 travels HBM -> registers while tile j is consumed, then goes
-// to the other LDS buffer. LDS operand reads are issued ahead of the MFMAs
+// tile: tile j+1 travels HBM -> LDS directly (buffer loads that write LDS)
+// while tile j is consumed. LDS operand reads are issued ahead of the MFMAs
 // that consume them (register double buffering).
 #include "attn_device.h"
 #include "launch.h"
@@ -326,38 +326,45 @@ __device__ __forceinline__ void epilogue(const Acc<D>& st, const Geo& g, int Tq,
   if (g.Lg && h == 0) g.Lg[qrow] = has ? (st.m + fast_log2(l_tot)) * kLn2 : -__builtin_inff();
 }
 
-// Global -> register -> LDS staging of K or V tiles (row-major, swizzled).
-// Thread tid stages chunks tid + i*THREADS: row ch / C8, 16-byte chunk ch % C8.
-// The tile is read with buffer loads whose descriptor starts at the tile's
-// first row and covers only the rows below the sequence length: the hardware
-// returns zeros for the rest (no branch, and no access beyond the tensor).
-// The per-lane offset is loop invariant and the per-pass row step is a scalar
-// offset, so no vector address arithmetic is spent per load.
+// Global -> LDS staging of K or V tiles (row-major, swizzled) with buffer
+// loads that write LDS directly (no registers, no LDS store instructions).
+// One such wavefront instruction fills 1 KiB of consecutive LDS: lane l writes
+// bytes [16 l, 16 l + 16) after a wave-uniform base. So instruction n of a tile
+// covers rows n*RPI .. n*RPI + RPI - 1, lane l the row n*RPI + l / C8 at slot
+// p = l % C8, and the lane fetches the global chunk that the swizzle places in
+// that slot, c = p ^ f(row). The descriptor starts at the tile's first row and
+// covers only the rows below the sequence length: the hardware writes zeros
+// for the rest (no branch, no access beyond the tensor).
 constexpr int kBufferDword3 = 0x00020000;  // raw (untyped) buffer, 32-bit data
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 template <int D, int BK, int THREADS>
 struct Stager {
   using S = Shape<D, BK>;
-  static constexpr int CPT = BK * S::C8 / THREADS;
-  static constexpr int RPP = THREADS / S::C8;  // rows per pass
-  static_assert(CPT >= 1 && BK * S::C8 % THREADS == 0, "staging shape");
-  int voff;
-  int off[CPT];
-  u32x4 reg[CPT];
+  static constexpr int NW = THREADS / 64;
+  static constexpr int RPI = 1024 / S::RB;      // rows per wavefront instruction
+  static constexpr int CPT = BK / (RPI * NW);   // instructions per wavefront per tile
+  static_assert(CPT >= 1 && BK % (RPI * NW) == 0, "staging shape");
+  int voff[CPT];  // per-lane byte offset of the fetched chunk within the tile
+  int loff[CPT];  // wave-uniform LDS byte offset of the instruction within the tile
   const uint16_t* base;
 
   __device__ __forceinline__ void init(const uint16_t* b, int tid) {
-    const int row0 = tid / S::C8;
-    const int c = tid % S::C8;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l = tid & 63;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int r = row0 + i * RPP;
-      off[i] = r * S::RB + 16 * (c ^ swz<D>(r));
+      const int n = i * NW + w;
+      const int row = n * RPI + l / S::C8;
+      voff[i] = row * S::RB + 16 * ((l % S::C8) ^ swz<D>(row));
+      loff[i] = n * RPI * S::RB;
     }
-    voff = row0 * S::RB + 16 * c;
     base = b;
   }
-  __device__ __forceinline__ void load(int kt, int Lk) {
+  // Issues the loads of tile kt into the LDS tile at `tile`; they complete
+  // asynchronously (wait for the vector memory counter before reading).
+  __device__ __forceinline__ void load(int kt, int Lk, char* tile) const {
     const int k0 = kt * BK;
     // uniform by construction; readfirstlane tells the compiler so (a
     // descriptor in vector registers would need a loop per load)
@@ -367,33 +374,44 @@ struct Stager {
                         (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(pu), (short)0, rows * S::RB, kBufferDword3);
+    // The host compilation pass of this file does not know the LDS-load
+    // builtin (and would then drop the kernels' host stubs); the function is
+    // only ever compiled for the device.
+#if defined(__HIP_DEVICE_COMPILE__)
 #pragma unroll
     for (int i = 0; i < CPT; ++i)
-      reg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, i * RPP * S::RB, 0));
-  }
-  __device__ __forceinline__ void store(char* tile) const {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) *reinterpret_cast<u32x4*>(tile + off[i]) = reg[i];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(tile + loff[i]), 16, voff[i], 0, 0, 0);
+#else
+    (void)rsrc;
+    (void)tile;
+#endif
   }
 };
 
-// One key tile: prefetch tile kt+1 into registers, consume tile kt from LDS
-// buffer BUF, stage tile kt+1 into the other buffer, barrier. BUF is a
-// template parameter so that every LDS address is a per-lane offset plus an
-// immediate.
-template <class T, int D, int BK, bool CAUSAL, int BUF, int THREADS>
-__device__ __forceinline__ void tile_step(int kt, char* smem, Stager<D, BK, THREADS>& ks,
-                                          Stager<D, BK, THREADS>& vs, Acc<D>& st, const Offs<D, BK>& o,
+// Waits until this wavefront's LDS-bound loads have landed, then synchronises
+// the workgroup so that every wavefront's loads are visible.
+__device__ __forceinline__ void staged_barrier() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
+// One key tile: start the loads of tile kt+1 into the other buffer, consume
+// tile kt from buffer `cur`, wait for the loads, barrier. The two buffers are
+// separate LDS arrays so that reads of one are never ordered behind the
+// in-flight loads into the other; with the loop unrolled by two every LDS
+// address is a per-lane offset plus an immediate.
+template <class T, int D, int BK, bool CAUSAL, int THREADS>
+__device__ __forceinline__ void tile_step(int kt, char* cur, char* nxt, const Stager<D, BK, THREADS>& ks,
+                                          const Stager<D, BK, THREADS>& vs, Acc<D>& st, const Offs<D, BK>& o,
                                           const Geo& g, bool wave_live, int w_lo, int qrow, int h, float cexp) {
   using S = Shape<D, BK>;
   const int k0 = kt * BK;
-  const bool more = kt + 1 < g.nkt;
-  if (more) {
-    ks.load(kt + 1, g.Lk);
-    vs.load(kt + 1, g.Lk);
+  if (kt + 1 < g.nkt) {
+    ks.load(kt + 1, g.Lk, nxt);
+    vs.load(kt + 1, g.Lk, nxt + S::TILE);
   }
-  const char* Ks = smem + BUF * 2 * S::TILE;
-  const char* Vs = Ks + S::TILE;
+  const char* Ks = cur;
+  const char* Vs = cur + S::TILE;
   // skip tiles entirely above this wavefront's part of the diagonal
   if (wave_live && (!CAUSAL || k0 <= min(w_lo + 31, g.Lq - 1) + g.off)) {
     f32x16 sacc[S::KB];
@@ -409,12 +427,7 @@ __device__ __forceinline__ void tile_step(int kt, char* smem, Stager<D, BK, THRE
     tile_pv<T, D, BK>(st, pf, Vs, o);
     __builtin_amdgcn_s_setprio(1);
   }
-  if (more) {
-    char* nb = smem + (BUF ^ 1) * 2 * S::TILE;
-    ks.store(nb);
-    vs.store(nb + S::TILE);
-  }
-  __syncthreads();
+  staged_barrier();
 }
 
 // ---------------------------------------------------------------------------
@@ -423,7 +436,8 @@ template <class T, int D, int BQ, int BK, bool CAUSAL>
 __global__ __launch_bounds__(BQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   using S = Shape<D, BK>;
   constexpr int THREADS = (BQ / 32) * 64;
-  __shared__ __align__(16) char smem[2 * 2 * S::TILE];  // [buffer][K | V]
+  __shared__ __align__(16) char buf0[2 * S::TILE];  // K | V
+  __shared__ __align__(16) char buf1[2 * S::TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5;
   const Geo g = make_geo<D, BQ, BK, CAUSAL>(a);
@@ -438,16 +452,14 @@ __global__ __launch_bounds__(BQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   vs.init(g.Vg, tid);
 
   if (g.nkt > 0) {
-    ks.load(0, g.Lk);
-    vs.load(0, g.Lk);
-    ks.store(smem);
-    vs.store(smem + S::TILE);
+    ks.load(0, g.Lk, buf0);
+    vs.load(0, g.Lk, buf0 + S::TILE);
   }
-  __syncthreads();
+  staged_barrier();
   const bool wave_live = w_lo < g.Lq;
   for (int kt = 0; kt < g.nkt; kt += 2) {
-    tile_step<T, D, BK, CAUSAL, 0>(kt, smem, ks, vs, st, o, g, wave_live, w_lo, qrow, h, a.c);
-    if (kt + 1 < g.nkt) tile_step<T, D, BK, CAUSAL, 1>(kt + 1, smem, ks, vs, st, o, g, wave_live, w_lo, qrow, h, a.c);
+    tile_step<T, D, BK, CAUSAL>(kt, buf0, buf1, ks, vs, st, o, g, wave_live, w_lo, qrow, h, a.c);
+    if (kt + 1 < g.nkt) tile_step<T, D, BK, CAUSAL>(kt + 1, buf1, buf0, ks, vs, st, o, g, wave_live, w_lo, qrow, h, a.c);
   }
   epilogue<T, D>(st, g, a.Tq, qrow, h);
 }
