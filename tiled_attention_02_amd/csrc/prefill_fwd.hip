@@ -185,12 +185,15 @@ __device__ __forceinline__ void make_offs(Offs<D, BK>& o, int lane) {
 }
 
 // S^T = K Q^T for one tile in LDS. The K fragments of k-step s+2 are read
-// while the MFMAs of step s run (a three-deep register ring).
+// while the MFMAs of step s run (a three-deep register ring). No scheduling
+// directives: callers add the pattern they want.
+constexpr int kQkDepth = 2;
+
 template <class T, int D, int BK>
-__device__ __forceinline__ void tile_qk(f32x16 (&sacc)[BK / 32], const char* Ks, const Offs<D, BK>& o,
-                                        const Acc<D>& st) {
+__device__ __forceinline__ void tile_qk_plain(f32x16 (&sacc)[BK / 32], const char* Ks, const Offs<D, BK>& o,
+                                              const Acc<D>& st) {
   using S = Shape<D, BK>;
-  constexpr int DEPTH = 2;
+  constexpr int DEPTH = kQkDepth;
   u32x4 fr[DEPTH + 1][S::KB];
 #pragma unroll
   for (int kb = 0; kb < S::KB; ++kb) sacc[kb] = f32x16{};
@@ -209,11 +212,18 @@ __device__ __forceinline__ void tile_qk(f32x16 (&sacc)[BK / 32], const char* Ks,
 #pragma unroll
     for (int kb = 0; kb < S::KB; ++kb) sacc[kb] = T::mfma32(fr[s % (DEPTH + 1)][kb], st.qf[s], sacc[kb]);
   }
+}
+
+template <class T, int D, int BK>
+__device__ __forceinline__ void tile_qk(f32x16 (&sacc)[BK / 32], const char* Ks, const Offs<D, BK>& o,
+                                        const Acc<D>& st) {
+  using S = Shape<D, BK>;
+  tile_qk_plain<T, D, BK>(sacc, Ks, o, st);
   // schedule: the reads of step s+DEPTH go out before the MFMAs of step s
-  __builtin_amdgcn_sched_group_barrier(0x100, DEPTH * S::KB, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, kQkDepth * S::KB, 0);
 #pragma unroll
   for (int s = 0; s < S::KS; ++s) {
-    if (s + DEPTH < S::KS) __builtin_amdgcn_sched_group_barrier(0x100, S::KB, 0);
+    if (s + kQkDepth < S::KS) __builtin_amdgcn_sched_group_barrier(0x100, S::KB, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, S::KB, 0);
   }
 }
@@ -249,10 +259,12 @@ __device__ __forceinline__ void tile_pv(Acc<D>& st, const u32x4 (&pf)[BK / 16], 
   }
 }
 
-// Mask, online-softmax update and P^T operand for one tile of scores.
+// Mask and online-softmax statistics for one tile of scores: the tile max,
+// and the (lazy) rescale of the running sums and of O. Returns the max to
+// subtract in the exponentials.
 template <class T, int D, int BK, bool CAUSAL>
-__device__ __forceinline__ void tile_softmax(f32x16 (&sacc)[BK / 32], u32x4 (&pf)[BK / 16], Acc<D>& st,
-                                             const Geo& g, int k0, int qrow, int w_lo, int h, float cexp) {
+__device__ __forceinline__ float softmax_stats(f32x16 (&sacc)[BK / 32], Acc<D>& st, const Geo& g, int k0, int qrow,
+                                               int w_lo, int h, float cexp) {
   using S = Shape<D, BK>;
   const bool need_mask = (k0 + BK > g.Lk) || (CAUSAL && k0 + BK - 1 > w_lo + g.off);
   if (need_mask) {
@@ -283,8 +295,14 @@ __device__ __forceinline__ void tile_softmax(f32x16 (&sacc)[BK / 32], u32x4 (&pf
 #pragma unroll
     for (int i = 0; i < S::DB; ++i) st.oacc[i] *= alpha;
   }
-  const float msub = st.m == -__builtin_inff() ? 0.f : st.m;
-  // p = 2^(s*c - m), row sums, pack to the P^T operand
+  return st.m == -__builtin_inff() ? 0.f : st.m;
+}
+
+// p = 2^(s*c - m), the two running sums, and the P^T operand (no branches).
+template <class T, int D, int BK>
+__device__ __forceinline__ void softmax_exp(const f32x16 (&sacc)[BK / 32], u32x4 (&pf)[BK / 16], Acc<D>& st,
+                                            float msub, float cexp) {
+  using S = Shape<D, BK>;
   float lsum = 0.f, lrsum = 0.f;
 #pragma unroll
   for (int kb = 0; kb < S::KB; ++kb)
@@ -395,49 +413,71 @@ __device__ __forceinline__ void staged_barrier() {
   __syncthreads();
 }
 
-// One key tile: start the loads of tile kt+1 into the other buffer, consume
-// tile kt from buffer `cur`, wait for the loads, barrier. The two buffers are
-// separate LDS arrays so that reads of one are never ordered behind the
-// in-flight loads into the other; with the loop unrolled by two every LDS
-// address is a per-lane offset plus an immediate.
+// One pipelined key step kt. On entry the scores of tile kt (s_cur) are in
+// registers, K of tile kt+1 and V of tile kt are in LDS. The step starts the
+// loads of K_{kt+2} and V_{kt+1} into the buffers read one step earlier, then
+//   * masks tile kt where needed, takes its max and rescales lazily (VALU);
+//   * computes S of tile kt+1 (MFMA) interleaved with the exponentials, sums
+//     and packing of tile kt (VALU): the matrix core and the vector ALU of
+//     the wavefront work at the same time;
+//   * accumulates O^T += V^T P^T for tile kt (MFMA);
+// and ends with the wait for its loads and a barrier.
 template <class T, int D, int BK, bool CAUSAL, int THREADS>
-__device__ __forceinline__ void tile_step(int kt, char* cur, char* nxt, const Stager<D, BK, THREADS>& ks,
-                                          const Stager<D, BK, THREADS>& vs, Acc<D>& st, const Offs<D, BK>& o,
-                                          const Geo& g, bool wave_live, int w_lo, int qrow, int h, float cexp) {
+__device__ __forceinline__ void pipe_step(int kt, const char* kcur, const char* vcur, char* kload, char* vload,
+                                          f32x16 (&s_cur)[BK / 32], f32x16 (&s_nxt)[BK / 32],
+                                          const Stager<D, BK, THREADS>& ks, const Stager<D, BK, THREADS>& vs,
+                                          Acc<D>& st, const Offs<D, BK>& o, const Geo& g, bool wave_live,
+                                          int w_last, int w_lo, int qrow, int h, float cexp) {
   using S = Shape<D, BK>;
-  const int k0 = kt * BK;
-  if (kt + 1 < g.nkt) {
-    ks.load(kt + 1, g.Lk, nxt);
-    vs.load(kt + 1, g.Lk, nxt + S::TILE);
-  }
-  const char* Ks = cur;
-  const char* Vs = cur + S::TILE;
-  // skip tiles entirely above this wavefront's part of the diagonal
-  if (wave_live && (!CAUSAL || k0 <= min(w_lo + 31, g.Lq - 1) + g.off)) {
-    f32x16 sacc[S::KB];
+  if (kt + 2 < g.nkt) ks.load(kt + 2, g.Lk, kload);
+  if (kt + 1 < g.nkt) vs.load(kt + 1, g.Lk, vload);
+  // causal: tiles entirely above this wavefront's part of the diagonal are
+  // skipped (monotone in kt, so work_next implies work)
+  const bool work = wave_live && (!CAUSAL || kt * BK <= w_last);
+  const bool work_next = kt + 1 < g.nkt && wave_live && (!CAUSAL || (kt + 1) * BK <= w_last);
+  if (work) {
     u32x4 pf[S::PS];
-    // Wave priority: the MFMA sections run at a higher priority than the
-    // softmax, so when both wavefronts of a SIMD are ready the matrix pipe is
-    // re-fed first and the other wavefront's VALU work fills its gaps.
+    const float msub = softmax_stats<T, D, BK, CAUSAL>(s_cur, st, g, kt * BK, qrow, w_lo, h, cexp);
+    if (work_next) {
+      tile_qk_plain<T, D, BK>(s_nxt, kcur, o, st);
+      softmax_exp<T, D, BK>(s_cur, pf, st, msub, cexp);
+      // interleave: each MFMA of the next tile's S is followed by a share of
+      // the current tile's vector work; K fragments stay kQkDepth steps ahead
+      constexpr int NMF = S::KS * S::KB;
+      constexpr int NVALU = S::KB * 16 * 3 + S::KB * 16;  // fma, exp, add; cvt and dot2 per pair
+      constexpr int PER = (NVALU + NMF - 1) / NMF;
+      __builtin_amdgcn_sched_group_barrier(0x100, kQkDepth * S::KB, 0);
+#pragma unroll
+      for (int s2 = 0; s2 < S::KS; ++s2) {
+        if (s2 + kQkDepth < S::KS) __builtin_amdgcn_sched_group_barrier(0x100, S::KB, 0);
+#pragma unroll
+        for (int kb = 0; kb < S::KB; ++kb) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, PER, 0);
+        }
+      }
+    } else {
+      softmax_exp<T, D, BK>(s_cur, pf, st, msub, cexp);
+    }
     __builtin_amdgcn_s_setprio(2);
-    tile_qk<T, D, BK>(sacc, Ks, o, st);
+    tile_pv<T, D, BK>(st, pf, vcur, o);
     __builtin_amdgcn_s_setprio(0);
-    tile_softmax<T, D, BK, CAUSAL>(sacc, pf, st, g, k0, qrow, w_lo, h, cexp);
-    __builtin_amdgcn_s_setprio(2);
-    tile_pv<T, D, BK>(st, pf, Vs, o);
-    __builtin_amdgcn_s_setprio(1);
   }
   staged_barrier();
 }
 
 // ---------------------------------------------------------------------------
-// Small grids: 4 wavefronts x 32 rows, double-buffered K/V tiles.
+// 4 wavefronts x 32 rows, pipelined key steps over double-buffered K and V.
 template <class T, int D, int BQ, int BK, bool CAUSAL>
 __global__ __launch_bounds__(BQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   using S = Shape<D, BK>;
   constexpr int THREADS = (BQ / 32) * 64;
-  __shared__ __align__(16) char buf0[2 * S::TILE];  // K | V
-  __shared__ __align__(16) char buf1[2 * S::TILE];
+  // K of tile t lives in kb[t & 1], V of tile t in vb[t & 1]; separate LDS
+  // arrays, so reads of one are never ordered behind the loads into another
+  __shared__ __align__(16) char kb0[S::TILE];
+  __shared__ __align__(16) char kb1[S::TILE];
+  __shared__ __align__(16) char vb0[S::TILE];
+  __shared__ __align__(16) char vb1[S::TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5;
   const Geo g = make_geo<D, BQ, BK, CAUSAL>(a);
@@ -452,14 +492,21 @@ __global__ __launch_bounds__(BQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   vs.init(g.Vg, tid);
 
   if (g.nkt > 0) {
-    ks.load(0, g.Lk, buf0);
-    vs.load(0, g.Lk, buf0 + S::TILE);
+    ks.load(0, g.Lk, kb0);
+    vs.load(0, g.Lk, vb0);
+    if (g.nkt > 1) ks.load(1, g.Lk, kb1);
   }
   staged_barrier();
   const bool wave_live = w_lo < g.Lq;
+  const int w_last = min(w_lo + 31, g.Lq - 1) + g.off;  // last key any row of this wavefront sees
+  f32x16 s0[S::KB], s1[S::KB];
+  if (g.nkt > 0 && wave_live && (!CAUSAL || 0 <= w_last)) tile_qk<T, D, BK>(s0, kb0, o, st);
   for (int kt = 0; kt < g.nkt; kt += 2) {
-    tile_step<T, D, BK, CAUSAL>(kt, buf0, buf1, ks, vs, st, o, g, wave_live, w_lo, qrow, h, a.c);
-    if (kt + 1 < g.nkt) tile_step<T, D, BK, CAUSAL>(kt + 1, buf1, buf0, ks, vs, st, o, g, wave_live, w_lo, qrow, h, a.c);
+    pipe_step<T, D, BK, CAUSAL>(kt, kb1, vb0, kb0, vb1, s0, s1, ks, vs, st, o, g, wave_live, w_last, w_lo, qrow,
+                                h, a.c);
+    if (kt + 1 < g.nkt)
+      pipe_step<T, D, BK, CAUSAL>(kt + 1, kb0, vb1, kb1, vb0, s1, s0, ks, vs, st, o, g, wave_live, w_last, w_lo,
+                                  qrow, h, a.c);
   }
   epilogue<T, D>(st, g, a.Tq, qrow, h);
 }
@@ -479,7 +526,7 @@ static hipError_t launch_D(const PrefillArgs& a, hipStream_t stream) {
 template <class T>
 static hipError_t launch_t(const PrefillArgs& a, int D, bool causal, hipStream_t stream) {
   if (D == 128) return causal ? launch_D<T, 128, 64, true>(a, stream) : launch_D<T, 128, 64, false>(a, stream);
-  return causal ? launch_D<T, 64, 128, true>(a, stream) : launch_D<T, 64, 128, false>(a, stream);
+  return causal ? launch_D<T, 64, 64, true>(a, stream) : launch_D<T, 64, 64, false>(a, stream);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int D, bool causal, hipStream_t stream) {
