@@ -303,25 +303,31 @@ template <class T, int D, int BK>
 __device__ __forceinline__ void softmax_exp(const f32x16 (&sacc)[BK / 32], u32x4 (&pf)[BK / 16], Acc<D>& st,
                                             float msub, float cexp) {
   using S = Shape<D, BK>;
-  float lsum = 0.f, lrsum = 0.f;
+  // one partial sum per 8 probabilities keeps the dependency chains short, so
+  // the work interleaves with the matrix instructions of the next tile
+  float lsum[S::PS], lrsum[S::PS];
 #pragma unroll
   for (int kb = 0; kb < S::KB; ++kb)
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
+      const int i = kb * 2 + hf;
       float p[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[e] = fast_exp2(__builtin_fmaf(sacc[kb][8 * hf + e], cexp, -msub));
-        lsum += p[e];
-      }
+      for (int e = 0; e < 8; ++e) p[e] = fast_exp2(__builtin_fmaf(sacc[kb][8 * hf + e], cexp, -msub));
+      lsum[i] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
       const u32x4 pk = {T::pack2(p[0], p[1]), T::pack2(p[2], p[3]), T::pack2(p[4], p[5]), T::pack2(p[6], p[7])};
       // the normaliser adds the rounded probabilities the P.V product uses
-#pragma unroll
-      for (int e = 0; e < 4; ++e) lrsum = T::sum2(pk[e], lrsum);
-      pf[kb * 2 + hf] = pk;
+      lrsum[i] = T::sum2(pk[3], T::sum2(pk[2], T::sum2(pk[1], T::sum2(pk[0], 0.f))));
+      pf[i] = pk;
     }
-  st.l += lsum;
-  st.lr += lrsum;
+  float ls = 0.f, lrs = 0.f;
+#pragma unroll
+  for (int i = 0; i < S::PS; ++i) {
+    ls += lsum[i];
+    lrs += lrsum[i];
+  }
+  st.l += ls;
+  st.lr += lrs;
 }
 
 // O = O^T / l, lse = (m + log2 l) ln 2; padding rows -> 0, -inf.
