@@ -182,10 +182,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   for (int i = 0; i < kSplitBlocks; ++i) phys[i] = trow[min(blk0 + i, a.max_blocks - 1)];
   // materialise the entries here (one wait for all) rather than letting the
   // compiler sink each load into the branch that uses it
-  asm volatile("" ::"s"(phys[0]), "s"(phys[1]), "s"(phys[2]), "s"(phys[3]), "s"(phys[4]), "s"(phys[5]),
-               "s"(phys[6]), "s"(phys[7]));
-  asm volatile("" ::"s"(phys[8]), "s"(phys[9]), "s"(phys[10]), "s"(phys[11]), "s"(phys[12]), "s"(phys[13]),
-               "s"(phys[14]), "s"(phys[15]));
+  static_assert(kSplitBlocks % 8 == 0, "split length");
+#pragma unroll
+  for (int i = 0; i < kSplitBlocks; i += 8)
+    asm volatile("" ::"s"(phys[i]), "s"(phys[i + 1]), "s"(phys[i + 2]), "s"(phys[i + 3]), "s"(phys[i + 4]),
+                 "s"(phys[i + 5]), "s"(phys[i + 6]), "s"(phys[i + 7]));
   const int ctx = a.ctx[b];
   const int nblk = (ctx + kDecodeBlock - 1) / kDecodeBlock;
   const int nsp = (nblk + kSplitBlocks - 1) / kSplitBlocks;
