@@ -36,69 +36,142 @@
 namespace attn {
 
 constexpr float kDecodeLazy = 8.0f;
+constexpr int kDecodeDword3 = 0x00020000;  // raw (untyped) buffer descriptor, 32-bit data
 
-// Registers of one pair of cache blocks: K as the A operand of S^T (lane
-// (g, c): token c, columns 32s + 8g .. +8 of step s), V as 16-byte rows
-// (lane (g, c): tokens 4g + e of each block, columns VC*c .. +VC).
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// LDS image of one pair of cache blocks: K block 0, K block 1, V block 0,
+// V block 1, each 16 token rows of RB bytes, row-major with a 16-byte-chunk
+// XOR swizzle: chunk c of row r sits in slot c ^ f(r). LDS serves 256 bytes
+// per cycle (16 lanes of a 16-byte access, 32 lanes of an 8-byte one); f makes
+// the K operand reads (16 rows, one chunk) and the transposing V reads (8 rows
+// x 2 chunks per 32 lanes) hit distinct banks.
 template <int D>
-struct PairRegs {
-  static constexpr int KS = D / 32;
-  typedef uint32_t vchunk __attribute__((ext_vector_type(D / 32)));
-  u32x4 k[2][KS];
-  vchunk v[8];
+struct PairLds {
+  static constexpr int RB = 2 * D;           // bytes per token row
+  static constexpr int BLK = 16 * RB;        // one (block, kv head) of K or V
+  static constexpr int BYTES = 4 * BLK;
+  static constexpr int RPI = 1024 / RB;      // rows filled by one wavefront load instruction
+  static constexpr int NI = 16 / RPI;        // load instructions per block
+  static constexpr int C8 = D / 8;           // 16-byte chunks per row
+  static constexpr int LOADS = 4 * NI;       // load instructions per pair
 };
 
-// A K load instruction reads 64 contiguous bytes of each of 16 token rows, so
-// each 128-byte line is requested by two consecutive instructions: K keeps the
-// normal cache policy so that the second one hits. A V load instruction reads
-// whole rows, so V is streamed with non-temporal loads. The second block of
-// the pair may lie beyond the sequence's last block (live1 == false): it then
-// re-reads the first block (a cache hit) instead of branching, since every
-// token there is >= ctx and is masked (scores) or zeroed (V rows) anyway;
-// loads on both sides of a branch would cost register copies that wait for
-// the loads in flight.
 template <int D>
-__device__ __forceinline__ void load_pair(PairRegs<D>& P, const uint16_t* kbase, const uint16_t* vbase,
-                                          size_t block_stride, int ph0, int ph1, bool live1, int g, int c) {
-  typedef typename PairRegs<D>::vchunk vchunk;
+__device__ __forceinline__ int dswz(int row) {
+  if constexpr (D == 128) return ((row & 7) << 1) | ((row >> 3) & 1);
+  else return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
+}
+
+// Per-lane byte offsets, identical for every pair.
+template <int D>
+struct DecOffs {
+  int ld[PairLds<D>::NI];  // chunk fetched by load instruction i (within a block)
+  int k[D / 32];           // K operand of k-step s
+  int v[D / 16];           // V^T operand of product n (first of two 8-byte reads)
+};
+
+template <int D>
+__device__ __forceinline__ void make_dec_offs(DecOffs<D>& o, int lane) {
+  using L = PairLds<D>;
+  const int g = lane >> 4, c = lane & 15;
+  // load instruction i writes rows RPI*i .. (1 KiB of consecutive LDS, lane l
+  // at 16 l): lane l fetches the logical chunk its slot holds
+#pragma unroll
+  for (int i = 0; i < L::NI; ++i) {
+    const int row = L::RPI * i + lane / L::C8;
+    o.ld[i] = row * L::RB + 16 * ((lane % L::C8) ^ dswz<D>(row));
+  }
+  // K operand (A of S^T = K Q^T): lane (g, c) takes token c, columns
+  // 32s + 8g .. +8, i.e. chunk 4s + g
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s) o.k[s] = c * L::RB + 16 * ((4 * s + g) ^ dswz<D>(c));
+  // V^T operand of product n (B of O += P V, columns 16n .. 16n + 15): in
+  // each 16-lane group g, lane i = a + 4e addresses token row 4g + e at
+  // columns 16n + 4a .. +4 and receives column 16n + i of those 4 rows
+  const int i = lane & 15, a4 = i & 3, row = 4 * g + (i >> 2);
+#pragma unroll
+  for (int n = 0; n < D / 16; ++n) o.v[n] = row * L::RB + 16 * ((2 * n + (a4 >> 1)) ^ dswz<D>(row)) + 8 * (a4 & 1);
+}
+
+// Starts the loads of one pair of blocks (K and V of both) into an LDS pair
+// buffer: buffer loads that write LDS directly, each instruction 1 KiB of
+// consecutive bytes of one block (whole rows). The second block may lie past
+// the sequence's last block (live1 == false): it then re-reads the first one
+// (a cache hit), since every token there is masked or zeroed anyway, which
+// keeps the number of loads per pair fixed for the in-order memory counter.
+template <int D>
+__device__ __forceinline__ void load_pair(char* buf, const uint16_t* kbase, const uint16_t* vbase,
+                                          size_t block_stride, int ph0, int ph1, bool live1, const DecOffs<D>& o) {
+  using L = PairLds<D>;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const size_t off = (size_t)(j && live1 ? ph1 : ph0) * block_stride;
-    const uint16_t* kb = kbase + off;
-    const uint16_t* vb = vbase + off;
 #pragma unroll
-    for (int s = 0; s < PairRegs<D>::KS; ++s)
-      P.k[j][s] = *reinterpret_cast<const u32x4*>(kb + c * D + 32 * s + 8 * g);
+    for (int kv = 0; kv < 2; ++kv) {
+      const uint64_t p = reinterpret_cast<uint64_t>((kv ? vbase : kbase) + off);
+      // uniform by construction; readfirstlane keeps the descriptor scalar
+      const uint64_t pu = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(p >> 32)) << 32) |
+                          (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+      const __amdgpu_buffer_rsrc_t rsrc =
+          __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(pu), (short)0, L::BLK, kDecodeDword3);
+      char* dst = buf + (2 * kv + j) * L::BLK;
+      // the host compilation pass of this file does not know this builtin (it
+      // would drop the kernels' host stubs); the function only runs on the device
+#if defined(__HIP_DEVICE_COMPILE__)
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      P.v[4 * j + e] = __builtin_nontemporal_load(reinterpret_cast<const vchunk*>(vb + (4 * g + e) * D + (D / 16) * c));
+      for (int i = 0; i < L::NI; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + i * 1024), 16, o.ld[i], 0, 0,
+                                                 /*non-temporal*/ 2);
+#else
+      (void)rsrc;
+      (void)dst;
+#endif
+    }
   }
 }
 
 // Online-softmax state of one wavefront: per lane, head c's running max (log2
 // units), the fp32 sum of p and the sum of the rounded p over the lane's
-// tokens; the accumulator rows are heads 4g + r, columns VC*c + n.
+// tokens; the accumulator rows are heads 4g + r, product n covers columns
+// 16n .. 16n + 15 (lane c: column 16n + c).
 template <int D>
 struct WaveState {
   f32x4 o[D / 16];
   float m, l, lr;
 };
 
-// One step: the 32 tokens starting at t0. In the sequence's last pair (TAIL)
-// tokens >= ctx are masked and their V rows zeroed, since unused cache slots
-// may hold anything, NaN included.
+// One step: the 32 tokens starting at t0, from an LDS pair buffer. In the
+// sequence's last pair (TAIL) tokens >= ctx are masked, and their V rows are
+// zeroed in LDS first, since unused cache slots may hold anything, NaN
+// included.
 template <class T, int D, bool TAIL>
-__device__ __forceinline__ void pair_step(WaveState<D>& st, PairRegs<D>& P, const u32x4 (&qf)[D / 32], int t0,
-                                          int ctx, float cexp, int g) {
+__device__ __forceinline__ void pair_step(WaveState<D>& st, char* buf, const u32x4 (&qf)[D / 32],
+                                          const DecOffs<D>& o, int t0, int ctx, float cexp, int lane) {
+  using L = PairLds<D>;
   constexpr int KS = D / 32;
   constexpr int VC = D / 16;
-  typedef typename PairRegs<D>::vchunk vchunk;
+  const int g = lane >> 4;
+  if constexpr (TAIL) {
+    // whole rows: the swizzle only permutes chunks within a row
+#pragma unroll
+    for (int k = 0; k < 32 * L::C8 / 64; ++k) {
+      const int idx = lane + 64 * k;
+      const int row = idx / L::C8;  // 0..31 over the two blocks
+      if (t0 + row >= ctx)
+        *reinterpret_cast<u32x4*>(buf + 2 * L::BLK + (row >> 4) * L::BLK + (row & 15) * L::RB + 16 * (idx % L::C8)) =
+            u32x4{0, 0, 0, 0};
+    }
+  }
   f32x4 sacc[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     sacc[j] = f32x4{};
 #pragma unroll
-    for (int s = 0; s < KS; ++s) sacc[j] = T::mfma16(P.k[j][s], qf[s], sacc[j]);
+    for (int s = 0; s < KS; ++s)
+      sacc[j] = T::mfma16(*reinterpret_cast<const u32x4*>(buf + j * L::BLK + o.k[s]), qf[s], sacc[j]);
   }
   if constexpr (TAIL) {
 #pragma unroll
@@ -106,9 +179,6 @@ __device__ __forceinline__ void pair_step(WaveState<D>& st, PairRegs<D>& P, cons
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         sacc[j][r] = (t0 + 16 * j + 4 * g + r) >= ctx ? -__builtin_inff() : sacc[j][r];
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      P.v[e] = (t0 + 16 * (e >> 2) + 4 * g + (e & 3)) < ctx ? P.v[e] : vchunk{};
   }
   float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
                    fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
@@ -143,26 +213,29 @@ __device__ __forceinline__ void pair_step(WaveState<D>& st, PairRegs<D>& P, cons
   // the running sum adds the rounded probabilities that the P.V product applies
 #pragma unroll
   for (int e = 0; e < 4; ++e) st.lr = T::sum2(pf[e], st.lr);
-  // V operand of product n: element e = V[token e][VC*c + n]
+  // P's k order in lane group g: tokens 4g .. 4g+3 of block 0, then of block 1;
+  // the two transposing reads give V in the same order
 #pragma unroll
   for (int n = 0; n < VC; ++n) {
-    const int dw = n >> 1;
-    u32x4 vf;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t x0 = P.v[2 * k][dw], x1 = P.v[2 * k + 1][dw];
-      vf[k] = (n & 1) ? pack_hi16(x0, x1) : pack_lo16(x0, x1);
-    }
-    st.o[n] = T::mfma16(pf, vf, st.o[n]);
+    const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(buf + 2 * L::BLK + o.v[n]));
+    const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(buf + 3 * L::BLK + o.v[n]));
+    const u32x2 a0 = __builtin_bit_cast(u32x2, v0);
+    const u32x2 a1 = __builtin_bit_cast(u32x2, v1);
+    st.o[n] = T::mfma16(pf, u32x4{a0[0], a0[1], a1[0], a1[1]}, st.o[n]);
   }
 }
 
 template <class T, int D>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
+  using L = PairLds<D>;
   constexpr int KS = D / 32;
   constexpr int VC = D / 16;
   constexpr int NP = kSplitBlocks / 2;  // block pairs per split
   static_assert(D == 128 || D == 64, "head size");
+  // two pair buffers, separate LDS arrays so that reads of one are never
+  // ordered behind the loads into the other
+  __shared__ __align__(16) char buf0[L::BYTES];
+  __shared__ __align__(16) char buf1[L::BYTES];
 
   const int split = blockIdx.x;
   const int kvh = blockIdx.y;
@@ -174,7 +247,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   const int blk0 = split * kSplitBlocks;
   const int* trow = a.table + (size_t)b * a.max_blocks;
 
-  // The split's 16 block-table entries are read together with the context
+  // The split's block-table entries are read together with the context
   // length (scalar loads, one round trip); entries at or beyond the sequence's
   // end are read only if they exist in the table and never used.
   int phys[kSplitBlocks];
@@ -204,6 +277,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   const size_t block_stride = (size_t)a.Hkv * head_stride;
   const uint16_t* kbase = static_cast<const uint16_t*>(a.kc) + kvh * head_stride;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.vc) + kvh * head_stride;
+  DecOffs<D> o;
+  make_dec_offs<D>(o, lane);
 
   // ---- q^T operand: head c, columns 32s + 8g .. +8 (step s, lane group g);
   // loaded first: the memory counter is in order, so the first step then waits
@@ -222,17 +297,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   }
 
   // Pair q's table entries; a pair beyond the split (q >= np) re-reads pair 0
-  // (cache hits) so that every load is unconditional: the hardware counts
-  // loads in order, and paths with different numbers of loads in flight would
-  // make the waits before the MFMAs conservative.
+  // (cache hits) so that every pair issues the same loads.
   auto ph = [&](int q, int j) { return q < np ? phys[2 * q + j] : phys[0]; };
-  // The scheduling barriers keep the load groups in this order (the scheduler
-  // would otherwise interleave them and the first step would wait for all).
-  PairRegs<D> P0, P1;
+  // The scheduling barriers keep q's loads and the two pairs' loads in this
+  // order (the memory counter is in order; the waits below rely on it).
   __builtin_amdgcn_sched_barrier(0);
-  load_pair<D>(P0, kbase, vbase, block_stride, phys[0], phys[1], nb > 1, g, c);
+  load_pair<D>(buf0, kbase, vbase, block_stride, phys[0], phys[1], nb > 1, o);
   __builtin_amdgcn_sched_barrier(0);
-  load_pair<D>(P1, kbase, vbase, block_stride, ph(1, 0), ph(1, 1), 3 < nb, g, c);
+  load_pair<D>(buf1, kbase, vbase, block_stride, ph(1, 0), ph(1, 1), 3 < nb, o);
   __builtin_amdgcn_sched_barrier(0);
 
   WaveState<D> st;
@@ -245,15 +317,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     if (p >= np) break;  // wave-uniform
-    PairRegs<D>& P = (p & 1) ? P1 : P0;
+    char* buf = (p & 1) ? buf1 : buf0;
+    // pair p has landed once at most the next pair's loads are outstanding
+    if (p + 1 < NP)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L::LOADS) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     const int t0 = (blk0 + 2 * p) * kDecodeBlock;
     if (t0 + 32 > ctx)
-      pair_step<T, D, true>(st, P, qf, t0, ctx, a.c, g);
+      pair_step<T, D, true>(st, buf, qf, o, t0, ctx, a.c, lane);
     else
-      pair_step<T, D, false>(st, P, qf, t0, ctx, a.c, g);
+      pair_step<T, D, false>(st, buf, qf, o, t0, ctx, a.c, lane);
     if (p + 2 < NP) {
+      // every read of this buffer has returned before new data is written to it
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       const int q = p + 2 < NP ? p + 2 : 0;  // in range also where the branch is dead
-      load_pair<D>(P, kbase, vbase, block_stride, ph(q, 0), ph(q, 1), 2 * q + 1 < nb, g, c);
+      load_pair<D>(buf, kbase, vbase, block_stride, ph(q, 0), ph(q, 1), 2 * q + 1 < nb, o);
     }
   }
 
@@ -269,24 +348,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     const float inv = 1.f / __shfl(lr_head, h);  // > 0: the split holds a visible token
     if (h < G) {
       const int hq = kvh * G + h;
-      float val[VC];
-#pragma unroll
-      for (int n = 0; n < VC; ++n) val[n] = st.o[n][r] * inv;
       if (single) {
-        uint32_t pk[VC / 2];
+        uint16_t* op = static_cast<uint16_t*>(a.o) + ((size_t)b * a.Hq + hq) * D + c;
 #pragma unroll
-        for (int n = 0; n < VC / 2; ++n) pk[n] = T::pack2(val[2 * n], val[2 * n + 1]);
-        uint16_t* op = static_cast<uint16_t*>(a.o) + ((size_t)b * a.Hq + hq) * D + VC * c;
-        if constexpr (VC == 8) {
-          *reinterpret_cast<u32x4*>(op) = u32x4{pk[0], pk[1], pk[2], pk[3]};
-        } else {
-          *reinterpret_cast<u32x2*>(op) = u32x2{pk[0], pk[1]};
-        }
+        for (int n = 0; n < VC; ++n) op[16 * n] = (uint16_t)(T::pack2(st.o[n][r] * inv, 0.f) & 0xffffu);
       } else {
-        float* wp = a.ws + (((size_t)b * a.Hq + hq) * a.nsplit + split) * (D + 4) + VC * c;
+        float* wp = a.ws + (((size_t)b * a.Hq + hq) * a.nsplit + split) * (D + 4) + c;
 #pragma unroll
-        for (int n = 0; n < VC; n += 4)
-          *reinterpret_cast<f32x4*>(wp + n) = f32x4{val[n], val[n + 1], val[n + 2], val[n + 3]};
+        for (int n = 0; n < VC; ++n) wp[16 * n] = st.o[n][r] * inv;
       }
     }
   }
