@@ -44,9 +44,6 @@ struct BF16 {
     f32x2 v = {lo, hi};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
   }
-  static __device__ __forceinline__ float to_f32(uint16_t x) {
-    return __builtin_bit_cast(float, (uint32_t)x << 16);
-  }
   // acc + lo + hi of a packed pair (v_dot2c_f32_bf16 against {1, 1}): sums the
   // rounded values exactly as the matrix core sees them
   static __device__ __forceinline__ float sum2(uint32_t pk, float acc) {
@@ -67,9 +64,6 @@ struct F16 {
   static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     f32x2 v = {lo, hi};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
-  }
-  static __device__ __forceinline__ float to_f32(uint16_t x) {
-    return (float)__builtin_bit_cast(_Float16, x);
   }
   static __device__ __forceinline__ float sum2(uint32_t pk, float acc) {
     const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
@@ -93,15 +87,6 @@ __device__ __forceinline__ float half_swap_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
-
-// Byte-select helper (v_perm_b32): result byte i = sel byte i picks from {hi:lo}.
-__device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
-  return __builtin_amdgcn_perm(hi, lo, sel);
-}
-// low 16 bits of a and low 16 bits of b -> {b.lo, a.lo}
-__device__ __forceinline__ uint32_t pack_lo16(uint32_t a, uint32_t b) { return perm_b32(b, a, 0x05040100u); }
-// high 16 bits of a and high 16 bits of b -> {b.hi, a.hi}
-__device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) { return perm_b32(b, a, 0x07060302u); }
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
