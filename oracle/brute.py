@@ -71,3 +71,29 @@ def decode_paged(q, k_cache, v_cache, block_table, ctx_lens, scale):
             vals = [vc[bt[b][t // blk]][kh][t % blk] for t in range(L)]
             o[b][h], lse[b][h] = _row(q[b][h], keys, vals, scale)
     return np.array(o), np.array(lse)
+
+
+def prefill_paged(q, k_cache, v_cache, block_table, ctx_lens, q_lens, scale, causal=True):
+    """Chunked prefill through the paged cache, one scalar at a time."""
+    q = np.asarray(q, dtype=np.float64).tolist()
+    kc = np.asarray(k_cache, dtype=np.float64).tolist()
+    vc = np.asarray(v_cache, dtype=np.float64).tolist()
+    bt = np.asarray(block_table).tolist()
+    scale = float(np.float32(scale))
+    B, Hq, Tq, D = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
+    Hkv, blk = len(kc[0]), len(kc[0][0])
+    G = Hq // Hkv
+    o = [[[[0.0] * D for _ in range(Tq)] for _ in range(Hq)] for _ in range(B)]
+    lse = [[[-math.inf] * Tq for _ in range(Hq)] for _ in range(B)]
+    for b in range(B):
+        L = int(ctx_lens[b])
+        n = Tq if q_lens is None else int(q_lens[b])
+        for h in range(Hq):
+            kh = h // G
+            for i in range(n):
+                pos = L - n + i  # this query's own position
+                vis = [t for t in range(L) if (not causal) or t <= pos]
+                keys = [kc[bt[b][t // blk]][kh][t % blk] for t in vis]
+                vals = [vc[bt[b][t // blk]][kh][t % blk] for t in vis]
+                o[b][h][i], lse[b][h][i] = _row(q[b][h][i], keys, vals, scale)
+    return np.array(o), np.array(lse)

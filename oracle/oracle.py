@@ -43,7 +43,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = ["scale64", "head_rows", "prefill", "prefill_rows", "probs", "decode_paged",
-           "gather_paged", "combine"]
+           "gather_paged", "combine", "prefill_paged", "cache_append"]
 
 
 def scale64(scale: float) -> float:
@@ -225,3 +225,58 @@ def combine(o_parts, lse_parts):
     wn = np.where(fin, w / np.where(fin, W, 1.0), 0.0)
     o = (wn[..., None] * o_parts).sum(axis=0)
     return o, lse
+
+
+def prefill_paged(q, k_cache, v_cache, block_table, ctx_lens, q_lens, scale, causal=True):
+    """Chunked prefill through the paged cache. Returns (o [B,Hq,Tq,D], lse [B,Hq,Tq]).
+
+    Row i of q[b] (i < q_lens[b]) is position ctx_lens[b] - q_lens[b] + i of
+    sequence b: the newest q_lens[b] positions, whose keys/values are already
+    in the cache. Keys/values are positions 0 .. ctx_lens[b]-1, read through
+    the block table. With causal, row i sees keys j <= i + (ctx - q_len) (the
+    bottom-right alignment of the prefill definition); rows >= q_lens[b] are
+    padding (O = 0, lse = -inf). q_lens None means every row is a query.
+    """
+    B, Hq, Tq, _ = q.shape
+    Hkv, Dv = k_cache.shape[1], v_cache.shape[3]
+    G = Hq // Hkv
+    o = np.zeros((B, Hq, Tq, Dv))
+    lse = np.full((B, Hq, Tq), -np.inf)
+    for b in range(B):
+        Lk = int(ctx_lens[b])
+        Lq = Tq if q_lens is None else int(q_lens[b])
+        if Lq > Lk:
+            raise ValueError("q_lens[b] > ctx_lens[b]")
+        for kvh in range(Hkv):
+            K, V = gather_paged(k_cache, v_cache, block_table, Lk, b, kvh)
+            for g in range(G):
+                hq = kvh * G + g
+                ob, lb, _ = head_rows(q[b, hq], K, V, scale, causal, Lq, Lk, np.arange(Tq))
+                o[b, hq] = ob
+                lse[b, hq] = lb
+    return o, lse
+
+
+def cache_append(k_new, v_new, k_cache, v_cache, block_table, start_pos, new_lens=None):
+    """Write new tokens into copies of the paged caches and return them.
+
+    Token i < new_lens[b] of k_new[b] / v_new[b] ([B,Hkv,Tnew,D]) becomes
+    position start_pos[b] + i of sequence b: physical block
+    block_table[b, pos // block], slot pos % block (the address translation
+    of the paged cache). Nothing else changes.
+    """
+    kc = np.array(k_cache, copy=True)
+    vc = np.array(v_cache, copy=True)
+    B, Hkv, Tnew, _ = k_new.shape
+    block = kc.shape[2]
+    table = np.asarray(block_table)
+    for b in range(B):
+        n = Tnew if new_lens is None else int(new_lens[b])
+        pos = int(start_pos[b]) + np.arange(n)
+        phys = table[b, pos // block]
+        if n and (phys < 0).any():
+            raise ValueError("block table entry < 0 where a token is written")
+        for kvh in range(Hkv):
+            kc[phys, kvh, pos % block] = k_new[b, kvh, :n]
+            vc[phys, kvh, pos % block] = v_new[b, kvh, :n]
+    return kc, vc

@@ -413,3 +413,107 @@ def test_gqa_mapping_mistake_is_caught(monkeypatch):
     assert not np.allclose(o_wrong, _arr(case["o"]))
     o, _ = O.prefill(q, k, v, case["scale"])
     np.testing.assert_allclose(o, _arr(case["o"]), atol=1e-12)
+
+
+# ---------------------------------------------------------------- chunked prefill and append (paged cache)
+_CHUNK_TINY = [
+    W.ChunkCase("ct-a", B=3, Hq=4, Hkv=2, D=4, dtype="bf16", ctx_lo=0, ctx_hi=20, chunk_lo=1, chunk_hi=9, seed=51),
+    W.ChunkCase("ct-b", B=2, Hq=2, Hkv=2, D=4, dtype="fp16", ctx_lo=14, ctx_hi=18, chunk_lo=1, chunk_hi=3, seed=52),
+]
+
+
+@pytest.mark.parametrize("case", _CHUNK_TINY, ids=lambda c: c.name)
+@pytest.mark.parametrize("causal", [True, False])
+def test_brute_force_prefill_paged(case, causal):
+    """P-14: chunked prefill through the block table = scalar brute force (padding rows NaN)."""
+    x = W.chunk_inputs(case, nan_fill=False)
+    kc, vc = O.cache_append(x["k_new"], x["v_new"], x["k_cache"], x["v_cache"], x["block_table"],
+                            x["start_pos"], x["new_lens"])
+    q = x["q"].copy()
+    for b, n in enumerate(x["new_lens"]):
+        q[b, :, n:] = np.nan  # padding rows must not matter
+    o1, l1 = O.prefill_paged(q, kc, vc, x["block_table"], x["ctx_lens"], x["new_lens"], 0.7, causal)
+    o2, l2 = brute.prefill_paged(q, kc, vc, x["block_table"], x["ctx_lens"], x["new_lens"], 0.7, causal)
+    for b, n in enumerate(x["new_lens"]):
+        np.testing.assert_allclose(o1[b, :, :n], o2[b, :, :n], atol=1e-12)
+        np.testing.assert_allclose(l1[b, :, :n], l2[b, :, :n], atol=1e-12)
+        assert (o1[b, :, n:] == 0).all() and np.isneginf(l1[b, :, n:]).all()
+
+
+def test_prefill_paged_is_bottom_rows_of_contiguous_causal_prefill():
+    """P-15: the chunk's rows equal the last rows of a causal prefill over the whole sequence
+    laid out contiguously (checks the bottom-right alignment through the Tq == Tk path)."""
+    case = W.ChunkCase("p15", B=3, Hq=6, Hkv=2, D=8, dtype="bf16", ctx_lo=5, ctx_hi=60, chunk_lo=1, chunk_hi=30,
+                       seed=53)
+    x = W.chunk_inputs(case, nan_fill=True)
+    kc, vc = O.cache_append(x["k_new"], x["v_new"], x["k_cache"], x["v_cache"], x["block_table"],
+                            x["start_pos"], x["new_lens"])
+    o, lse = O.prefill_paged(x["q"], kc, vc, x["block_table"], x["ctx_lens"], x["new_lens"], case.scale)
+    for b in range(case.B):
+        L, n = int(x["ctx_lens"][b]), int(x["new_lens"][b])
+        K = np.stack([O.gather_paged(kc, vc, x["block_table"], L, b, h)[0] for h in range(2)])
+        V = np.stack([O.gather_paged(kc, vc, x["block_table"], L, b, h)[1] for h in range(2)])
+        assert np.isfinite(K).all() and np.isfinite(V).all()  # the append overwrote every NaN it had to
+        qf = np.zeros((1, 6, L, 8))
+        qf[0, :, L - n:] = x["q"][b, :, :n]
+        of, lf = O.prefill(qf, K[None], V[None], case.scale, causal=True)
+        np.testing.assert_allclose(o[b, :, :n], of[0, :, L - n:], atol=1e-13)
+        np.testing.assert_allclose(lse[b, :, :n], lf[0, :, L - n:], atol=1e-13)
+
+
+def test_prefill_paged_single_row_is_decode():
+    """P-16: a chunk of one token is the paged decode of that token."""
+    case = W.ChunkCase("p16", B=4, Hq=6, Hkv=3, D=8, dtype="bf16", ctx_lo=0, ctx_hi=50, chunk_lo=1, chunk_hi=1,
+                       seed=54)
+    x = W.chunk_inputs(case)
+    kc, vc = O.cache_append(x["k_new"], x["v_new"], x["k_cache"], x["v_cache"], x["block_table"],
+                            x["start_pos"], x["new_lens"])
+    o, lse = O.prefill_paged(x["q"], kc, vc, x["block_table"], x["ctx_lens"], x["new_lens"], case.scale)
+    od, ld = O.decode_paged(x["q"][:, :, 0], kc, vc, x["block_table"], x["ctx_lens"], case.scale)
+    np.testing.assert_allclose(o[:, :, 0], od, atol=1e-14)
+    np.testing.assert_allclose(lse[:, :, 0], ld, atol=1e-14)
+
+
+def test_cache_append_then_gather_is_concatenation():
+    """P-17: after appending, the gathered sequence is the old tokens followed by the new ones,
+    and no other slot of the cache changed (bit for bit)."""
+    case = W.ChunkCase("p17", B=5, Hq=2, Hkv=2, D=4, dtype="fp16", ctx_lo=0, ctx_hi=40, chunk_lo=1, chunk_hi=37,
+                       seed=55)
+    x = W.chunk_inputs(case, nan_fill=True)
+    kc, vc = O.cache_append(x["k_new"], x["v_new"], x["k_cache"], x["v_cache"], x["block_table"],
+                            x["start_pos"], x["new_lens"])
+    written = np.zeros(kc.shape[:3], dtype=bool)
+    for b in range(case.B):
+        s0, n = int(x["start_pos"][b]), int(x["new_lens"][b])
+        for h in range(2):
+            Kold, Vold = O.gather_paged(x["k_cache"], x["v_cache"], x["block_table"], s0, b, h)
+            Knew, Vnew = O.gather_paged(kc, vc, x["block_table"], s0 + n, b, h)
+            assert np.array_equal(Knew[:s0], Kold) and np.array_equal(Vnew[:s0], Vold)
+            assert np.array_equal(Knew[s0:], x["k_new"][b, h, :n]) and np.array_equal(Vnew[s0:], x["v_new"][b, h, :n])
+        pos = np.arange(s0, s0 + n)
+        written[x["block_table"][b, pos // 16], :, pos % 16] = True
+    same_k = (kc == x["k_cache"]) | (np.isnan(kc) & np.isnan(x["k_cache"]))
+    same_v = (vc == x["v_cache"]) | (np.isnan(vc) & np.isnan(x["v_cache"]))
+    assert same_k[~written].all() and same_v[~written].all()
+
+
+def test_sdpa_cross_check_prefill_paged():
+    """P-2 for the chunked form: torch SDPA (float64, CPU) on the gathered sequence with an explicit mask."""
+    torch = pytest.importorskip("torch")
+    case = W.ChunkCase("sdpa-chunk", B=3, Hq=8, Hkv=2, D=32, dtype="bf16", ctx_lo=10, ctx_hi=200, chunk_lo=1,
+                       chunk_hi=64, seed=56)
+    x = W.chunk_inputs(case)
+    kc, vc = O.cache_append(x["k_new"], x["v_new"], x["k_cache"], x["v_cache"], x["block_table"],
+                            x["start_pos"], x["new_lens"])
+    o, _ = O.prefill_paged(x["q"], kc, vc, x["block_table"], x["ctx_lens"], x["new_lens"], case.scale)
+    for b in range(case.B):
+        L, n = int(x["ctx_lens"][b]), int(x["new_lens"][b])
+        K = np.stack([O.gather_paged(kc, vc, x["block_table"], L, b, h)[0] for h in range(2)])
+        V = np.stack([O.gather_paged(kc, vc, x["block_table"], L, b, h)[1] for h in range(2)])
+        Kx = torch.from_numpy(np.repeat(K, 4, axis=0)).double()
+        Vx = torch.from_numpy(np.repeat(V, 4, axis=0)).double()
+        Q = torch.from_numpy(x["q"][b, :, :n]).double()
+        mask = torch.from_numpy(np.arange(L)[None, :] <= (np.arange(n)[:, None] + L - n))
+        ref = torch.nn.functional.scaled_dot_product_attention(Q, Kx, Vx, attn_mask=mask,
+                                                               scale=O.scale64(case.scale))
+        np.testing.assert_allclose(o[b, :, :n], ref.numpy(), atol=1e-10)

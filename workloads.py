@@ -78,6 +78,30 @@ class DecodeCase:
             self.scale = 1.0 / math.sqrt(self.D)
 
 
+@dataclass
+class ChunkCase:
+    """A chunked-prefill batch through the paged cache: each sequence already
+    holds ctx tokens (uniform in [ctx_lo, ctx_hi]) and receives a chunk of n new
+    tokens (uniform in [chunk_lo, chunk_hi]); queries are padded to Tq = chunk_hi."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    dtype: str
+    ctx_lo: int
+    ctx_hi: int
+    chunk_lo: int
+    chunk_hi: int
+    seed: int
+    spare_blocks: int = 8
+    scale: float = field(default=0.0)
+
+    def __post_init__(self):
+        if self.scale == 0.0:
+            self.scale = 1.0 / math.sqrt(self.D)
+
+
 # The five measured cases.
 TINY = PrefillCase("tiny fp16 1x1x128x64", B=1, Hq=1, Hkv=1, T=128, D=64, dtype="fp16",
                    causal=False, ragged=False, seed=1)
@@ -160,6 +184,72 @@ def decode_inputs(case: DecodeCase, nan_fill: bool = False, ctx_lens=None):
         kc[used:] = np.nan
         vc[used:] = np.nan
     return dict(q=q, k_cache=kc, v_cache=vc, block_table=table, ctx_lens=ctx)
+
+
+def chunk_inputs(case: ChunkCase, nan_fill: bool = False):
+    """Return dict(q, k_new, v_new, k_cache, v_cache, block_table, start_pos, new_lens, ctx_lens).
+
+    Draw order: context lengths before the chunk, chunk lengths, a permutation
+    of the physical blocks (enough for context + chunk), then q [B,Hq,Tq,D],
+    k_new / v_new [B,Hkv,Tq,D] and the caches (N(0,1)). The caches hold
+    values at every slot, the chunk's own positions included: appending the
+    chunk overwrites them. ctx_lens = start_pos + new_lens. With ``nan_fill``
+    the chunk's positions in the cache, the tail of each last block, the spare
+    blocks and the padded rows of q / k_new / v_new hold NaN.
+    """
+    rng = np.random.default_rng(case.seed)
+    start = rng.integers(case.ctx_lo, case.ctx_hi + 1, case.B).astype(np.int32)
+    n = rng.integers(case.chunk_lo, case.chunk_hi + 1, case.B).astype(np.int32)
+    total = start + n
+    nblk = (total + BLOCK - 1) // BLOCK
+    used = int(nblk.sum())
+    NB = used + case.spare_blocks
+    perm = rng.permutation(used).astype(np.int32)
+    max_blocks = int(-(-(case.ctx_hi + case.chunk_hi) // BLOCK))
+    table = np.full((case.B, max_blocks), -1, dtype=np.int32)
+    off = 0
+    for b in range(case.B):
+        table[b, : nblk[b]] = perm[off: off + nblk[b]]
+        off += nblk[b]
+    Tq = case.chunk_hi
+    q = rng.standard_normal((case.B, case.Hq, Tq, case.D), dtype=np.float32)
+    kn = rng.standard_normal((case.B, case.Hkv, Tq, case.D), dtype=np.float32)
+    vn = rng.standard_normal((case.B, case.Hkv, Tq, case.D), dtype=np.float32)
+    kc = rng.standard_normal((NB, case.Hkv, BLOCK, case.D), dtype=np.float32)
+    vc = rng.standard_normal((NB, case.Hkv, BLOCK, case.D), dtype=np.float32)
+    q, kn, vn, kc, vc = (round_to(a, case.dtype) for a in (q, kn, vn, kc, vc))
+    if nan_fill:
+        for b in range(case.B):
+            q[b, :, n[b]:] = np.nan
+            kn[b, :, n[b]:] = np.nan
+            vn[b, :, n[b]:] = np.nan
+            pos = np.arange(start[b], total[b])
+            kc[table[b, pos // BLOCK], :, pos % BLOCK] = np.nan
+            vc[table[b, pos // BLOCK], :, pos % BLOCK] = np.nan
+            tail = int(total[b]) % BLOCK
+            if tail:
+                last = table[b, nblk[b] - 1]
+                kc[last, :, tail:, :] = np.nan
+                vc[last, :, tail:, :] = np.nan
+        kc[used:] = np.nan
+        vc[used:] = np.nan
+    return dict(q=q, k_new=kn, v_new=vn, k_cache=kc, v_cache=vc, block_table=table, start_pos=start,
+                new_lens=n, ctx_lens=total)
+
+
+def chunk_flops(ctx_lens, q_lens, Hq, D, causal=True):
+    """Algorithmic flops of a chunked prefill: 4*D per visible (query, key) pair."""
+    pairs = 0
+    for L, n in zip(np.asarray(ctx_lens), np.asarray(q_lens)):
+        L, n = int(L), int(n)
+        pairs += sum(L - n + i + 1 for i in range(n)) if causal else n * L
+    return 4.0 * D * Hq * pairs
+
+
+def append_bytes(new_lens, Hkv, D, elem=2):
+    """Algorithmic HBM bytes of an append: the new K and V read once and written once, plus table reads."""
+    n = int(np.asarray(new_lens, dtype=np.int64).sum())
+    return 2 * 2 * n * Hkv * D * elem
 
 
 def prefill_flops(B, Hq, Tq, Tk, D, causal, seq_lens=None):
