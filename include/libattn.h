@@ -114,6 +114,67 @@ attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_
                               attn_dtype dtype, void* workspace, size_t workspace_bytes,
                               hipStream_t stream);
 
+/*
+ * Chunked prefill through the paged KV cache: the prefill of the section cited
+ * above, with keys/values read through the block table of the paged cache
+ * (the address translation attn_decode_paged uses), so that a long prompt can
+ * be processed in chunks whose keys/values have already been appended to the
+ * cache (attn_cache_append), or one more chunk attends to a cached prefix.
+ *
+ *  q, o        : [B, Hq, Tq, D] elements of `dtype`. Row i < q_lens[b] of
+ *                sequence b is position ctx_lens[b] - q_lens[b] + i: the
+ *                newest q_lens[b] positions. Rows >= q_lens[b] are padding and
+ *                receive O = 0, lse = -inf.
+ *  k_cache,
+ *  v_cache     : [num_blocks, Hkv, block_size, D] as for attn_decode_paged;
+ *                the keys/values of positions 0 .. ctx_lens[b]-1 must be in
+ *                the cache (the chunk's own included).
+ *  block_table : device int32 [B, max_blocks_per_seq]; entries at or beyond
+ *                ceil(ctx_lens[b] / block_size) are never read; entries read
+ *                must lie in [0, num_blocks) (others are clamped into it).
+ *  ctx_lens    : device int32 [B]; q_lens[b] <= ctx_lens[b] <=
+ *                max_blocks_per_seq * block_size.
+ *  q_lens      : device int32 [B] with 0 <= q_lens[b] <= Tq, or NULL (every
+ *                row is a query: q_lens[b] = Tq).
+ *  lse         : [B, Hq, Tq] fp32 natural-log log-sum-exp; may be NULL.
+ *  causal      : nonzero -> row i sees keys j <= i + ctx_lens[b] - q_lens[b]
+ *                (the bottom-right alignment of attn_fwd); zero -> every row
+ *                sees all ctx_lens[b] keys.
+ *  block_size == 16, D in {64, 128}, Hq % Hkv == 0,
+ *  max_blocks_per_seq <= 2048 (contexts up to 32768 tokens: a workgroup keeps
+ *  the sequence's table row in on-chip memory). No workspace.
+ */
+attn_status attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache,
+                           const int* block_table, const int* ctx_lens, const int* q_lens,
+                           void* o, float* lse, int B, int Hq, int Hkv, int Tq, int D,
+                           int block_size, int max_blocks_per_seq, int num_blocks, float scale,
+                           int causal, attn_dtype dtype, hipStream_t stream);
+
+/*
+ * Appends new keys/values to the paged KV cache (the block/slot mapping of the
+ * paged cache of the section cited above): token i < new_lens[b] of k_new[b]
+ * and v_new[b] becomes position p = start_pos[b] + i of sequence b, written to
+ * physical block block_table[b, p / block_size], slot p % block_size. Nothing
+ * else in the caches changes. Pure data movement (bit-exact copies).
+ *
+ *  k_new, v_new: [B, Hkv, Tnew, D] elements of `dtype`.
+ *  k_cache,
+ *  v_cache     : [num_blocks, Hkv, block_size, D], updated in place.
+ *  block_table : device int32 [B, max_blocks_per_seq]; the blocks written must
+ *                be mapped (entries in [0, num_blocks)); a token whose position
+ *                falls outside the table or on an unmapped entry is not written.
+ *  start_pos   : device int32 [B], first position written (>= 0).
+ *  new_lens    : device int32 [B] with 0 <= new_lens[b] <= Tnew, or NULL (all
+ *                Tnew tokens).
+ *  block_size == 16, D in {64, 128}. Two sequences must not map a written slot
+ *  to the same physical block (the writes would race).
+ */
+attn_status attn_cache_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                              const int* block_table, const int* start_pos, const int* new_lens,
+                              int B, int Hkv, int Tnew, int D, int block_size,
+                              int max_blocks_per_seq, int num_blocks, attn_dtype dtype,
+                              hipStream_t stream);
+
 /* Workspace bytes attn_decode_paged needs for these sizes (0 if they are invalid). */
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_blocks_per_seq, int block_size);
 

@@ -84,6 +84,41 @@ def test_decode_rejects_before_launch(L, kw, code):
     assert ta.attn_last_error().startswith("attn_decode_paged:")
 
 
+def _pfw(L, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, cl=FAKE, ql=None, o=FAKE, lse=None, B=2, Hq=8, Hkv=2, Tq=64,
+         D=128, bs=16, maxb=64, nb=100, scale=0.1, causal=1, dtype=1):
+    return L.attn_fwd_paged(q, kc, vc, bt, cl, ql, o, lse, B, Hq, Hkv, Tq, D, bs, maxb, nb, ctypes.c_float(scale),
+                            causal, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(bt=None), 1), (dict(cl=None), 1), (dict(o=None), 1), (dict(Tq=0), 1),
+    (dict(nb=0), 1), (dict(Hq=7), 1), (dict(bs=8), 2), (dict(D=32), 2), (dict(dtype=3), 2),
+    (dict(maxb=2049), 2), (dict(scale=float("-inf")), 1), (dict(vc=FAKE_MIS), 1),
+    (dict(ql=ctypes.c_void_p(0x10002)), 1), (dict(cl=ctypes.c_void_p(0x10001)), 1),
+    (dict(B=1 << 14, Hq=1 << 10, Tq=1 << 10, Hkv=1), 2),
+])
+def test_paged_prefill_rejects_before_launch(L, kw, code):
+    import tiled_attention_02_amd as ta
+    assert _pfw(L, **kw) == code
+    assert ta.attn_last_error().startswith("attn_fwd_paged:")
+
+
+def _app(L, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sp=FAKE, nl=None, B=2, Hkv=2, Tnew=64, D=128, bs=16,
+         maxb=64, nb=100, dtype=1):
+    return L.attn_cache_append(kn, vn, kc, vc, bt, sp, nl, B, Hkv, Tnew, D, bs, maxb, nb, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kn=None), 1), (dict(vc=None), 1), (dict(bt=None), 1), (dict(sp=None), 1), (dict(Tnew=0), 1),
+    (dict(maxb=0), 1), (dict(bs=32), 2), (dict(D=100), 2), (dict(dtype=2), 2), (dict(kn=FAKE_MIS), 1),
+    (dict(nl=ctypes.c_void_p(0x10006)), 1), (dict(B=1 << 16), 2),
+])
+def test_append_rejects_before_launch(L, kw, code):
+    import tiled_attention_02_amd as ta
+    assert _app(L, **kw) == code
+    assert ta.attn_last_error().startswith("attn_cache_append:")
+
+
 def test_workspace_size(L):
     import tiled_attention_02_amd as ta
     # 256 blocks of 16 tokens -> 16 splits of 256 tokens, each partial holding D values + log-sum,

@@ -12,11 +12,13 @@ import ctypes
 import math
 import os
 
-__all__ = ["attn_fwd", "attn_decode_paged", "attn_decode_workspace_bytes", "attn_status_str",
-           "attn_last_error", "AttnError", "lib", "LIB_PATH", "EXPORTS", "BLOCK_SIZE", "decode_workspace"]
+__all__ = ["attn_fwd", "attn_decode_paged", "attn_fwd_paged", "attn_cache_append", "attn_decode_workspace_bytes",
+           "attn_status_str", "attn_last_error", "AttnError", "lib", "LIB_PATH", "EXPORTS", "BLOCK_SIZE",
+           "decode_workspace"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
-EXPORTS = ("attn_fwd", "attn_decode_paged", "attn_decode_workspace_bytes", "attn_status_str", "attn_last_error")
+EXPORTS = ("attn_fwd", "attn_decode_paged", "attn_fwd_paged", "attn_cache_append", "attn_decode_workspace_bytes",
+           "attn_status_str", "attn_last_error")
 BLOCK_SIZE = 16
 
 ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
@@ -45,6 +47,10 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd.restype = i
     L.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, sz, vp]
     L.attn_decode_paged.restype = i
+    L.attn_fwd_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, i, vp]
+    L.attn_fwd_paged.restype = i
+    L.attn_cache_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp]
+    L.attn_cache_append.restype = i
     L.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
     L.attn_decode_workspace_bytes.restype = sz
     L.attn_status_str.argtypes = [i]
@@ -176,3 +182,72 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, ctx_lens, scale: float |
                                  _stream(q.device))
     _raise(st)
     return out, lse
+
+
+def _check_paged(caches, dtype, D):
+    import torch
+    k_cache, v_cache = caches
+    _check(k_cache.dim() == 4 and v_cache.shape == k_cache.shape, "caches must be [num_blocks, Hkv, 16, D]")
+    _check(k_cache.dtype == dtype and v_cache.dtype == dtype, "caches must share the dtype of the inputs")
+    _check(k_cache.shape[3] == D, "head size mismatch")
+    _check(k_cache.is_cuda and v_cache.is_cuda and k_cache.is_contiguous() and v_cache.is_contiguous(),
+           "caches must be contiguous GPU tensors")
+    return k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+
+
+def _check_i32(t, n, name, optional=False):
+    import torch
+    if t is None:
+        _check(optional, f"{name} is required")
+        return
+    _check(t.is_cuda and t.dtype == torch.int32 and t.is_contiguous() and t.numel() == n,
+           f"{name} must be a contiguous int32 GPU tensor of {n} elements")
+
+
+def attn_fwd_paged(q, k_cache, v_cache, block_table, ctx_lens, q_lens=None, scale: float | None = None,
+                   causal: bool = True, out=None, lse=None, need_lse: bool = True):
+    """Chunked prefill through the paged cache. q [B,Hq,Tq,D]: row i of sequence b is position
+    ctx_lens[b] - q_lens[b] + i (q_lens None: all Tq rows). Returns (o like q, lse [B,Hq,Tq] or None)."""
+    import torch
+    dt = _dtype_code(q)
+    _check(q.is_cuda and q.dim() == 4 and q.is_contiguous(), "q must be a contiguous 4-D GPU tensor")
+    B, Hq, Tq, D = q.shape
+    NB, Hkv, bs = _check_paged((k_cache, v_cache), q.dtype, D)
+    _check(block_table.dim() == 2 and block_table.shape[0] == B, "block_table must be [B, max_blocks]")
+    _check_i32(block_table, block_table.numel(), "block_table")
+    _check_i32(ctx_lens, B, "ctx_lens")
+    _check_i32(q_lens, B, "q_lens", optional=True)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out.shape == q.shape and out.dtype == q.dtype and out.is_contiguous() and out.is_cuda, "bad out")
+    if need_lse and lse is None:
+        lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check(lse.shape == (B, Hq, Tq) and lse.dtype == torch.float32 and lse.is_contiguous(), "bad lse")
+    st = lib().attn_fwd_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(ctx_lens),
+                              _ptr(q_lens), _ptr(out), _ptr(lse), B, Hq, Hkv, Tq, D, bs, block_table.shape[1], NB,
+                              ctypes.c_float(scale), int(bool(causal)), dt, _stream(q.device))
+    _raise(st)
+    return out, lse
+
+
+def attn_cache_append(k_new, v_new, k_cache, v_cache, block_table, start_pos, new_lens=None):
+    """Write k_new/v_new [B,Hkv,Tnew,D] into the paged caches in place: token i < new_lens[b]
+    becomes position start_pos[b] + i of sequence b (new_lens None: all Tnew tokens)."""
+    dt = _dtype_code(k_new)
+    _check(k_new.is_cuda and k_new.dim() == 4 and v_new.shape == k_new.shape and v_new.dtype == k_new.dtype
+           and k_new.is_contiguous() and v_new.is_contiguous() and v_new.is_cuda,
+           "k_new / v_new must be contiguous GPU tensors of one shape [B,Hkv,Tnew,D]")
+    B, Hkv, Tnew, D = k_new.shape
+    NB, Hc, bs = _check_paged((k_cache, v_cache), k_new.dtype, D)
+    _check(Hc == Hkv, "kv head count mismatch")
+    _check(block_table.dim() == 2 and block_table.shape[0] == B, "block_table must be [B, max_blocks]")
+    _check_i32(block_table, block_table.numel(), "block_table")
+    _check_i32(start_pos, B, "start_pos")
+    _check_i32(new_lens, B, "new_lens", optional=True)
+    st = lib().attn_cache_append(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                 _ptr(start_pos), _ptr(new_lens), B, Hkv, Tnew, D, bs, block_table.shape[1], NB,
+                                 dt, _stream(k_new.device))
+    _raise(st)

@@ -22,7 +22,25 @@ struct PrefillArgs {
   float c;    // |scale| * log2(e), or 1 when scale == 0
   int qmode;
   int xcd_remap;  // set by the launcher: group kv-head siblings on one XCD
+  // paged form (chunked prefill): k / v are the caches [num_blocks][Hkv][16][D]
+  const int* table;     // [B][max_blocks]
+  const int* ctx_lens;  // [B] keys per sequence
+  const int* q_lens;    // [B] query rows per sequence, or null (all Tq)
+  int max_blocks, num_blocks;
 };
+
+struct AppendArgs {
+  const void* k_new;  // [B][Hkv][Tnew][D]
+  const void* v_new;
+  void* kc;           // [num_blocks][Hkv][16][D]
+  void* vc;
+  const int* table;   // [B][max_blocks]
+  const int* start;   // [B]
+  const int* new_lens;  // [B] or null (all Tnew)
+  int B, Hkv, Tnew, D, max_blocks, num_blocks;
+};
+
+constexpr int kMaxPagedPrefillBlocks = 2048;  // block-table entries a chunked prefill keeps in LDS
 
 struct DecodeArgs {
   const void* q;
@@ -44,6 +62,8 @@ constexpr int kDecodeBlock = 16;        // tokens per cache block
 constexpr int kSplitBlocks = 16;        // cache blocks per split (256 tokens)
 
 hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int D, bool causal, hipStream_t stream);
+hipError_t launch_prefill_paged(const PrefillArgs& a, bool bf16, int D, bool causal, hipStream_t stream);
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, bool bf16, hipStream_t stream);
 
 // Workspace: the per-split partials (Hkv is part of the signature so that a

@@ -100,6 +100,11 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
   a.G = Hq / Hkv;
   a.nqt = 0;
   a.xcd_remap = 0;
+  a.table = nullptr;
+  a.ctx_lens = nullptr;
+  a.q_lens = nullptr;
+  a.max_blocks = 0;
+  a.num_blocks = 0;
   scale_mode(scale, &a.c, &a.qmode);
   hipError_t e = attn::launch_prefill(a, dtype == ATTN_BF16, D, causal != 0, stream);
   if (e != hipSuccess) return fail(ATTN_ERR_HIP, "attn_fwd: launch failed: %s", hipGetErrorString(e));
@@ -169,6 +174,102 @@ attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_
   scale_mode(scale, &a.c, &a.qmode);
   hipError_t e = attn::launch_decode(a, dtype == ATTN_BF16, stream);
   if (e != hipSuccess) return fail(ATTN_ERR_HIP, "attn_decode_paged: launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+attn_status attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache, const int* block_table,
+                           const int* ctx_lens, const int* q_lens, void* o, float* lse, int B, int Hq, int Hkv,
+                           int Tq, int D, int block_size, int max_blocks_per_seq, int num_blocks, float scale,
+                           int causal, attn_dtype dtype, hipStream_t stream) {
+  if (!q || !k_cache || !v_cache || !block_table || !ctx_lens || !o)
+    return fail(ATTN_ERR_INVALID, "attn_fwd_paged: q, caches, block_table, ctx_lens and o must be non-null");
+  if (B < 1 || Hq < 1 || Hkv < 1 || Tq < 1 || D < 1 || max_blocks_per_seq < 1 || num_blocks < 1)
+    return fail(ATTN_ERR_INVALID, "attn_fwd_paged: sizes must be >= 1");
+  if (Hq % Hkv != 0) return fail(ATTN_ERR_INVALID, "attn_fwd_paged: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_paged: unknown dtype %d", (int)dtype);
+  if (block_size != attn::kDecodeBlock)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_paged: block_size=%d (supported: 16)", block_size);
+  if (D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_paged: head size D=%d (supported: 64, 128)", D);
+  if (max_blocks_per_seq > attn::kMaxPagedPrefillBlocks)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_paged: max_blocks_per_seq=%d (supported: <= %d)", max_blocks_per_seq,
+                attn::kMaxPagedPrefillBlocks);
+  if (!isfinite(scale)) return fail(ATTN_ERR_INVALID, "attn_fwd_paged: scale must be finite");
+  const double nq = (double)B * Hq * Tq * D, ncache = (double)num_blocks * Hkv * block_size * D;
+  if (nq >= 2147483648.0 || ncache >= 9.0e18 || (double)B * max_blocks_per_seq >= 2147483648.0)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_paged: sizes too large");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+    return fail(ATTN_ERR_INVALID, "attn_fwd_paged: q, caches and o must be 16-byte aligned");
+  if ((lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) || (reinterpret_cast<uintptr_t>(block_table) & 3u) ||
+      (reinterpret_cast<uintptr_t>(ctx_lens) & 3u) || (q_lens && (reinterpret_cast<uintptr_t>(q_lens) & 3u)))
+    return fail(ATTN_ERR_INVALID, "attn_fwd_paged: lse, block_table, ctx_lens and q_lens must be 4-byte aligned");
+
+  attn::PrefillArgs a;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.o = o;
+  a.lse = lse;
+  a.seq_lens = nullptr;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Tq = Tq;
+  a.Tk = 0;
+  a.G = Hq / Hkv;
+  a.nqt = 0;
+  a.xcd_remap = 0;
+  a.table = block_table;
+  a.ctx_lens = ctx_lens;
+  a.q_lens = q_lens;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  scale_mode(scale, &a.c, &a.qmode);
+  hipError_t e = attn::launch_prefill_paged(a, dtype == ATTN_BF16, D, causal != 0, stream);
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "attn_fwd_paged: launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+attn_status attn_cache_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                              const int* block_table, const int* start_pos, const int* new_lens, int B, int Hkv,
+                              int Tnew, int D, int block_size, int max_blocks_per_seq, int num_blocks,
+                              attn_dtype dtype, hipStream_t stream) {
+  if (!k_new || !v_new || !k_cache || !v_cache || !block_table || !start_pos)
+    return fail(ATTN_ERR_INVALID, "attn_cache_append: k_new, v_new, caches, block_table and start_pos must be non-null");
+  if (B < 1 || Hkv < 1 || Tnew < 1 || D < 1 || max_blocks_per_seq < 1 || num_blocks < 1)
+    return fail(ATTN_ERR_INVALID, "attn_cache_append: sizes must be >= 1");
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_cache_append: unknown dtype %d", (int)dtype);
+  if (block_size != attn::kDecodeBlock)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_cache_append: block_size=%d (supported: 16)", block_size);
+  if (D != 64 && D != 128)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_cache_append: head size D=%d (supported: 64, 128)", D);
+  const double nnew = (double)B * Hkv * Tnew * D, ncache = (double)num_blocks * Hkv * block_size * D;
+  if (nnew >= 2147483648.0 || ncache >= 9.0e18 || (double)B * max_blocks_per_seq >= 2147483648.0 || B > 65535 ||
+      Hkv > 65535)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_cache_append: sizes too large");
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(ATTN_ERR_INVALID, "attn_cache_append: k_new, v_new and the caches must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(start_pos) & 3u) ||
+      (new_lens && (reinterpret_cast<uintptr_t>(new_lens) & 3u)))
+    return fail(ATTN_ERR_INVALID, "attn_cache_append: block_table, start_pos and new_lens must be 4-byte aligned");
+
+  attn::AppendArgs a;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.kc = k_cache;
+  a.vc = v_cache;
+  a.table = block_table;
+  a.start = start_pos;
+  a.new_lens = new_lens;
+  a.B = B;
+  a.Hkv = Hkv;
+  a.Tnew = Tnew;
+  a.D = D;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  hipError_t e = attn::launch_append(a, stream);
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "attn_cache_append: launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

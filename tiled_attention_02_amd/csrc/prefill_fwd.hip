@@ -91,7 +91,7 @@ struct Geo {
   float* Lg;
 };
 
-template <int D, int BQ, int BK, bool CAUSAL>
+template <int D, int BQ, int BK, bool CAUSAL, bool PAGED>
 __device__ __forceinline__ Geo make_geo(const PrefillArgs& a) {
   Geo g;
   int id = blockIdx.x;
@@ -105,17 +105,27 @@ __device__ __forceinline__ Geo make_geo(const PrefillArgs& a) {
   g.hq = rem % a.Hq;
   g.b = rem / a.Hq;
   g.kvh = g.hq / a.G;
-  g.Lq = a.Tq;
-  g.Lk = a.Tk;
-  if (a.seq_lens) {
-    g.Lq = a.seq_lens[g.b];
-    g.Lk = g.Lq;
+  if constexpr (PAGED) {
+    // the newest Lq positions of a sequence of Lk cached tokens
+    // (clamped to what the table and q can hold, which keeps every access in bounds)
+    g.Lk = min(a.ctx_lens[g.b], a.max_blocks * 16);
+    g.Lq = a.q_lens ? min(a.q_lens[g.b], a.Tq) : a.Tq;
+    // block 0 of the kv head; the stager adds physical block offsets
+    g.Kg = static_cast<const uint16_t*>(a.k) + (size_t)g.kvh * 16 * D;
+    g.Vg = static_cast<const uint16_t*>(a.v) + (size_t)g.kvh * 16 * D;
+  } else {
+    g.Lq = a.Tq;
+    g.Lk = a.Tk;
+    if (a.seq_lens) {
+      g.Lq = a.seq_lens[g.b];
+      g.Lk = g.Lq;
+    }
+    g.Kg = static_cast<const uint16_t*>(a.k) + (size_t)(g.b * a.Hkv + g.kvh) * a.Tk * D;
+    g.Vg = static_cast<const uint16_t*>(a.v) + (size_t)(g.b * a.Hkv + g.kvh) * a.Tk * D;
   }
   g.off = g.Lk - g.Lq;  // bottom-right causal alignment
   g.q_lo = qt * BQ;
   g.Qg = static_cast<const uint16_t*>(a.q) + (size_t)(g.b * a.Hq + g.hq) * a.Tq * D;
-  g.Kg = static_cast<const uint16_t*>(a.k) + (size_t)(g.b * a.Hkv + g.kvh) * a.Tk * D;
-  g.Vg = static_cast<const uint16_t*>(a.v) + (size_t)(g.b * a.Hkv + g.kvh) * a.Tk * D;
   g.Og = static_cast<uint16_t*>(a.o) + (size_t)(g.b * a.Hq + g.hq) * a.Tq * D;
   g.Lg = a.lse ? a.lse + (size_t)(g.b * a.Hq + g.hq) * a.Tq : nullptr;
   int kend = g.Lk;  // exclusive key bound of the whole tile
@@ -363,51 +373,80 @@ constexpr int kBufferDword3 = 0x00020000;  // raw (untyped) buffer, 32-bit data
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int D, int BK, int THREADS>
+template <int D, int BK, int THREADS, bool PAGED>
 struct Stager {
   using S = Shape<D, BK>;
   static constexpr int NW = THREADS / 64;
   static constexpr int RPI = 1024 / S::RB;      // rows per wavefront instruction
   static constexpr int CPT = BK / (RPI * NW);   // instructions per wavefront per tile
   static_assert(CPT >= 1 && BK % (RPI * NW) == 0, "staging shape");
-  int voff[CPT];  // per-lane byte offset of the fetched chunk within the tile
+  static_assert(16 % RPI == 0, "an instruction's rows lie in one cache block");
+  int voff[CPT];  // per-lane byte offset of the fetched chunk (within the tile, or within the cache block)
   int loff[CPT];  // wave-uniform LDS byte offset of the instruction within the tile
+  int blk[CPT];   // paged: wave-uniform index of the instruction's cache block within the tile
   const uint16_t* base;
+  size_t bstride;   // paged: elements per physical block (all kv heads)
+  const int* tbl;   // paged: the sequence's block-table row, in LDS
 
-  __device__ __forceinline__ void init(const uint16_t* b, int tid) {
+  __device__ __forceinline__ void init(const uint16_t* b, int tid, size_t block_stride = 0,
+                                       const int* table = nullptr) {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l = tid & 63;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int n = i * NW + w;
       const int row = n * RPI + l / S::C8;
-      voff[i] = row * S::RB + 16 * ((l % S::C8) ^ swz<D>(row));
+      const int chunk = 16 * ((l % S::C8) ^ swz<D>(row));
+      voff[i] = (PAGED ? row % 16 : row) * S::RB + chunk;
       loff[i] = n * RPI * S::RB;
+      blk[i] = n * RPI / 16;
     }
     base = b;
+    bstride = block_stride;
+    tbl = table;
   }
   // Issues the loads of tile kt into the LDS tile at `tile`; they complete
   // asynchronously (wait for the vector memory counter before reading).
   __device__ __forceinline__ void load(int kt, int Lk, char* tile) const {
     const int k0 = kt * BK;
-    // uniform by construction; readfirstlane tells the compiler so (a
-    // descriptor in vector registers would need a loop per load)
-    const int rows = __builtin_amdgcn_readfirstlane(min(max(Lk - k0, 0), BK));
-    const uint64_t p = reinterpret_cast<uint64_t>(base + (size_t)k0 * D);
-    const uint64_t pu = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(p >> 32)) << 32) |
-                        (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
-    const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(pu), (short)0, rows * S::RB, kBufferDword3);
-    // The host compilation pass of this file does not know the LDS-load
-    // builtin (and would then drop the kernels' host stubs); the function is
-    // only ever compiled for the device.
-#if defined(__HIP_DEVICE_COMPILE__)
+    if constexpr (!PAGED) {
+      // uniform by construction; readfirstlane tells the compiler so (a
+      // descriptor in vector registers would need a loop per load)
+      const int rows = __builtin_amdgcn_readfirstlane(min(max(Lk - k0, 0), BK));
+      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          uniform_ptr(base + (size_t)k0 * D), (short)0, rows * S::RB, kBufferDword3);
 #pragma unroll
-    for (int i = 0; i < CPT; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(tile + loff[i]), 16, voff[i], 0, 0, 0);
+      for (int i = 0; i < CPT; ++i) load_lds(rsrc, tile + loff[i], voff[i]);
+    } else {
+      // one descriptor per cache block: its physical block, and only its rows
+      // below Lk (a block past the sequence gets none: nothing is read and the
+      // LDS rows receive zeros)
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const int lb = k0 / 16 + blk[i];
+        const int rows = __builtin_amdgcn_readfirstlane(min(max(Lk - 16 * lb, 0), 16));
+        const int phys = rows > 0 ? __builtin_amdgcn_readfirstlane(tbl[min(lb, kMaxPagedPrefillBlocks - 1)]) : 0;
+        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            uniform_ptr(base + (size_t)phys * bstride), (short)0, rows * S::RB, kBufferDword3);
+        load_lds(rsrc, tile + loff[i], voff[i]);
+      }
+    }
+  }
+  static __device__ __forceinline__ void* uniform_ptr(const uint16_t* ptr) {
+    const uint64_t p = reinterpret_cast<uint64_t>(ptr);
+    return reinterpret_cast<void*>(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(p >> 32)) << 32) |
+                                   (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p));
+  }
+  // The host compilation pass of this file does not know the LDS-load
+  // builtin (and would then drop the kernels' host stubs); the function is
+  // only ever compiled for the device.
+  static __device__ __forceinline__ void load_lds(__amdgpu_buffer_rsrc_t rsrc, char* dst, int voffset) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16, voffset, 0, 0, 0);
 #else
     (void)rsrc;
-    (void)tile;
+    (void)dst;
+    (void)voffset;
 #endif
   }
 };
@@ -428,10 +467,10 @@ __device__ __forceinline__ void staged_barrier() {
 //     the wavefront work at the same time;
 //   * accumulates O^T += V^T P^T for tile kt (MFMA);
 // and ends with the wait for its loads and a barrier.
-template <class T, int D, int BK, bool CAUSAL, int THREADS>
+template <class T, int D, int BK, bool CAUSAL, class Stg>
 __device__ __forceinline__ void pipe_step(int kt, const char* kcur, const char* vcur, char* kload, char* vload,
                                           f32x16 (&s_cur)[BK / 32], f32x16 (&s_nxt)[BK / 32],
-                                          const Stager<D, BK, THREADS>& ks, const Stager<D, BK, THREADS>& vs,
+                                          const Stg& ks, const Stg& vs,
                                           Acc<D>& st, const Offs<D, BK>& o, const Geo& g, bool wave_live,
                                           int w_last, int w_lo, int qrow, int h, float cexp) {
   using S = Shape<D, BK>;
@@ -474,7 +513,7 @@ __device__ __forceinline__ void pipe_step(int kt, const char* kcur, const char* 
 
 // ---------------------------------------------------------------------------
 // 4 wavefronts x 32 rows, pipelined key steps over double-buffered K and V.
-template <class T, int D, int BQ, int BK, bool CAUSAL>
+template <class T, int D, int BQ, int BK, bool CAUSAL, bool PAGED>
 __global__ __launch_bounds__(BQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   using S = Shape<D, BK>;
   constexpr int THREADS = (BQ / 32) * 64;
@@ -485,17 +524,30 @@ __global__ __launch_bounds__(BQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   __shared__ __align__(16) char vb0[S::TILE];
   __shared__ __align__(16) char vb1[S::TILE];
 
+  // paged form: the sequence's block-table row, read once into LDS
+  __shared__ int tbl[PAGED ? kMaxPagedPrefillBlocks : 1];
+
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5;
-  const Geo g = make_geo<D, BQ, BK, CAUSAL>(a);
+  const Geo g = make_geo<D, BQ, BK, CAUSAL, PAGED>(a);
   const int w_lo = g.q_lo + w * 32;
   const int qrow = w_lo + (lane & 31);
   Acc<D> st;
   load_q(st, g, a.qmode, qrow, h);
   Offs<D, BK> o;
   make_offs(o, lane);
-  Stager<D, BK, THREADS> ks, vs;
-  ks.init(g.Kg, tid);
-  vs.init(g.Vg, tid);
+  Stager<D, BK, THREADS, PAGED> ks, vs;
+  if constexpr (PAGED) {
+    const size_t bstride = (size_t)a.Hkv * 16 * D;
+    ks.init(g.Kg, tid, bstride, tbl);
+    vs.init(g.Vg, tid, bstride, tbl);
+    const int nb = min((g.Lk + 15) / 16, kMaxPagedPrefillBlocks);
+    const int* trow = a.table + (size_t)g.b * a.max_blocks;
+    for (int i = tid; i < nb; i += THREADS) tbl[i] = min(max(trow[i], 0), a.num_blocks - 1);
+    __syncthreads();
+  } else {
+    ks.init(g.Kg, tid);
+    vs.init(g.Vg, tid);
+  }
 
   if (g.nkt > 0) {
     ks.load(0, g.Lk, kb0);
@@ -518,25 +570,31 @@ __global__ __launch_bounds__(BQ * 2, 2) void prefill_kernel(PrefillArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-template <class T, int D, int BK, bool CAUSAL>
+template <class T, int D, int BK, bool CAUSAL, bool PAGED>
 static hipError_t launch_D(const PrefillArgs& a, hipStream_t stream) {
   PrefillArgs x = a;
   x.nqt = (a.Tq + 127) / 128;
   const long long blocks = (long long)x.nqt * a.Hq * a.B;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   x.xcd_remap = (blocks % (8LL * a.G) == 0) ? 1 : 0;
-  hipLaunchKernelGGL((prefill_kernel<T, D, 128, BK, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, stream, x);
+  hipLaunchKernelGGL((prefill_kernel<T, D, 128, BK, CAUSAL, PAGED>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                     x);
   return hipGetLastError();
 }
 
-template <class T>
+template <class T, bool PAGED>
 static hipError_t launch_t(const PrefillArgs& a, int D, bool causal, hipStream_t stream) {
-  if (D == 128) return causal ? launch_D<T, 128, 64, true>(a, stream) : launch_D<T, 128, 64, false>(a, stream);
-  return causal ? launch_D<T, 64, 64, true>(a, stream) : launch_D<T, 64, 64, false>(a, stream);
+  if (D == 128)
+    return causal ? launch_D<T, 128, 64, true, PAGED>(a, stream) : launch_D<T, 128, 64, false, PAGED>(a, stream);
+  return causal ? launch_D<T, 64, 64, true, PAGED>(a, stream) : launch_D<T, 64, 64, false, PAGED>(a, stream);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int D, bool causal, hipStream_t stream) {
-  return bf16 ? launch_t<BF16>(a, D, causal, stream) : launch_t<F16>(a, D, causal, stream);
+  return bf16 ? launch_t<BF16, false>(a, D, causal, stream) : launch_t<F16, false>(a, D, causal, stream);
+}
+
+hipError_t launch_prefill_paged(const PrefillArgs& a, bool bf16, int D, bool causal, hipStream_t stream) {
+  return bf16 ? launch_t<BF16, true>(a, D, causal, stream) : launch_t<F16, true>(a, D, causal, stream);
 }
 
 }  // namespace attn

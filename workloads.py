@@ -116,6 +116,11 @@ LONG = PrefillCase("long causal bf16 B=1 Hq=32 Hkv=8 T=16384 D=128", B=1, Hq=32,
 
 ALL_PREFILL = [TINY, BERT, LLAMA, LONG]
 
+# Chunked prefill of a long prompt against its cached prefix (llama3-8b heads).
+CHUNK = ChunkCase("chunked prefill llama3-8b bf16 B=4 Hq=32 Hkv=8 D=128 prefix~U[2048,8192] chunk=1024", B=4,
+                  Hq=32, Hkv=8, D=128, dtype="bf16", ctx_lo=2048, ctx_hi=8192, chunk_lo=1024, chunk_hi=1024,
+                  seed=6)
+
 
 def prefill_inputs(case: PrefillCase, nan_padding: bool = False, Tq: int | None = None,
                    Tk: int | None = None):
@@ -186,7 +191,7 @@ def decode_inputs(case: DecodeCase, nan_fill: bool = False, ctx_lens=None):
     return dict(q=q, k_cache=kc, v_cache=vc, block_table=table, ctx_lens=ctx)
 
 
-def chunk_inputs(case: ChunkCase, nan_fill: bool = False):
+def chunk_inputs(case: ChunkCase, nan_fill: bool = False, starts=None, lens=None):
     """Return dict(q, k_new, v_new, k_cache, v_cache, block_table, start_pos, new_lens, ctx_lens).
 
     Draw order: context lengths before the chunk, chunk lengths, a permutation
@@ -195,17 +200,24 @@ def chunk_inputs(case: ChunkCase, nan_fill: bool = False):
     values at every slot, the chunk's own positions included: appending the
     chunk overwrites them. ctx_lens = start_pos + new_lens. With ``nan_fill``
     the chunk's positions in the cache, the tail of each last block, the spare
-    blocks and the padded rows of q / k_new / v_new hold NaN.
+    blocks and the padded rows of q / k_new / v_new hold NaN. ``starts`` /
+    ``lens`` replace the drawn context / chunk lengths (the draws still happen,
+    so the other arrays do not change).
     """
     rng = np.random.default_rng(case.seed)
     start = rng.integers(case.ctx_lo, case.ctx_hi + 1, case.B).astype(np.int32)
     n = rng.integers(case.chunk_lo, case.chunk_hi + 1, case.B).astype(np.int32)
+    if starts is not None:
+        start = np.asarray(starts, dtype=np.int32)
+    if lens is not None:
+        n = np.asarray(lens, dtype=np.int32)
+    assert start.shape == (case.B,) and n.shape == (case.B,) and (n <= case.chunk_hi).all()
     total = start + n
     nblk = (total + BLOCK - 1) // BLOCK
     used = int(nblk.sum())
     NB = used + case.spare_blocks
     perm = rng.permutation(used).astype(np.int32)
-    max_blocks = int(-(-(case.ctx_hi + case.chunk_hi) // BLOCK))
+    max_blocks = int(-(-max(case.ctx_hi + case.chunk_hi, int(total.max())) // BLOCK))
     table = np.full((case.B, max_blocks), -1, dtype=np.int32)
     off = 0
     for b in range(case.B):
@@ -247,7 +259,7 @@ def chunk_flops(ctx_lens, q_lens, Hq, D, causal=True):
 
 
 def append_bytes(new_lens, Hkv, D, elem=2):
-    """Algorithmic HBM bytes of an append: the new K and V read once and written once, plus table reads."""
+    """Algorithmic HBM bytes of an append: the new K and V read once and written once."""
     n = int(np.asarray(new_lens, dtype=np.int64).sum())
     return 2 * 2 * n * Hkv * D * elem
 
