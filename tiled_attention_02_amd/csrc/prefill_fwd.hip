@@ -381,9 +381,11 @@ struct Stager {
   static constexpr int CPT = BK / (RPI * NW);   // instructions per wavefront per tile
   static_assert(CPT >= 1 && BK % (RPI * NW) == 0, "staging shape");
   static_assert(16 % RPI == 0, "an instruction's rows lie in one cache block");
+  static constexpr int EPT = BK / 16;         // cache blocks per tile (paged form)
+  static constexpr int JW = NW * RPI / 16;      // paged: distinct wave-dependent block choices per instruction
   int voff[CPT];  // per-lane byte offset of the fetched chunk (within the tile, or within the cache block)
   int loff[CPT];  // wave-uniform LDS byte offset of the instruction within the tile
-  int blk[CPT];   // paged: wave-uniform index of the instruction's cache block within the tile
+  int wblk;       // paged: the wave's share of an instruction's block index, in [0, JW)
   const uint16_t* base;
   size_t bstride;   // paged: elements per physical block (all kv heads)
   const int* tbl;   // paged: the sequence's block-table row, in LDS
@@ -399,15 +401,32 @@ struct Stager {
       const int chunk = 16 * ((l % S::C8) ^ swz<D>(row));
       voff[i] = (PAGED ? row % 16 : row) * S::RB + chunk;
       loff[i] = n * RPI * S::RB;
-      blk[i] = n * RPI / 16;
     }
+    // instruction i of wave w covers rows (i*NW + w)*RPI ..: cache block i*JW + (w*RPI)/16 of the tile
+    wblk = (w * RPI) / 16;
     base = b;
     bstride = block_stride;
     tbl = table;
   }
+  // Paged form: the physical block ids of tile kt's cache blocks, read with
+  // one LDS access (the same address in every lane) and made wave-uniform.
+  __device__ __forceinline__ void entries(int kt, int (&e)[EPT]) const {
+    if constexpr (PAGED) {
+      static_assert(EPT == 4, "one 16-byte table read per tile");
+      const int idx = min(kt * EPT, kMaxPagedPrefillBlocks - EPT);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(tbl + idx);
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) e[i] = __builtin_amdgcn_readfirstlane((int)v[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) e[i] = 0;
+    }
+    (void)kt;
+  }
   // Issues the loads of tile kt into the LDS tile at `tile`; they complete
   // asynchronously (wait for the vector memory counter before reading).
-  __device__ __forceinline__ void load(int kt, int Lk, char* tile) const {
+  // e: the tile's physical blocks (paged form only).
+  __device__ __forceinline__ void load(int kt, int Lk, char* tile, const int (&e)[EPT]) const {
     const int k0 = kt * BK;
     if constexpr (!PAGED) {
       // uniform by construction; readfirstlane tells the compiler so (a
@@ -417,17 +436,21 @@ struct Stager {
           uniform_ptr(base + (size_t)k0 * D), (short)0, rows * S::RB, kBufferDword3);
 #pragma unroll
       for (int i = 0; i < CPT; ++i) load_lds(rsrc, tile + loff[i], voff[i]);
+      (void)e;
     } else {
       // one descriptor per cache block: its physical block, and only its rows
       // below Lk (a block past the sequence gets none: nothing is read and the
       // LDS rows receive zeros)
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
-        const int lb = k0 / 16 + blk[i];
+        int phys = e[i * JW];
+#pragma unroll
+        for (int j = 1; j < JW; ++j)
+          if (wblk == j) phys = e[i * JW + j];
+        const int lb = k0 / 16 + i * JW + wblk;
         const int rows = __builtin_amdgcn_readfirstlane(min(max(Lk - 16 * lb, 0), 16));
-        const int phys = rows > 0 ? __builtin_amdgcn_readfirstlane(tbl[min(lb, kMaxPagedPrefillBlocks - 1)]) : 0;
         const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-            uniform_ptr(base + (size_t)phys * bstride), (short)0, rows * S::RB, kBufferDword3);
+            (void*)(base + (size_t)(rows > 0 ? phys : 0) * bstride), (short)0, rows * S::RB, kBufferDword3);
         load_lds(rsrc, tile + loff[i], voff[i]);
       }
     }
@@ -471,11 +494,22 @@ template <class T, int D, int BK, bool CAUSAL, class Stg>
 __device__ __forceinline__ void pipe_step(int kt, const char* kcur, const char* vcur, char* kload, char* vload,
                                           f32x16 (&s_cur)[BK / 32], f32x16 (&s_nxt)[BK / 32],
                                           const Stg& ks, const Stg& vs,
-                                          Acc<D>& st, const Offs<D, BK>& o, const Geo& g, bool wave_live,
-                                          int w_last, int w_lo, int qrow, int h, float cexp) {
+                                          int (&ecar)[Stg::EPT], Acc<D>& st, const Offs<D, BK>& o,
+                                          const Geo& g, bool wave_live, int w_last, int w_lo, int qrow, int h,
+                                          float cexp) {
   using S = Shape<D, BK>;
-  if (kt + 2 < g.nkt) ks.load(kt + 2, g.Lk, kload);
-  if (kt + 1 < g.nkt) vs.load(kt + 1, g.Lk, vload);
+  // (paged form) ecar: the physical blocks of tile kt+1, read one step earlier
+  // for its K and reused now for its V
+  if (kt + 2 < g.nkt) {
+    int enew[Stg::EPT];
+    ks.entries(kt + 2, enew);
+    ks.load(kt + 2, g.Lk, kload, enew);
+    if (kt + 1 < g.nkt) vs.load(kt + 1, g.Lk, vload, ecar);
+#pragma unroll
+    for (int i = 0; i < Stg::EPT; ++i) ecar[i] = enew[i];
+  } else if (kt + 1 < g.nkt) {
+    vs.load(kt + 1, g.Lk, vload, ecar);
+  }
   // causal: tiles entirely above this wavefront's part of the diagonal are
   // skipped (monotone in kt, so work_next implies work)
   const bool work = wave_live && (!CAUSAL || kt * BK <= w_last);
@@ -525,7 +559,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   __shared__ __align__(16) char vb1[S::TILE];
 
   // paged form: the sequence's block-table row, read once into LDS
-  __shared__ int tbl[PAGED ? kMaxPagedPrefillBlocks : 1];
+  __shared__ __align__(16) int tbl[PAGED ? kMaxPagedPrefillBlocks : 4];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5;
   const Geo g = make_geo<D, BQ, BK, CAUSAL, PAGED>(a);
@@ -549,10 +583,16 @@ __global__ __launch_bounds__(BQ * 2, 2) void prefill_kernel(PrefillArgs a) {
     vs.init(g.Vg, tid);
   }
 
+  int ecar[Stager<D, BK, THREADS, PAGED>::EPT] = {};  // physical blocks of the tile after the current one
   if (g.nkt > 0) {
-    ks.load(0, g.Lk, kb0);
-    vs.load(0, g.Lk, vb0);
-    if (g.nkt > 1) ks.load(1, g.Lk, kb1);
+    int e0[Stager<D, BK, THREADS, PAGED>::EPT];
+    ks.entries(0, e0);
+    ks.load(0, g.Lk, kb0, e0);
+    vs.load(0, g.Lk, vb0, e0);
+    if (g.nkt > 1) {
+      ks.entries(1, ecar);
+      ks.load(1, g.Lk, kb1, ecar);
+    }
   }
   staged_barrier();
   const bool wave_live = w_lo < g.Lq;
@@ -560,11 +600,11 @@ __global__ __launch_bounds__(BQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   f32x16 s0[S::KB], s1[S::KB];
   if (g.nkt > 0 && wave_live && (!CAUSAL || 0 <= w_last)) tile_qk<T, D, BK>(s0, kb0, o, st);
   for (int kt = 0; kt < g.nkt; kt += 2) {
-    pipe_step<T, D, BK, CAUSAL>(kt, kb1, vb0, kb0, vb1, s0, s1, ks, vs, st, o, g, wave_live, w_last, w_lo, qrow,
-                                h, a.c);
+    pipe_step<T, D, BK, CAUSAL>(kt, kb1, vb0, kb0, vb1, s0, s1, ks, vs, ecar, st, o, g, wave_live, w_last, w_lo,
+                                qrow, h, a.c);
     if (kt + 1 < g.nkt)
-      pipe_step<T, D, BK, CAUSAL>(kt + 1, kb0, vb1, kb1, vb0, s1, s0, ks, vs, st, o, g, wave_live, w_last, w_lo,
-                                  qrow, h, a.c);
+      pipe_step<T, D, BK, CAUSAL>(kt + 1, kb0, vb1, kb1, vb0, s1, s0, ks, vs, ecar, st, o, g, wave_live, w_last,
+                                  w_lo, qrow, h, a.c);
   }
   epilogue<T, D>(st, g, a.Tq, qrow, h);
 }
