@@ -2,9 +2,13 @@
 """Benchmark of libattn on one MI355X.
 
 One step = one pass of the whole hot path on seeded synthetic inputs:
-  * causal bf16 prefill, B=1, Hq=32, Hkv=8, T=16384, D=128 (attn_fwd), and
+  * causal bf16 prefill, B=1, Hq=32, Hkv=8, T=16384, D=128 (attn_fwd),
   * paged bf16 decode, B=64, Hq=12, Hkv=2, D=128, ctx ~ U[512, 4096],
-    16-token blocks (attn_decode_paged).
+    16-token blocks (attn_decode_paged), and
+  * a chunked prefill through the paged cache: 1024-token chunks of 4
+    sequences with cached prefixes ~ U[2048, 8192], Llama3-8B heads
+    (attn_cache_append of the chunk's K/V into each of 8 layers' caches,
+    then attn_fwd_paged on one of them).
 Each call is timed with HIP events on the stream it runs on. Before each call
 (outside its events) a read pass over a 1 GiB buffer evicts the inputs from
 the 256 MB Infinity Cache and the L2s, so the timed call reads its inputs from
@@ -38,7 +42,10 @@ PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = {
     "prefill": ["tiled_attention_02_amd/csrc/prefill_fwd.hip", "tiled_attention_02_amd/csrc/attn_device.h"],
     "decode": ["tiled_attention_02_amd/csrc/decode_paged.hip", "tiled_attention_02_amd/csrc/attn_device.h"],
+    "chunked_prefill": ["tiled_attention_02_amd/csrc/prefill_fwd.hip", "tiled_attention_02_amd/csrc/attn_device.h"],
+    "append": ["tiled_attention_02_amd/csrc/paged_cache.hip"],
 }
+APPEND_LAYERS = 8
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
 
@@ -69,7 +76,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-flush", action="store_true", help="skip the cache flush between calls")
-    p.add_argument("--only", choices=["prefill", "decode"], default=None,
+    p.add_argument("--only", choices=["prefill", "decode", "chunked"], default=None,
                    help="profile helper: run only one of the two calls (not a benchmark line)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="run a plain device copy of this many MiB (counter calibration) and exit")
@@ -124,6 +131,21 @@ def cpu_baseline_decode(x, case, nseq=64, min_seconds=5.0):
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": _oracle_threads(), "kind": "oracle",
             "sample": f"float64 oracle on the whole batch ({nseq} sequences), repeated {reps} times; "
                       f"{dt:.1f} s wall"}
+
+
+def cpu_baseline_chunked(x, case, nseq=1):
+    """Time the float64 oracle on the first sequence(s) of the chunked-prefill batch (all heads, all rows)."""
+    import workloads as W
+    from oracle import oracle as O
+    sl = slice(0, nseq)
+    t0 = time.perf_counter()
+    O.prefill_paged(x["q"][sl], x["k_cache"], x["v_cache"], x["block_table"][sl], x["ctx_lens"][sl],
+                    x["new_lens"][sl], case.scale, True)
+    dt = time.perf_counter() - t0
+    flops = W.chunk_flops(x["ctx_lens"][sl], x["new_lens"][sl], case.Hq, case.D, True)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _oracle_threads(), "kind": "oracle",
+            "sample": f"float64 oracle (prefill through the block table) on {nseq} of {case.B} sequences, "
+                      f"all {case.Hq} heads and rows; {dt:.1f} s wall"}
 
 
 def context_measurements(ta, W, torch, np, dev, flush_rows, flush_dst, evict):
@@ -239,10 +261,31 @@ def main():
     flush_rows = flush_src.view(-1, 4096)
     flush_dst = torch.empty(flush_rows.shape[0], dtype=torch.float32, device=dev)
 
+    cc = W.CHUNK
+    log(f"[bench] building inputs: {cc.name}")
+    xc = W.chunk_inputs(cc)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)  # noqa: E731
+    cq = torch.from_numpy(xc["q"]).to(bf).to(dev)
+    ckn = torch.from_numpy(xc["k_new"]).to(bf).to(dev)
+    cvn = torch.from_numpy(xc["v_new"]).to(bf).to(dev)
+    ckc = torch.from_numpy(xc["k_cache"]).to(bf).to(dev)
+    cvc = torch.from_numpy(xc["v_cache"]).to(bf).to(dev)
+    cbt, cst, cnl, ccl = (i32(xc[n]) for n in ("block_table", "start_pos", "new_lens", "ctx_lens"))
+    co = torch.empty_like(cq)
+    clse = torch.empty(cq.shape[:3], dtype=torch.float32, device=dev)
+    # the append is timed as a burst over APPEND_LAYERS layers, each with its
+    # own chunk and its own cache (as a model appends once per layer): one
+    # ~10 us call between two events would mostly time the launch
+    app_sets = [(ckn, cvn, ckc, cvc)] + [tuple(t.clone() for t in (ckn, cvn, ckc, cvc))
+                                         for _ in range(APPEND_LAYERS - 1)]
+
     pflops = W.prefill_flops(pc.B, pc.Hq, pc.T, pc.T, pc.D, True)
     dbytes = W.decode_bytes(xd["ctx_lens"], dc.Hq, dc.Hkv, dc.D)
+    cflops = W.chunk_flops(xc["ctx_lens"], xc["new_lens"], cc.Hq, cc.D, True)
+    abytes = W.append_bytes(xc["new_lens"], cc.Hkv, cc.D)
     run_p = args.only in (None, "prefill")
     run_d = args.only in (None, "decode")
+    run_c = args.only in (None, "chunked")
 
     def evict():
         # read-only pass over 1 GiB: pushes the inputs out of every cache level
@@ -261,8 +304,20 @@ def main():
             evs[2].record()
             ta.attn_decode_paged(dq, kc, vc, bt, cl, scale=dc.scale, out=do, lse=dlse, workspace=ws)
             evs[3].record()
+        if run_c:
+            # the chunk's K/V go into the cache (every layer), then the chunk
+            # attends to prefix + itself (first layer's cache)
+            evict()
+            evs[4].record()
+            for kn_, vn_, kc_, vc_ in app_sets:
+                ta.attn_cache_append(kn_, vn_, kc_, vc_, cbt, cst, cnl)
+            evs[5].record()
+            evict()
+            evs[6].record()
+            ta.attn_fwd_paged(cq, ckc, cvc, cbt, ccl, cnl, scale=cc.scale, causal=True, out=co, lse=clse)
+            evs[7].record()
 
-    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(4)]  # noqa: E731
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(8)]  # noqa: E731
     for i in range(args.warmup):
         step(mk())
     torch.cuda.synchronize()
@@ -276,15 +331,22 @@ def main():
     wall = time.perf_counter() - t0
     p_ms = [e[0].elapsed_time(e[1]) for e in evs] if run_p else [float("nan")]
     d_ms = [e[2].elapsed_time(e[3]) for e in evs] if run_d else [float("nan")]
+    a_ms = [e[4].elapsed_time(e[5]) / APPEND_LAYERS for e in evs] if run_c else [float("nan")]
+    c_ms = [e[6].elapsed_time(e[7]) for e in evs] if run_c else [float("nan")]
     p_avg, d_avg = float(np.mean(p_ms)), float(np.mean(d_ms))
+    a_avg, c_avg = float(np.mean(a_ms)), float(np.mean(c_ms))
     log(f"[bench] prefill {p_avg:.3f} ms (min {min(p_ms):.3f}); decode {d_avg * 1e3:.1f} us "
-        f"(min {min(d_ms) * 1e3:.1f}); wall/step {wall / args.steps * 1e3:.2f} ms")
+        f"(min {min(d_ms) * 1e3:.1f}); append {a_avg * 1e3:.1f} us; chunked prefill {c_avg * 1e3:.1f} us; "
+        f"wall/step {wall / args.steps * 1e3:.2f} ms")
     if args.only:
-        print(json.dumps({"only": args.only, "prefill_ms": p_avg, "decode_ms": d_avg}))
+        print(json.dumps({"only": args.only, "prefill_ms": p_avg, "decode_ms": d_avg, "append_ms": a_avg,
+                          "chunked_prefill_ms": c_avg}))
         return
 
     p_tfs = pflops / (p_avg * 1e-3) / 1e12
     d_gbs = dbytes / (d_avg * 1e-3) / 1e9
+    c_tfs = cflops / (c_avg * 1e-3) / 1e12
+    a_gbs = abytes / (a_avg * 1e-3) / 1e9
     out = {
         "metric": METRIC,
         "value": round(p_tfs, 2),
@@ -292,14 +354,16 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(p_avg + d_avg, 4),
+        "ms_per_step": round(p_avg + d_avg + APPEND_LAYERS * a_avg + c_avg, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "causal bf16 prefill B=1 Hq=32 Hkv=8 T=16384 D=128 (value) + paged bf16 decode "
-                               "B=64 Hq=12 Hkv=2 D=128 ctx~U[512,4096] block=16 (decode)",
+                               "B=64 Hq=12 Hkv=2 D=128 ctx~U[512,4096] block=16 (decode) + chunked bf16 prefill "
+                               "B=4 Hq=32 Hkv=8 D=128 prefix~U[2048,8192] chunk=1024 through the block table "
+                               "(chunked)",
                    "prefill_gflop_per_call": round(pflops / 1e9, 3),
                    "decode_mb_per_call": round(dbytes / 1e6, 3),
                    "cache_eviction_before_each_call": "none" if args.no_flush else "1 GiB read pass",
@@ -313,6 +377,19 @@ def main():
                                 "frac": round(d_gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic("decode"),
                                 "kernels": "decode_split_kernel + decode_combine_kernel",
                                 "algorithmic_bytes_per_call": dbytes}},
+        "chunked": {
+            "workload": cc.name, "ctx_lens": [int(c) for c in xc["ctx_lens"]],
+            "prefill": {"value": round(c_tfs, 2), "unit": "TFLOP/s", "us_per_call": round(c_avg * 1e3, 2),
+                        "roofline": {"bound": "mfma", "achieved": round(c_tfs, 2), "peak": PEAK_BF16_TFLOPS,
+                                     "unit": "TFLOP/s", "frac": round(c_tfs / PEAK_BF16_TFLOPS, 4),
+                                     "traffic": measured_traffic("chunked_prefill"),
+                                     "kernel": "prefill_kernel (paged form)", "algorithmic_flops_per_launch": cflops}},
+            "append": {"value": round(a_gbs, 1), "unit": "GB/s", "us_per_call": round(a_avg * 1e3, 2),
+                       "timing": f"a burst of {APPEND_LAYERS} appends (one per layer, each with its own chunk "
+                                 "and cache) between two events, after the eviction pass; per-call mean",
+                       "roofline": {"bound": "hbm", "achieved": round(a_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                    "frac": round(a_gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic("append"),
+                                    "kernel": "append_kernel", "algorithmic_bytes_per_launch": abytes}}},
     }
     out["context"] = context_measurements(ta, W, torch, np, dev, flush_rows, flush_dst, evict)
     if not args.no_cpu_baseline:
@@ -320,6 +397,8 @@ def main():
         out["cpu_baseline"] = cpu_baseline_prefill(xp, pc)
         log("[bench] cpu baseline: float64 oracle on a sample of the decode workload")
         out["decode"]["cpu_baseline"] = cpu_baseline_decode(xd, dc)
+        log("[bench] cpu baseline: float64 oracle on a sample of the chunked-prefill workload")
+        out["chunked"]["cpu_baseline"] = cpu_baseline_chunked(xc, cc)
     print(json.dumps(out), flush=True)
 
 
