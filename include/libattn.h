@@ -175,6 +175,42 @@ attn_status attn_cache_append(const void* k_new, const void* v_new, void* k_cach
                               int max_blocks_per_seq, int num_blocks, attn_dtype dtype,
                               hipStream_t stream);
 
+/*
+ * FP8 KV cache. The pages name FP8 inference as the next step for LLM serving
+ * (comemg.com, "天下苦英偉達久矣！PyTorch免CUDA加速推理，Triton時代要來？", section
+ * "未來工作") and the fusion of dequantisation into the consuming product as a
+ * standard fusion (the-ai.news page cited above, operator-fusion section);
+ * they fix no format. Here the caches hold codes of the E4M3 format of the
+ * OCP 8-bit floating point specification (1 byte per element: sign, 4
+ * exponent bits with bias 7, 3 mantissa bits; largest finite 448; S.1111.111
+ * is NaN) with one float scale per cache: an entry means value(code) * scale.
+ *
+ * attn_cache_append_fp8: as attn_cache_append, but k_new / v_new (bf16 or
+ * fp16, `dtype`) are quantized on the way: code = E4M3(x / scale) with the
+ * division in fp32 (correctly rounded), magnitudes above 448 saturating to
+ * 448, round to nearest even. k_cache / v_cache are uint8
+ * [num_blocks, Hkv, block_size, D]. k_scale, v_scale: finite, > 0.
+ */
+attn_status attn_cache_append_fp8(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                                  float k_scale, float v_scale, const int* block_table,
+                                  const int* start_pos, const int* new_lens, int B, int Hkv, int Tnew,
+                                  int D, int block_size, int max_blocks_per_seq, int num_blocks,
+                                  attn_dtype dtype, hipStream_t stream);
+
+/*
+ * attn_decode_paged_fp8: as attn_decode_paged over uint8 E4M3 caches
+ * [num_blocks, Hkv, block_size, D] with scales k_scale, v_scale (finite,
+ * > 0): the result is the decode of the dequantized cache. q, o stay bf16 or
+ * fp16 (`dtype`); the products run on that type (E4M3 values are exact in
+ * both). Workspace: attn_decode_workspace_bytes, as for attn_decode_paged.
+ */
+attn_status attn_decode_paged_fp8(const void* q, const void* k_cache, const void* v_cache,
+                                  float k_scale, float v_scale, const int* block_table,
+                                  const int* ctx_lens, void* o, float* lse, int B, int Hq, int Hkv,
+                                  int D, int block_size, int max_blocks_per_seq, int num_blocks,
+                                  float scale, attn_dtype dtype, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
 /* Workspace bytes attn_decode_paged needs for these sizes (0 if they are invalid). */
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_blocks_per_seq, int block_size);
 

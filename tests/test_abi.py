@@ -119,6 +119,38 @@ def test_append_rejects_before_launch(L, kw, code):
     assert ta.attn_last_error().startswith("attn_cache_append:")
 
 
+def _dec8(L, q=FAKE, kc=FAKE, vc=FAKE, ks=0.5, vs=0.25, bt=FAKE, cl=FAKE, o=FAKE, lse=None, B=2, Hq=12, Hkv=2,
+          D=128, bs=16, maxb=64, nb=100, scale=0.1, dtype=1, ws=FAKE, wsb=1 << 30):
+    return L.attn_decode_paged_fp8(q, kc, vc, ctypes.c_float(ks), ctypes.c_float(vs), bt, cl, o, lse, B, Hq, Hkv, D,
+                                   bs, maxb, nb, ctypes.c_float(scale), dtype, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ks=0.0), 1), (dict(vs=-1.0), 1), (dict(ks=float("nan")), 1), (dict(vs=float("inf")), 1),
+    (dict(q=None), 1), (dict(D=96), 2), (dict(Hq=34, Hkv=2), 2), (dict(ws=None), 1), (dict(kc=FAKE_MIS), 1),
+])
+def test_decode_fp8_rejects_before_launch(L, kw, code):
+    import tiled_attention_02_amd as ta
+    assert _dec8(L, **kw) == code
+    assert ta.attn_last_error().startswith("attn_decode_paged_fp8:")
+
+
+def _app8(L, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, ks=0.5, vs=0.25, bt=FAKE, sp=FAKE, nl=None, B=2, Hkv=2, Tnew=64,
+          D=128, bs=16, maxb=64, nb=100, dtype=1):
+    return L.attn_cache_append_fp8(kn, vn, kc, vc, ctypes.c_float(ks), ctypes.c_float(vs), bt, sp, nl, B, Hkv, Tnew,
+                                   D, bs, maxb, nb, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ks=0.0), 1), (dict(vs=float("nan")), 1), (dict(kn=None), 1), (dict(bs=8), 2), (dict(D=32), 2),
+    (dict(vc=FAKE_MIS), 1), (dict(dtype=4), 2),
+])
+def test_append_fp8_rejects_before_launch(L, kw, code):
+    import tiled_attention_02_amd as ta
+    assert _app8(L, **kw) == code
+    assert ta.attn_last_error().startswith("attn_cache_append_fp8:")
+
+
 def test_workspace_size(L):
     import tiled_attention_02_amd as ta
     # 256 blocks of 16 tokens -> 16 splits of 256 tokens, each partial holding D values + log-sum,

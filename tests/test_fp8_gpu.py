@@ -1,0 +1,177 @@
+"""GPU parity of the E4M3 (FP8) KV cache: quantizing append and decode over it.
+
+Both entry points are called through the C ABI and compared with the float64
+oracle (oracle/fp8.py) on the same seeded inputs:
+  - attn_cache_append_fp8 must produce the oracle's codes bit for bit (the
+    float32 division and the rounding decide an integer code; both sides
+    take that decision in float32), slots it must not touch unchanged;
+  - attn_decode_paged_fp8 must match the decode definition over the
+    dequantized cache to the library's tolerance (bf16 1e-2, fp16 2e-3 on O,
+    1e-4 relative on lse): E4M3 values are exact in both 16-bit types, so the
+    dequantization adds no error of its own;
+  - with power-of-two scales the FP8 decode equals, bit for bit, the 16-bit
+    decode of a cache that holds the dequantized values (the scales fold out
+    of the products exactly).
+Unused cache slots hold the E4M3 NaN code, so any read of them into a result
+shows up.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import fp8 as F8
+from test_parity_gpu import _compare, _dev, _note
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ta(gpu):
+    import torch  # noqa: F401
+    import tiled_attention_02_amd as ta
+    ta.lib()
+    return ta
+
+
+def _u8(x):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint8)).cuda()
+
+
+def _i32(x):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).cuda()
+
+
+def _run_decode_fp8(ta, x, case, ks, vs, scale=None):
+    import torch
+    scale = case.scale if scale is None else scale
+    o, lse = ta.attn_decode_paged_fp8(_dev(x["q"], case.dtype), _u8(x["k_cache"]), _u8(x["v_cache"]), ks, vs,
+                                      _i32(x["block_table"]), _i32(x["ctx_lens"]), scale=scale)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def _decode_fp8_check(ta, case, ks, vs, ctx_lens=None, what=None):
+    x = W.decode_inputs_fp8(case, nan_fill=True, ctx_lens=ctx_lens)
+    what = what or case.name
+    _note(f"[case] fp8 decode {what} ks={ks} vs={vs} ctx[min,max]=({x['ctx_lens'].min()},{x['ctx_lens'].max()})")
+    o, lse = _run_decode_fp8(ta, x, case, ks, vs)
+    o_ref, lse_ref = F8.decode_paged_fp8(x["q"], x["k_cache"], x["v_cache"], ks, vs, x["block_table"],
+                                         x["ctx_lens"], case.scale)
+    _compare(o, lse, o_ref, lse_ref, case.dtype, what=f"fp8 decode {what}")
+    return x, o, lse
+
+
+# ---------------------------------------------------------------- decode over an E4M3 cache vs the oracle
+def test_fp8_decode_qwen_shape(ta):
+    case = W.DecodeCase("fp8 qwen", B=64, Hq=12, Hkv=2, D=128, dtype="bf16", ctx_lo=512, ctx_hi=4096, seed=81)
+    _decode_fp8_check(ta, case, 0.25, 0.0625)
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,dtype,ks,vs", [(8, 8, 128, "bf16", 0.5, 2.0), (16, 1, 128, "fp16", 0.0173, 0.031),
+                                                 (12, 2, 64, "fp16", 0.125, 0.125), (5, 1, 64, "bf16", 1.0, 0.3),
+                                                 (32, 8, 128, "bf16", 0.09, 0.011)])
+def test_fp8_decode_head_layouts(ta, Hq, Hkv, D, dtype, ks, vs):
+    case = W.DecodeCase("fp8 heads", B=5, Hq=Hq, Hkv=Hkv, D=D, dtype=dtype, ctx_lo=1, ctx_hi=1500, seed=82)
+    _decode_fp8_check(ta, case, ks, vs, what=f"Hq={Hq} Hkv={Hkv} D={D} {dtype}")
+
+
+@pytest.mark.parametrize("ctx", [[1, 2, 15, 16, 17, 31, 32, 33], [255, 256, 257, 511, 512, 513, 1000, 4096]])
+def test_fp8_decode_context_edges(ta, ctx):
+    case = W.DecodeCase("fp8 edges", B=len(ctx), Hq=12, Hkv=2, D=128, dtype="bf16", ctx_lo=1, ctx_hi=4096, seed=83)
+    _decode_fp8_check(ta, case, 0.3, 0.7, ctx_lens=ctx, what=f"ctx={ctx}")
+
+
+def test_fp8_decode_extreme_codes(ta):
+    """Codes across the whole finite range (exponent fields 0..15): large scores, subnormal values."""
+    import torch
+    case = W.DecodeCase("fp8 wide", B=4, Hq=8, Hkv=2, D=128, dtype="bf16", ctx_lo=100, ctx_hi=900, seed=84)
+    x = W.decode_inputs_fp8(case, nan_fill=True)
+    rng = np.random.default_rng(85)
+    live = x["k_cache"] != W.E4M3_NAN
+    wide = W.e4m3_codes(rng, x["k_cache"].shape, exp_lo=0, exp_hi=15)
+    wide[(wide & 0x7F) == 0x7F] = 0x7E
+    x["k_cache"] = np.where(live, wide, x["k_cache"]).astype(np.uint8)
+    x["v_cache"] = np.where(live, W.e4m3_codes(rng, x["v_cache"].shape, exp_lo=0, exp_hi=14), x["v_cache"]).astype(np.uint8)
+    ks, vs = 2.0 ** -9, 2.0 ** -4
+    o, lse = _run_decode_fp8(ta, x, case, ks, vs)
+    o_ref, lse_ref = F8.decode_paged_fp8(x["q"], x["k_cache"], x["v_cache"], ks, vs, x["block_table"],
+                                         x["ctx_lens"], case.scale)
+    _compare(o, lse, o_ref, lse_ref, "bf16", what="fp8 decode wide codes")
+    del torch
+
+
+def test_fp8_decode_equals_16bit_decode_of_dequantized_cache(ta):
+    """Power-of-two scales: the FP8 decode and the 16-bit decode over the dequantized values agree bit for bit."""
+    import torch
+    case = W.DecodeCase("fp8 vs bf16", B=16, Hq=12, Hkv=2, D=128, dtype="bf16", ctx_lo=1, ctx_hi=3000, seed=86)
+    x = W.decode_inputs_fp8(case, nan_fill=False)
+    ks, vs = 0.125, 0.5
+    o8, l8 = _run_decode_fp8(ta, x, case, ks, vs)
+    kd = F8.dequantize(x["k_cache"], ks).astype(np.float32)  # exact in bf16
+    vd = F8.dequantize(x["v_cache"], vs).astype(np.float32)
+    assert np.array_equal(W.round_to(kd, "bf16"), kd) and np.array_equal(W.round_to(vd, "bf16"), vd)
+    o16, l16 = ta.attn_decode_paged(_dev(x["q"], "bf16"), _dev(kd, "bf16"), _dev(vd, "bf16"),
+                                    _i32(x["block_table"]), _i32(x["ctx_lens"]), scale=case.scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(o8, o16.float().cpu().numpy()) and np.array_equal(l8, l16.cpu().numpy())
+
+
+# ---------------------------------------------------------------- quantizing append vs the oracle
+@pytest.mark.parametrize("D,dtype,ks,vs", [(128, "bf16", 0.0173, 0.0625), (64, "fp16", 0.5, 0.003),
+                                         (128, "fp16", 1.0, 1.0), (64, "bf16", 0.25, 0.11)])
+def test_fp8_append_codes_bit_exact(ta, D, dtype, ks, vs):
+    import torch
+    case = W.ChunkCase("fp8 append", B=3, Hq=8, Hkv=2, D=D, dtype=dtype, ctx_lo=0, ctx_hi=700, chunk_lo=0,
+                       chunk_hi=300, seed=87)
+    x = W.chunk_inputs(case, nan_fill=True)
+    rng = np.random.default_rng(88)
+    k8 = W.e4m3_codes(rng, x["k_cache"].shape)
+    v8 = W.e4m3_codes(rng, x["v_cache"].shape)
+    # some inputs beyond the format's range after scaling (saturation), some in the subnormal range
+    kn = x["k_new"].copy()
+    kn[:, :, ::7] *= 300.0
+    kn[:, :, 3::11] *= 1e-3
+    kn = W.round_to(kn, dtype)
+    _note(f"[case] fp8 append D={D} {dtype} ks={ks} vs={vs} n={x['new_lens'].tolist()}")
+    kc, vc = _u8(k8), _u8(v8)
+    ta.attn_cache_append_fp8(_dev(kn, dtype), _dev(x["v_new"], dtype), kc, vc, ks, vs, _i32(x["block_table"]),
+                             _i32(x["start_pos"]), _i32(x["new_lens"]))
+    torch.cuda.synchronize()
+    kref, vref = F8.cache_append_fp8(kn, x["v_new"], k8, v8, x["block_table"], x["start_pos"], ks, vs,
+                                     x["new_lens"])
+    assert np.array_equal(kc.cpu().numpy(), kref), "K codes differ"
+    assert np.array_equal(vc.cpu().numpy(), vref), "V codes differ"
+
+
+def test_fp8_append_then_decode(ta):
+    """A decode step as a server runs it: the new token's K/V quantized into the cache, then the decode."""
+    import torch
+    case = W.ChunkCase("fp8 step", B=6, Hq=12, Hkv=2, D=128, dtype="bf16", ctx_lo=0, ctx_hi=2000, chunk_lo=1,
+                       chunk_hi=1, seed=89)
+    x = W.chunk_inputs(case, nan_fill=True)
+    rng = np.random.default_rng(90)
+    k8 = W.e4m3_codes(rng, x["k_cache"].shape)
+    v8 = W.e4m3_codes(rng, x["v_cache"].shape)
+    ks, vs = 0.02, 0.013
+    kc, vc = _u8(k8), _u8(v8)
+    ta.attn_cache_append_fp8(_dev(x["k_new"], "bf16"), _dev(x["v_new"], "bf16"), kc, vc, ks, vs,
+                             _i32(x["block_table"]), _i32(x["start_pos"]), None)
+    o, lse = ta.attn_decode_paged_fp8(_dev(x["q"][:, :, 0], "bf16"), kc, vc, ks, vs, _i32(x["block_table"]),
+                                      _i32(x["ctx_lens"]), scale=case.scale)
+    torch.cuda.synchronize()
+    kref, vref = F8.cache_append_fp8(x["k_new"], x["v_new"], k8, v8, x["block_table"], x["start_pos"], ks, vs)
+    o_ref, lse_ref = F8.decode_paged_fp8(x["q"][:, :, 0], kref, vref, ks, vs, x["block_table"], x["ctx_lens"],
+                                         case.scale)
+    _compare(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, "bf16", what="fp8 append + decode")
+
+
+def test_fp8_rejects_bad_scales(ta):
+    import torch
+    q = torch.zeros((2, 4, 128), dtype=torch.bfloat16, device="cuda")
+    kc = torch.zeros((4, 2, 16, 128), dtype=torch.uint8, device="cuda")
+    bt, cl = _i32(np.zeros((2, 2))), _i32([1, 1])
+    for ks, vs in ((0.0, 1.0), (1.0, -1.0), (float("nan"), 1.0), (1.0, float("inf"))):
+        with pytest.raises(ta.AttnError, match="k_scale and v_scale"):
+            ta.attn_decode_paged_fp8(q, kc, kc, ks, vs, bt, cl)

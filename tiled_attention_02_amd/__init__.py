@@ -12,13 +12,14 @@ import ctypes
 import math
 import os
 
-__all__ = ["attn_fwd", "attn_decode_paged", "attn_fwd_paged", "attn_cache_append", "attn_decode_workspace_bytes",
+__all__ = ["attn_fwd", "attn_decode_paged", "attn_fwd_paged", "attn_cache_append", "attn_cache_append_fp8",
+           "attn_decode_paged_fp8", "attn_decode_workspace_bytes",
            "attn_status_str", "attn_last_error", "AttnError", "lib", "LIB_PATH", "EXPORTS", "BLOCK_SIZE",
            "decode_workspace"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
-EXPORTS = ("attn_fwd", "attn_decode_paged", "attn_fwd_paged", "attn_cache_append", "attn_decode_workspace_bytes",
-           "attn_status_str", "attn_last_error")
+EXPORTS = ("attn_fwd", "attn_decode_paged", "attn_fwd_paged", "attn_cache_append", "attn_cache_append_fp8",
+           "attn_decode_paged_fp8", "attn_decode_workspace_bytes", "attn_status_str", "attn_last_error")
 BLOCK_SIZE = 16
 
 ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
@@ -51,6 +52,10 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd_paged.restype = i
     L.attn_cache_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp]
     L.attn_cache_append.restype = i
+    L.attn_cache_append_fp8.argtypes = [vp, vp, vp, vp, f, f, vp, vp, vp, i, i, i, i, i, i, i, i, vp]
+    L.attn_cache_append_fp8.restype = i
+    L.attn_decode_paged_fp8.argtypes = [vp, vp, vp, f, f, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, sz, vp]
+    L.attn_decode_paged_fp8.restype = i
     L.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
     L.attn_decode_workspace_bytes.restype = sz
     L.attn_status_str.argtypes = [i]
@@ -154,10 +159,25 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, ctx_lens, scale: float |
                       lse=None, workspace=None, need_lse: bool = True):
     """Paged one-token decode. q [B,Hq,D]; caches [num_blocks,Hkv,16,D]; block_table int32
     [B,max_blocks]; ctx_lens int32 [B]. Returns (o [B,Hq,D], lse [B,Hq] float32 or None)."""
+    return _decode(q, k_cache, v_cache, None, block_table, ctx_lens, scale, out, lse, workspace, need_lse)
+
+
+def attn_decode_paged_fp8(q, k_cache, v_cache, k_scale: float, v_scale: float, block_table, ctx_lens,
+                          scale: float | None = None, out=None, lse=None, workspace=None, need_lse: bool = True):
+    """Paged one-token decode over E4M3 caches (uint8 [num_blocks,Hkv,16,D]; an entry means
+    value(code) * k_scale or * v_scale). q, o bf16 or fp16."""
+    return _decode(q, k_cache, v_cache, (k_scale, v_scale), block_table, ctx_lens, scale, out, lse, workspace,
+                   need_lse)
+
+
+def _decode(q, k_cache, v_cache, scales, block_table, ctx_lens, scale, out, lse, workspace, need_lse):
     import torch
     dt = _dtype_code(q)
     _check(q.dim() == 3 and k_cache.dim() == 4 and v_cache.shape == k_cache.shape, "bad q / cache rank or shape")
-    _check(k_cache.dtype == q.dtype and v_cache.dtype == q.dtype, "q and caches must share a dtype")
+    if scales is None:
+        _check(k_cache.dtype == q.dtype and v_cache.dtype == q.dtype, "q and caches must share a dtype")
+    else:
+        _check(k_cache.dtype == torch.uint8 and v_cache.dtype == torch.uint8, "E4M3 caches must be uint8 tensors")
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (block_table, "block_table"),
                  (ctx_lens, "ctx_lens")):
         _check(t.is_cuda and t.is_contiguous(), f"{n} must be a contiguous GPU tensor")
@@ -176,10 +196,13 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, ctx_lens, scale: float |
     need = attn_decode_workspace_bytes(B, Hq, Hkv, D, maxb, bs)
     if workspace is None:
         workspace = decode_workspace(q.device, need)
-    st = lib().attn_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(ctx_lens),
-                                 _ptr(out), _ptr(lse), B, Hq, Hkv, D, bs, maxb, NB, ctypes.c_float(scale), dt,
-                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                 _stream(q.device))
+    tail = (_ptr(out), _ptr(lse), B, Hq, Hkv, D, bs, maxb, NB, ctypes.c_float(scale), dt, _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(q.device))
+    if scales is None:
+        st = lib().attn_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(ctx_lens), *tail)
+    else:
+        st = lib().attn_decode_paged_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.c_float(scales[0]),
+                                         ctypes.c_float(scales[1]), _ptr(block_table), _ptr(ctx_lens), *tail)
     _raise(st)
     return out, lse
 
@@ -250,4 +273,26 @@ def attn_cache_append(k_new, v_new, k_cache, v_cache, block_table, start_pos, ne
     st = lib().attn_cache_append(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
                                  _ptr(start_pos), _ptr(new_lens), B, Hkv, Tnew, D, bs, block_table.shape[1], NB,
                                  dt, _stream(k_new.device))
+    _raise(st)
+
+
+def attn_cache_append_fp8(k_new, v_new, k_cache, v_cache, k_scale: float, v_scale: float, block_table, start_pos,
+                          new_lens=None):
+    """Quantize k_new/v_new [B,Hkv,Tnew,D] (bf16 / fp16) to E4M3 codes of x / scale and write them into the
+    uint8 caches [num_blocks,Hkv,16,D] in place (token i < new_lens[b] -> position start_pos[b] + i)."""
+    import torch
+    dt = _dtype_code(k_new)
+    _check(k_new.is_cuda and k_new.dim() == 4 and v_new.shape == k_new.shape and v_new.dtype == k_new.dtype
+           and k_new.is_contiguous() and v_new.is_contiguous() and v_new.is_cuda,
+           "k_new / v_new must be contiguous GPU tensors of one shape [B,Hkv,Tnew,D]")
+    B, Hkv, Tnew, D = k_new.shape
+    NB, Hc, bs = _check_paged((k_cache, v_cache), torch.uint8, D)
+    _check(Hc == Hkv, "kv head count mismatch")
+    _check(block_table.dim() == 2 and block_table.shape[0] == B, "block_table must be [B, max_blocks]")
+    _check_i32(block_table, block_table.numel(), "block_table")
+    _check_i32(start_pos, B, "start_pos")
+    _check_i32(new_lens, B, "new_lens", optional=True)
+    st = lib().attn_cache_append_fp8(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), ctypes.c_float(k_scale),
+                                     ctypes.c_float(v_scale), _ptr(block_table), _ptr(start_pos), _ptr(new_lens), B,
+                                     Hkv, Tnew, D, bs, block_table.shape[1], NB, dt, _stream(k_new.device))
     _raise(st)

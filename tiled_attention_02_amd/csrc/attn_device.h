@@ -50,6 +50,12 @@ struct BF16 {
     const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), one, acc, false);
   }
+  // E4M3 codes in bytes 2*HI, 2*HI + 1 of w -> packed pair (low half from the
+  // lower byte). Exact: every E4M3 value is a bf16 value.
+  template <bool HI>
+  static __device__ __forceinline__ uint32_t from_e4m3x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, HI));
+  }
 };
 
 struct F16 {
@@ -69,7 +75,21 @@ struct F16 {
     const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk), one, acc, false);
   }
+  // E4M3 codes in bytes 2*HI, 2*HI + 1 of w -> packed pair. Exact: every E4M3
+  // value is an fp16 value.
+  template <bool HI>
+  static __device__ __forceinline__ uint32_t from_e4m3x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, HI));
+  }
 };
+
+// Eight E4M3 codes (two dwords, code e in byte e) -> eight 16-bit values in
+// element order: one MFMA operand fragment.
+template <class T>
+__device__ __forceinline__ u32x4 e4m3x8(u32x2 w) {
+  return u32x4{T::template from_e4m3x2<false>(w[0]), T::template from_e4m3x2<true>(w[0]),
+               T::template from_e4m3x2<false>(w[1]), T::template from_e4m3x2<true>(w[1])};
+}
 
 // Max / sum of a value with the same lane in the other half of the wavefront
 // (lane l <-> lane l^32) through v_permlane32_swap: swap(x, x) returns the

@@ -14,22 +14,26 @@
 //
 // Decomposition: one wavefront per (split of 256 tokens = 16 cache blocks,
 // kv head, sequence). It streams its blocks two at a time (32 tokens per
-// step) with the next two pairs' loads in flight, and serves all
-// G = Hq/Hkv query heads of the kv head from one read of each block:
+// step) with the next pair's loads in flight, and serves all G = Hq/Hkv query
+// heads of the kv head from one read of each block:
 //   S^T = K Q^T       v_mfma_f32_16x16x32: rows = 16 tokens of a block,
 //                     columns = query heads (G <= 16, the rest zero).
 //   O  += P V         v_mfma_f32_16x16x32: rows = heads, columns = 16 of D,
 //                     contraction = the 32 tokens of the two blocks.
-// The transposed scores of the two blocks are already the A operand (P) of
-// the second product. The V operand needs 8 tokens at one column per lane:
-// lane (g = l/16, c = l%16) loads 16-byte rows of its 8 tokens at columns
-// [VC*c, VC*c + VC) (VC = D/16) and transposes them in registers (v_perm), so
-// product n yields column d = VC*c + n.
-// Every (block, kv head) of K and V is 16*D contiguous elements, read once.
-// The split's partial (O normalised, log2 of its sum) comes straight from
-// the wavefront's registers: no LDS and no barrier. A second, light kernel
-// merges the partials; when the whole batch fits in one split the first
-// kernel writes the output directly.
+// Every (block, kv head) of K and V is 16*D contiguous elements, read once,
+// straight into LDS; the transposed scores of the two blocks are already the
+// A operand (P) of the second product, and V's operand comes from LDS through
+// the transposing reads. The split's partial (O normalised, log2 of its sum)
+// is written from registers; a second, light kernel merges the partials.
+// When the whole batch fits in one split the first kernel writes the output.
+//
+// FP8 form: the caches hold E4M3 codes with one scale per cache (an entry
+// means code value * scale). Blocks are half the bytes; the operands are
+// converted to the 16-bit type right after their LDS reads (exact: E4M3 values
+// are bf16 and fp16 values), and the two scales are folded out of the
+// products: k_scale into the exponent factor of the scores, v_scale into the
+// final normalisation. This is the fusion of dequantisation into the
+// consuming product named on the-ai.news page's operator-fusion section.
 #include "attn_device.h"
 #include "launch.h"
 
@@ -41,59 +45,110 @@ constexpr int kDecodeDword3 = 0x00020000;  // raw (untyped) buffer descriptor, 3
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 // LDS image of one pair of cache blocks: K block 0, K block 1, V block 0,
 // V block 1, each 16 token rows of RB bytes, row-major with a 16-byte-chunk
 // XOR swizzle: chunk c of row r sits in slot c ^ f(r). LDS serves 256 bytes
 // per cycle (16 lanes of a 16-byte access, 32 lanes of an 8-byte one); f makes
-// the K operand reads (16 rows, one chunk) and the transposing V reads (8 rows
-// x 2 chunks per 32 lanes) hit distinct banks.
-template <int D>
+// the K operand reads and the transposing V reads of each lane group hit
+// distinct banks.
+template <int D, bool KV8>
 struct PairLds {
-  static constexpr int RB = 2 * D;           // bytes per token row
+  static constexpr int EB = KV8 ? 1 : 2;     // bytes per cache element
+  static constexpr int RB = EB * D;          // bytes per token row
   static constexpr int BLK = 16 * RB;        // one (block, kv head) of K or V
   static constexpr int BYTES = 4 * BLK;
   static constexpr int RPI = 1024 / RB;      // rows filled by one wavefront load instruction
   static constexpr int NI = 16 / RPI;        // load instructions per block
-  static constexpr int C8 = D / 8;           // 16-byte chunks per row
+  static constexpr int C8 = RB / 16;         // 16-byte chunks per row
   static constexpr int LOADS = 4 * NI;       // load instructions per pair
 };
 
+// 16-bit cache: one swizzle for K and V. K reads: 16 rows at one chunk per
+// 16 lanes; V reads (ds_read_b64_tr_b16): 4 rows x 2 chunk halves per 16
+// lanes, 8 rows per 32 lanes.
 template <int D>
 __device__ __forceinline__ int dswz(int row) {
   if constexpr (D == 128) return ((row & 7) << 1) | ((row >> 3) & 1);
   else return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
 }
+// E4M3 cache: rows of D bytes. K reads are 8 bytes per lane (rows 0..15 at
+// two adjacent 8-byte chunks per 32 lanes): rows of equal parity (D = 128; of
+// equal row % 4 at D = 64) must take distinct chunk swaps. V reads
+// (ds_read_b64_tr_b8) take rows 0..7 of both V blocks at two adjacent 8-byte
+// chunks per 32 lanes, so the V swizzle also depends on the block.
+template <int D>
+__device__ __forceinline__ int kswz8(int row) {
+  if constexpr (D == 128) return (row >> 1) & 7;
+  else return (row >> 2) & 3;
+}
+template <int D>
+__device__ __forceinline__ int vswz8(int row, int blk) {
+  if constexpr (D == 128) return ((row >> 1) & 3) | (blk << 2);
+  else return ((row >> 2) & 1) | (blk << 1);
+}
+template <int D, bool KV8>
+__device__ __forceinline__ int kswz(int row) {
+  if constexpr (KV8) return kswz8<D>(row);
+  else return dswz<D>(row);
+}
+template <int D, bool KV8>
+__device__ __forceinline__ int vswz(int row, int blk) {
+  if constexpr (KV8) return vswz8<D>(row, blk);
+  else return dswz<D>(row);
+}
 
 // Per-lane byte offsets, identical for every pair.
-template <int D>
+template <int D, bool KV8>
 struct DecOffs {
-  int ld[PairLds<D>::NI];  // chunk fetched by load instruction i (within a block)
-  int k[D / 32];           // K operand of k-step s
-  int v[D / 16];           // V^T operand of product n (first of two 8-byte reads)
+  int ldk[PairLds<D, KV8>::NI];     // chunk fetched by load instruction i of a K block
+  int ldv[2][PairLds<D, KV8>::NI];  // ... of V block 0 / 1
+  int k[D / 32];                    // K operand of k-step s
+  int v[D / 16];                    // V operand of product n (16-bit: first of two reads; E4M3: the read)
 };
 
-template <int D>
-__device__ __forceinline__ void make_dec_offs(DecOffs<D>& o, int lane) {
-  using L = PairLds<D>;
+template <int D, bool KV8>
+__device__ __forceinline__ void make_dec_offs(DecOffs<D, KV8>& o, int lane) {
+  using L = PairLds<D, KV8>;
   const int g = lane >> 4, c = lane & 15;
   // load instruction i writes rows RPI*i .. (1 KiB of consecutive LDS, lane l
   // at 16 l): lane l fetches the logical chunk its slot holds
 #pragma unroll
   for (int i = 0; i < L::NI; ++i) {
     const int row = L::RPI * i + lane / L::C8;
-    o.ld[i] = row * L::RB + 16 * ((lane % L::C8) ^ dswz<D>(row));
+    const int slot = lane % L::C8;
+    o.ldk[i] = row * L::RB + 16 * (slot ^ kswz<D, KV8>(row));
+    o.ldv[0][i] = row * L::RB + 16 * (slot ^ vswz<D, KV8>(row, 0));
+    o.ldv[1][i] = row * L::RB + 16 * (slot ^ vswz<D, KV8>(row, 1));
   }
-  // K operand (A of S^T = K Q^T): lane (g, c) takes token c, columns
-  // 32s + 8g .. +8, i.e. chunk 4s + g
+  if constexpr (!KV8) {
+    // K operand (A of S^T = K Q^T): lane (g, c) takes token c, columns
+    // 32s + 8g .. +8, i.e. chunk 4s + g
 #pragma unroll
-  for (int s = 0; s < D / 32; ++s) o.k[s] = c * L::RB + 16 * ((4 * s + g) ^ dswz<D>(c));
-  // V^T operand of product n (B of O += P V, columns 16n .. 16n + 15): in
-  // each 16-lane group g, lane i = a + 4e addresses token row 4g + e at
-  // columns 16n + 4a .. +4 and receives column 16n + i of those 4 rows
-  const int i = lane & 15, a4 = i & 3, row = 4 * g + (i >> 2);
+    for (int s = 0; s < D / 32; ++s) o.k[s] = c * L::RB + 16 * ((4 * s + g) ^ dswz<D>(c));
+    // V^T operand of product n (B of O += P V, columns 16n .. 16n + 15): in
+    // each 16-lane group g, lane i = a + 4e addresses token row 4g + e at
+    // columns 16n + 4a .. +4 and receives column 16n + i of those 4 rows
+    const int i = lane & 15, a4 = i & 3, row = 4 * g + (i >> 2);
 #pragma unroll
-  for (int n = 0; n < D / 16; ++n) o.v[n] = row * L::RB + 16 * ((2 * n + (a4 >> 1)) ^ dswz<D>(row)) + 8 * (a4 & 1);
+    for (int n = 0; n < D / 16; ++n) o.v[n] = row * L::RB + 16 * ((2 * n + (a4 >> 1)) ^ dswz<D>(row)) + 8 * (a4 & 1);
+  } else {
+    // K operand: lane (g, c) takes token c, columns 32s + 8g .. +8: the 8-byte
+    // half (g & 1) of 16-byte chunk 2s + (g >> 1)
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) o.k[s] = c * L::RB + 16 * ((2 * s + (g >> 1)) ^ kswz8<D>(c)) + 8 * (g & 1);
+    // V operand of product n via ds_read_b64_tr_b8: within each 16-lane group,
+    // lane j receives byte (j & 7) of the 8 bytes read by lanes 2e + (j >> 3),
+    // e = 0..7. So lane s addresses token e = s >> 1 of the group's 8 (block
+    // e >> 2, row 4g + e % 4: P's contraction order) at columns 16n + 8(s & 1)
+    // .. +8, and lane j receives column 16n + j of the 8 tokens.
+    const int e = c >> 1, bb = e >> 2, row = 4 * g + (e & 3);
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n)
+      o.v[n] = (2 + bb) * L::BLK + row * L::RB + 16 * (n ^ vswz8<D>(row, bb)) + 8 * (c & 1);
+  }
 }
 
 // Starts the loads of one pair of blocks (K and V of both) into an LDS pair
@@ -102,10 +157,10 @@ __device__ __forceinline__ void make_dec_offs(DecOffs<D>& o, int lane) {
 // the sequence's last block (live1 == false): it then re-reads the first one
 // (a cache hit), since every token there is masked or zeroed anyway, which
 // keeps the number of loads per pair fixed for the in-order memory counter.
-template <int D>
-__device__ __forceinline__ void load_pair(char* buf, const uint16_t* kbase, const uint16_t* vbase,
-                                          size_t block_stride, int ph0, int ph1, bool live1, const DecOffs<D>& o) {
-  using L = PairLds<D>;
+template <int D, bool KV8>
+__device__ __forceinline__ void load_pair(char* buf, const char* kbase, const char* vbase, size_t block_stride,
+                                          int ph0, int ph1, bool live1, const DecOffs<D, KV8>& o) {
+  using L = PairLds<D, KV8>;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const size_t off = (size_t)(j && live1 ? ph1 : ph0) * block_stride;
@@ -123,8 +178,8 @@ __device__ __forceinline__ void load_pair(char* buf, const uint16_t* kbase, cons
 #if defined(__HIP_DEVICE_COMPILE__)
 #pragma unroll
       for (int i = 0; i < L::NI; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + i * 1024), 16, o.ld[i], 0, 0,
-                                                 /*non-temporal*/ 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + i * 1024), 16,
+                                                 kv ? o.ldv[j][i] : o.ldk[i], 0, 0, /*non-temporal*/ 2);
 #else
       (void)rsrc;
       (void)dst;
@@ -147,10 +202,10 @@ struct WaveState {
 // sequence's last pair (TAIL) tokens >= ctx are masked, and their V rows are
 // zeroed in LDS first, since unused cache slots may hold anything, NaN
 // included.
-template <class T, int D, bool TAIL>
+template <class T, int D, bool KV8, bool TAIL>
 __device__ __forceinline__ void pair_step(WaveState<D>& st, char* buf, const u32x4 (&qf)[D / 32],
-                                          const DecOffs<D>& o, int t0, int ctx, float cexp, int lane) {
-  using L = PairLds<D>;
+                                          const DecOffs<D, KV8>& o, int t0, int ctx, float cexp, int lane) {
+  using L = PairLds<D, KV8>;
   constexpr int KS = D / 32;
   constexpr int VC = D / 16;
   const int g = lane >> 4;
@@ -170,8 +225,14 @@ __device__ __forceinline__ void pair_step(WaveState<D>& st, char* buf, const u32
   for (int j = 0; j < 2; ++j) {
     sacc[j] = f32x4{};
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
-      sacc[j] = T::mfma16(*reinterpret_cast<const u32x4*>(buf + j * L::BLK + o.k[s]), qf[s], sacc[j]);
+    for (int s = 0; s < KS; ++s) {
+      u32x4 kf;
+      if constexpr (KV8)
+        kf = e4m3x8<T>(*reinterpret_cast<const u32x2*>(buf + j * L::BLK + o.k[s]));
+      else
+        kf = *reinterpret_cast<const u32x4*>(buf + j * L::BLK + o.k[s]);
+      sacc[j] = T::mfma16(kf, qf[s], sacc[j]);
+    }
   }
   if constexpr (TAIL) {
 #pragma unroll
@@ -217,17 +278,22 @@ __device__ __forceinline__ void pair_step(WaveState<D>& st, char* buf, const u32
   // the two transposing reads give V in the same order
 #pragma unroll
   for (int n = 0; n < VC; ++n) {
-    const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(buf + 2 * L::BLK + o.v[n]));
-    const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(buf + 3 * L::BLK + o.v[n]));
-    const u32x2 a0 = __builtin_bit_cast(u32x2, v0);
-    const u32x2 a1 = __builtin_bit_cast(u32x2, v1);
-    st.o[n] = T::mfma16(pf, u32x4{a0[0], a0[1], a1[0], a1[1]}, st.o[n]);
+    if constexpr (KV8) {
+      const i32x2 v8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(buf + o.v[n]));
+      st.o[n] = T::mfma16(pf, e4m3x8<T>(__builtin_bit_cast(u32x2, v8)), st.o[n]);
+    } else {
+      const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(buf + 2 * L::BLK + o.v[n]));
+      const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(buf + 3 * L::BLK + o.v[n]));
+      const u32x2 a0 = __builtin_bit_cast(u32x2, v0);
+      const u32x2 a1 = __builtin_bit_cast(u32x2, v1);
+      st.o[n] = T::mfma16(pf, u32x4{a0[0], a0[1], a1[0], a1[1]}, st.o[n]);
+    }
   }
 }
 
-template <class T, int D>
+template <class T, int D, bool KV8>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
-  using L = PairLds<D>;
+  using L = PairLds<D, KV8>;
   constexpr int KS = D / 32;
   constexpr int VC = D / 16;
   constexpr int NP = kSplitBlocks / 2;  // block pairs per split
@@ -273,12 +339,14 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   const int nb = min(kSplitBlocks, nblk - blk0);  // blocks of this split, >= 1
   const int np = (nb + 1) >> 1;
 
-  const size_t head_stride = (size_t)kDecodeBlock * D;  // one (block, kv head)
-  const size_t block_stride = (size_t)a.Hkv * head_stride;
-  const uint16_t* kbase = static_cast<const uint16_t*>(a.kc) + kvh * head_stride;
-  const uint16_t* vbase = static_cast<const uint16_t*>(a.vc) + kvh * head_stride;
-  DecOffs<D> o;
-  make_dec_offs<D>(o, lane);
+  const size_t head_bytes = (size_t)L::BLK;  // one (block, kv head)
+  const size_t block_stride = (size_t)a.Hkv * head_bytes;
+  const char* kbase = static_cast<const char*>(a.kc) + kvh * head_bytes;
+  const char* vbase = static_cast<const char*>(a.vc) + kvh * head_bytes;
+  DecOffs<D, KV8> o;
+  make_dec_offs<D, KV8>(o, lane);
+  // E4M3 caches: k_scale multiplies every score, v_scale every value
+  const float cexp = KV8 ? a.c * a.k_scale : a.c;
 
   // ---- q^T operand: head c, columns 32s + 8g .. +8 (step s, lane group g);
   // loaded first: the memory counter is in order, so the first step then waits
@@ -302,9 +370,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   // The scheduling barriers keep q's loads and the two pairs' loads in this
   // order (the memory counter is in order; the waits below rely on it).
   __builtin_amdgcn_sched_barrier(0);
-  load_pair<D>(buf0, kbase, vbase, block_stride, phys[0], phys[1], nb > 1, o);
+  load_pair<D, KV8>(buf0, kbase, vbase, block_stride, phys[0], phys[1], nb > 1, o);
   __builtin_amdgcn_sched_barrier(0);
-  load_pair<D>(buf1, kbase, vbase, block_stride, ph(1, 0), ph(1, 1), 3 < nb, o);
+  load_pair<D, KV8>(buf1, kbase, vbase, block_stride, ph(1, 0), ph(1, 1), 3 < nb, o);
   __builtin_amdgcn_sched_barrier(0);
 
   WaveState<D> st;
@@ -325,14 +393,14 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     const int t0 = (blk0 + 2 * p) * kDecodeBlock;
     if (t0 + 32 > ctx)
-      pair_step<T, D, true>(st, buf, qf, o, t0, ctx, a.c, lane);
+      pair_step<T, D, KV8, true>(st, buf, qf, o, t0, ctx, cexp, lane);
     else
-      pair_step<T, D, false>(st, buf, qf, o, t0, ctx, a.c, lane);
+      pair_step<T, D, KV8, false>(st, buf, qf, o, t0, ctx, cexp, lane);
     if (p + 2 < NP) {
       // every read of this buffer has returned before new data is written to it
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       const int q = p + 2 < NP ? p + 2 : 0;  // in range also where the branch is dead
-      load_pair<D>(buf, kbase, vbase, block_stride, ph(q, 0), ph(q, 1), 2 * q + 1 < nb, o);
+      load_pair<D, KV8>(buf, kbase, vbase, block_stride, ph(q, 0), ph(q, 1), 2 * q + 1 < nb, o);
     }
   }
 
@@ -345,7 +413,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int h = 4 * g + r;
-    const float inv = 1.f / __shfl(lr_head, h);  // > 0: the split holds a visible token
+    // > 0: the split holds a visible token
+    const float inv = (KV8 ? a.v_scale : 1.f) / __shfl(lr_head, h);
     if (h < G) {
       const int hq = kvh * G + h;
       if (single) {
@@ -410,9 +479,9 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
   if (d == 0 && a.lse) a.lse[(size_t)b * a.Hq + hq] = (m + fast_log2(W)) * kLn2;
 }
 
-template <class T, int D>
+template <class T, int D, bool KV8>
 static hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3(a.nsplit, a.Hkv, a.B), dim3(64), 0, stream, a);
+  hipLaunchKernelGGL((decode_split_kernel<T, D, KV8>), dim3(a.nsplit, a.Hkv, a.B), dim3(64), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(a.Hq, a.B), dim3(D), 0, stream, a);
@@ -420,8 +489,13 @@ static hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, bool bf16, hipStream_t stream) {
-  if (a.D == 128) return bf16 ? launch_d<BF16, 128>(a, stream) : launch_d<F16, 128>(a, stream);
-  return bf16 ? launch_d<BF16, 64>(a, stream) : launch_d<F16, 64>(a, stream);
+  if (a.D == 128) return bf16 ? launch_d<BF16, 128, false>(a, stream) : launch_d<F16, 128, false>(a, stream);
+  return bf16 ? launch_d<BF16, 64, false>(a, stream) : launch_d<F16, 64, false>(a, stream);
+}
+
+hipError_t launch_decode_fp8(const DecodeArgs& a, bool bf16, hipStream_t stream) {
+  if (a.D == 128) return bf16 ? launch_d<BF16, 128, true>(a, stream) : launch_d<F16, 128, true>(a, stream);
+  return bf16 ? launch_d<BF16, 64, true>(a, stream) : launch_d<F16, 64, true>(a, stream);
 }
 
 }  // namespace attn

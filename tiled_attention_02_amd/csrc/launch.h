@@ -38,6 +38,8 @@ struct AppendArgs {
   const int* start;   // [B]
   const int* new_lens;  // [B] or null (all Tnew)
   int B, Hkv, Tnew, D, max_blocks, num_blocks;
+  // fp8 form: the caches hold E4M3 codes of x / scale
+  float k_scale, v_scale;
 };
 
 constexpr int kMaxPagedPrefillBlocks = 2048;  // block-table entries a chunked prefill keeps in LDS
@@ -56,6 +58,8 @@ struct DecodeArgs {
   int nsplit;  // maximum number of splits per sequence
   float c;
   int qmode;
+  // E4M3 caches (fp8 form): an entry means code value * scale
+  float k_scale, v_scale;
 };
 
 constexpr int kDecodeBlock = 16;        // tokens per cache block
@@ -64,7 +68,9 @@ constexpr int kSplitBlocks = 16;        // cache blocks per split (256 tokens)
 hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int D, bool causal, hipStream_t stream);
 hipError_t launch_prefill_paged(const PrefillArgs& a, bool bf16, int D, bool causal, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_append_fp8(const AppendArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, bool bf16, hipStream_t stream);
+hipError_t launch_decode_fp8(const DecodeArgs& a, bool bf16, hipStream_t stream);
 
 // Workspace: the per-split partials (Hkv is part of the signature so that a
 // layout that depends on it stays a library-internal change).

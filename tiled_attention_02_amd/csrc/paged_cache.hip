@@ -1,4 +1,4 @@
-// Writing new keys/values into the paged KV cache.
+// Writing new keys/values into the paged KV cache (16-bit, or E4M3 codes).
 //
 // The paged cache keeps a sequence's keys and values in fixed-size blocks of
 // 16 tokens, found through a per-sequence block table (the-ai.news, "Snelle
@@ -19,74 +19,134 @@ namespace attn {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-// A workgroup moves RPW consecutive new rows of one (sequence, kv head): each
-// thread one 16-byte chunk of K and of V for each of RPT rows, RPW / RPT rows
-// apart, so every wavefront instruction covers whole contiguous rows and a
-// thread keeps 2 * RPT loads in flight. The loads of the new rows depend only
-// on the sequence's chunk length, so they are issued together with the
-// block-table entries that place them: one round trip for the two
-// per-sequence scalars, then one for the data and the entries.
+// A workgroup moves consecutive new rows of one (sequence, kv head): each
+// thread one 16-byte chunk of the destination row of K and of V for each of
+// RPT rows, STRIDE rows apart, so every wavefront instruction covers whole
+// contiguous rows and a thread keeps 2 * RPT loads in flight. The loads of
+// the new rows depend only on the sequence's chunk length, so they are issued
+// together with the block-table entries that place them: one round trip for
+// the two per-sequence scalars, then one for the data and the entries.
+//
+// MODE 0 copies 16-bit rows. MODE 1 / 2 (bf16 / fp16 input) writes E4M3
+// codes of x / scale: float32 division (correctly rounded), magnitudes
+// clamped to 448 (the conversion would give NaN above 464; values in
+// (448, 464] round to 448 either way; NaN stays NaN), then the conversion's
+// round to nearest even.
 constexpr int kAppendRowsPerThread = 4;
 
-template <int D, bool HAS_LENS>
+template <int MODE>
+__device__ __forceinline__ float elem_to_f32(uint32_t w, int half) {
+  const uint32_t bits = half ? (w >> 16) : (w & 0xffffu);
+  if constexpr (MODE == 1) return __builtin_bit_cast(float, bits << 16);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
+__device__ __forceinline__ float e4m3_in_range(float x, float scale) {
+  const float y = __fdiv_rn(x, scale);
+  return y > 448.f ? 448.f : (y < -448.f ? -448.f : y);
+}
+
+// 16 source elements (two 16-byte chunks) -> 16 E4M3 codes, code e in byte e.
+template <int MODE>
+__device__ __forceinline__ u32x4_t quantize16(const u32x4_t (&x)[2], float scale) {
+  u32x4_t out;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t w0 = x[d / 2][2 * (d % 2)], w1 = x[d / 2][2 * (d % 2) + 1];
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_in_range(elem_to_f32<MODE>(w0, 0), scale),
+                                            e4m3_in_range(elem_to_f32<MODE>(w0, 1), scale), 0, false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_in_range(elem_to_f32<MODE>(w1, 0), scale),
+                                        e4m3_in_range(elem_to_f32<MODE>(w1, 1), scale), r, true);
+    out[d] = (uint32_t)r;
+  }
+  return out;
+}
+
+template <int D, bool HAS_LENS, int MODE>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
-  constexpr int C8 = D / 8;                    // 16-byte chunks per row
+  constexpr int NS = MODE ? 2 : 1;             // 16-byte source chunks per destination chunk
+  constexpr int EPC = 8 * NS;                  // elements per destination chunk
+  constexpr int CPR = D / EPC;                 // destination chunks per row
+  constexpr int EB = MODE ? 1 : 2;             // destination bytes per element
   constexpr int RPT = kAppendRowsPerThread;
-  constexpr int STRIDE = 256 / C8;             // rows covered by one pass of the workgroup
+  constexpr int STRIDE = 256 / CPR;            // rows covered by one pass of the workgroup
   const int kvh = blockIdx.y, b = blockIdx.z;
-  const int c = threadIdx.x % C8;
-  const int t0 = blockIdx.x * (STRIDE * RPT) + threadIdx.x / C8;
+  const int c = threadIdx.x % CPR;
+  const int t0 = blockIdx.x * (STRIDE * RPT) + threadIdx.x / CPR;
   const int start = a.start[b];
   const int n = HAS_LENS ? min(a.new_lens[b], a.Tnew) : a.Tnew;
   asm volatile("" ::"s"(start), "s"(n));  // both scalars in one round trip
   if (t0 >= n) return;
   const size_t row0 = (size_t)(b * a.Hkv + kvh) * a.Tnew;
   const int* trow = a.table + (size_t)b * a.max_blocks;
-  u32x4_t kx[RPT], vx[RPT];
+  u32x4_t kx[RPT][NS], vx[RPT][NS];
   int phys[RPT];
 #pragma unroll
   for (int j = 0; j < RPT; ++j) {
     // rows past the chunk re-read the last valid row (in bounds) and are dropped below
     const int t = min(t0 + j * STRIDE, n - 1);
-    const size_t src = (row0 + t) * D + 8 * c;
-    kx[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.k_new) + src));
-    vx[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.v_new) + src));
+    const size_t src = (row0 + t) * D + EPC * c;
+#pragma unroll
+    for (int h = 0; h < NS; ++h) {
+      kx[j][h] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.k_new) + src + 8 * h));
+      vx[j][h] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.v_new) + src + 8 * h));
+    }
     phys[j] = trow[min(max((start + t) / kDecodeBlock, 0), a.max_blocks - 1)];
   }
   // keeps the data loads here, ahead of the checks on the entries (the
   // compiler would otherwise sink them into the stores' blocks)
 #pragma unroll
-  for (int j = 0; j < RPT; ++j) asm volatile("" ::"v"(kx[j]), "v"(vx[j]));
+  for (int j = 0; j < RPT; ++j)
+#pragma unroll
+    for (int h = 0; h < NS; ++h) asm volatile("" ::"v"(kx[j][h]), "v"(vx[j][h]));
 #pragma unroll
   for (int j = 0; j < RPT; ++j) {
     const int t = t0 + j * STRIDE;
     const int pos = start + t;
     // past the chunk, outside the table or on an unmapped entry: nothing to write
     if (t >= n || pos < 0 || pos / kDecodeBlock >= a.max_blocks || phys[j] < 0 || phys[j] >= a.num_blocks) continue;
-    const size_t dst = (((size_t)phys[j] * a.Hkv + kvh) * kDecodeBlock + pos % kDecodeBlock) * D + 8 * c;
-    *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(a.kc) + dst) = kx[j];
-    *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(a.vc) + dst) = vx[j];
+    const size_t dst = ((((size_t)phys[j] * a.Hkv + kvh) * kDecodeBlock + pos % kDecodeBlock) * D + EPC * c) * EB;
+    u32x4_t ko, vo;
+    if constexpr (MODE == 0) {
+      ko = kx[j][0];
+      vo = vx[j][0];
+    } else {
+      ko = quantize16<MODE>(kx[j], a.k_scale);
+      vo = quantize16<MODE>(vx[j], a.v_scale);
+    }
+    *reinterpret_cast<u32x4_t*>(static_cast<char*>(a.kc) + dst) = ko;
+    *reinterpret_cast<u32x4_t*>(static_cast<char*>(a.vc) + dst) = vo;
   }
 }
 
-template <int D>
-static void launch_d(const AppendArgs& a, dim3 grid, hipStream_t stream) {
+template <int D, int MODE>
+static void launch_dm(const AppendArgs& a, dim3 grid, hipStream_t stream) {
   if (a.new_lens)
-    hipLaunchKernelGGL((append_kernel<D, true>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((append_kernel<D, true, MODE>), grid, dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((append_kernel<D, false>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((append_kernel<D, false, MODE>), grid, dim3(256), 0, stream, a);
 }
 
-hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
-  const long long rows_per_wg = (256 / (a.D / 8)) * kAppendRowsPerThread;
+template <int MODE>
+static hipError_t launch_mode(const AppendArgs& a, hipStream_t stream) {
+  const long long epc = MODE ? 16 : 8;
+  const long long rows_per_wg = (256 / (a.D / epc)) * kAppendRowsPerThread;
   const long long gx = (a.Tnew + rows_per_wg - 1) / rows_per_wg;
   if (gx > 0x7fffffffLL || a.Hkv > 65535 || a.B > 65535) return hipErrorInvalidValue;
   const dim3 grid((unsigned)gx, (unsigned)a.Hkv, (unsigned)a.B);
   if (a.D == 128)
-    launch_d<128>(a, grid, stream);
+    launch_dm<128, MODE>(a, grid, stream);
   else
-    launch_d<64>(a, grid, stream);
+    launch_dm<64, MODE>(a, grid, stream);
   return hipGetLastError();
+}
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream) { return launch_mode<0>(a, stream); }
+
+hipError_t launch_append_fp8(const AppendArgs& a, bool bf16, hipStream_t stream) {
+  return bf16 ? launch_mode<1>(a, stream) : launch_mode<2>(a, stream);
 }
 
 }  // namespace attn

@@ -191,6 +191,37 @@ def decode_inputs(case: DecodeCase, nan_fill: bool = False, ctx_lens=None):
     return dict(q=q, k_cache=kc, v_cache=vc, block_table=table, ctx_lens=ctx)
 
 
+E4M3_NAN = 0x7F  # an E4M3 NaN code (S.1111.111)
+
+
+def e4m3_codes(rng, shape, exp_lo=4, exp_hi=9, p_zero=0.02, p_sub=0.02):
+    """Random E4M3 codes (uint8) drawn field by field: random sign and mantissa,
+    exponent field uniform in [exp_lo, exp_hi] (values of magnitude 2^-3 ..
+    1.875 * 2^2 by default), a fraction p_zero of zeros and p_sub of subnormals
+    (exponent field 0). No arithmetic on values: the codes are the inputs."""
+    sign = rng.integers(0, 2, shape).astype(np.uint8) << 7
+    exp = rng.integers(exp_lo, exp_hi + 1, shape).astype(np.uint8)
+    mant = rng.integers(0, 8, shape).astype(np.uint8)
+    u = rng.random(shape)
+    exp = np.where(u < p_zero + p_sub, 0, exp).astype(np.uint8)
+    mant = np.where(u < p_zero, 0, mant).astype(np.uint8)
+    return (sign | (exp << 3) | mant).astype(np.uint8)
+
+
+def decode_inputs_fp8(case: DecodeCase, nan_fill: bool = False, ctx_lens=None):
+    """decode_inputs with E4M3 caches: q, block_table and ctx_lens as there;
+    k_cache / v_cache are uint8 codes from e4m3_codes (generator seeded with
+    seed + 1000). With ``nan_fill`` every unused slot holds the NaN code."""
+    x = decode_inputs(case, nan_fill=True, ctx_lens=ctx_lens)
+    rng = np.random.default_rng(case.seed + 1000)
+    k8 = e4m3_codes(rng, x["k_cache"].shape)
+    v8 = e4m3_codes(rng, x["v_cache"].shape)
+    if nan_fill:
+        k8[np.isnan(x["k_cache"])] = E4M3_NAN
+        v8[np.isnan(x["v_cache"])] = E4M3_NAN
+    return dict(q=x["q"], k_cache=k8, v_cache=v8, block_table=x["block_table"], ctx_lens=x["ctx_lens"])
+
+
 def chunk_inputs(case: ChunkCase, nan_fill: bool = False, starts=None, lens=None):
     """Return dict(q, k_new, v_new, k_cache, v_cache, block_table, start_pos, new_lens, ctx_lens).
 
@@ -283,15 +314,16 @@ def prefill_flops(B, Hq, Tq, Tk, D, causal, seq_lens=None):
     return 4.0 * D * Hq * pairs
 
 
-def decode_bytes(ctx_lens, Hq, Hkv, D, elem=2, max_blocks=None):
+def decode_bytes(ctx_lens, Hq, Hkv, D, elem=2, max_blocks=None, kv_elem=None):
     """Algorithmic HBM bytes of one paged decode call.
 
-    K and V of every valid token, read once per kv head, plus q, o (elem bytes),
-    lse (fp32), ctx_lens and the block-table entries actually read.
+    K and V of every valid token, read once per kv head (kv_elem bytes per
+    element, default elem; 1 for an E4M3 cache), plus q, o (elem bytes), lse
+    (fp32), ctx_lens and the block-table entries actually read.
     """
     ctx = np.asarray(ctx_lens, dtype=np.int64)
     B = ctx.shape[0]
-    kv = int(ctx.sum()) * Hkv * D * elem * 2
+    kv = int(ctx.sum()) * Hkv * D * (elem if kv_elem is None else kv_elem) * 2
     qo = 2 * B * Hq * D * elem
     lse = B * Hq * 4
     table = int(((ctx + BLOCK - 1) // BLOCK).sum()) * 4
