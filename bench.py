@@ -5,6 +5,8 @@ One step = one pass of the whole hot path on seeded synthetic inputs:
   * causal bf16 prefill, B=1, Hq=32, Hkv=8, T=16384, D=128 (attn_fwd),
   * paged bf16 decode, B=64, Hq=12, Hkv=2, D=128, ctx ~ U[512, 4096],
     16-token blocks (attn_decode_paged), and
+  * the same decode over an FP8 (E4M3) cache, one byte per element, codes
+    drawn field by field (attn_decode_paged_fp8), and
   * a chunked prefill through the paged cache: 1024-token chunks of 4
     sequences with cached prefixes ~ U[2048, 8192], Llama3-8B heads
     (attn_cache_append of the chunk's K/V into each of 8 layers' caches,
@@ -44,6 +46,7 @@ KERNEL_SOURCES = {
     "decode": ["tiled_attention_02_amd/csrc/decode_paged.hip", "tiled_attention_02_amd/csrc/attn_device.h"],
     "chunked_prefill": ["tiled_attention_02_amd/csrc/prefill_fwd.hip", "tiled_attention_02_amd/csrc/attn_device.h"],
     "append": ["tiled_attention_02_amd/csrc/paged_cache.hip"],
+    "decode_fp8": ["tiled_attention_02_amd/csrc/decode_paged.hip", "tiled_attention_02_amd/csrc/attn_device.h"],
 }
 APPEND_LAYERS = 8
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
@@ -76,7 +79,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-flush", action="store_true", help="skip the cache flush between calls")
-    p.add_argument("--only", choices=["prefill", "decode", "chunked"], default=None,
+    p.add_argument("--only", choices=["prefill", "decode", "decode_fp8", "chunked"], default=None,
                    help="profile helper: run only one of the two calls (not a benchmark line)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="run a plain device copy of this many MiB (counter calibration) and exit")
@@ -131,6 +134,25 @@ def cpu_baseline_decode(x, case, nseq=64, min_seconds=5.0):
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": _oracle_threads(), "kind": "oracle",
             "sample": f"float64 oracle on the whole batch ({nseq} sequences), repeated {reps} times; "
                       f"{dt:.1f} s wall"}
+
+
+def cpu_baseline_decode_fp8(x, case, ks, vs, nseq=64, min_seconds=5.0):
+    import workloads as W
+    from oracle import fp8 as F8
+    sl = slice(0, nseq)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        F8.decode_paged_fp8(x["q"][sl], x["k_cache"], x["v_cache"], ks, vs, x["block_table"][sl], x["ctx_lens"][sl],
+                            case.scale)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    nbytes = W.decode_bytes(x["ctx_lens"][sl], case.Hq, case.Hkv, case.D, kv_elem=1) * reps
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": _oracle_threads(), "kind": "oracle",
+            "sample": f"float64 oracle (dequantize, then the decode definition) on the whole batch ({nseq} "
+                      f"sequences), repeated {reps} times; {dt:.1f} s wall"}
 
 
 def cpu_baseline_chunked(x, case, nseq=1):
@@ -261,6 +283,14 @@ def main():
     flush_rows = flush_src.view(-1, 4096)
     flush_dst = torch.empty(flush_rows.shape[0], dtype=torch.float32, device=dev)
 
+    # the decode batch again, over an E4M3 cache (same q, table and lengths)
+    xd8 = W.decode_inputs_fp8(dc)
+    KS8, VS8 = 0.25, 0.0625
+    kc8 = torch.from_numpy(xd8["k_cache"]).to(dev)
+    vc8 = torch.from_numpy(xd8["v_cache"]).to(dev)
+    do8 = torch.empty_like(dq)
+    dlse8 = torch.empty_like(dlse)
+
     cc = W.CHUNK
     log(f"[bench] building inputs: {cc.name}")
     xc = W.chunk_inputs(cc)
@@ -281,11 +311,13 @@ def main():
 
     pflops = W.prefill_flops(pc.B, pc.Hq, pc.T, pc.T, pc.D, True)
     dbytes = W.decode_bytes(xd["ctx_lens"], dc.Hq, dc.Hkv, dc.D)
+    d8bytes = W.decode_bytes(xd8["ctx_lens"], dc.Hq, dc.Hkv, dc.D, kv_elem=1)
     cflops = W.chunk_flops(xc["ctx_lens"], xc["new_lens"], cc.Hq, cc.D, True)
     abytes = W.append_bytes(xc["new_lens"], cc.Hkv, cc.D)
     run_p = args.only in (None, "prefill")
     run_d = args.only in (None, "decode")
     run_c = args.only in (None, "chunked")
+    run_d8 = args.only in (None, "decode_fp8")
 
     def evict():
         # read-only pass over 1 GiB: pushes the inputs out of every cache level
@@ -304,6 +336,11 @@ def main():
             evs[2].record()
             ta.attn_decode_paged(dq, kc, vc, bt, cl, scale=dc.scale, out=do, lse=dlse, workspace=ws)
             evs[3].record()
+        if run_d8:
+            evict()
+            evs[8].record()
+            ta.attn_decode_paged_fp8(dq, kc8, vc8, KS8, VS8, bt, cl, scale=dc.scale, out=do8, lse=dlse8, workspace=ws)
+            evs[9].record()
         if run_c:
             # the chunk's K/V go into the cache (every layer), then the chunk
             # attends to prefix + itself (first layer's cache)
@@ -317,7 +354,7 @@ def main():
             ta.attn_fwd_paged(cq, ckc, cvc, cbt, ccl, cnl, scale=cc.scale, causal=True, out=co, lse=clse)
             evs[7].record()
 
-    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(8)]  # noqa: E731
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(10)]  # noqa: E731
     for i in range(args.warmup):
         step(mk())
     torch.cuda.synchronize()
@@ -333,13 +370,16 @@ def main():
     d_ms = [e[2].elapsed_time(e[3]) for e in evs] if run_d else [float("nan")]
     a_ms = [e[4].elapsed_time(e[5]) / APPEND_LAYERS for e in evs] if run_c else [float("nan")]
     c_ms = [e[6].elapsed_time(e[7]) for e in evs] if run_c else [float("nan")]
+    d8_ms = [e[8].elapsed_time(e[9]) for e in evs] if run_d8 else [float("nan")]
     p_avg, d_avg = float(np.mean(p_ms)), float(np.mean(d_ms))
     a_avg, c_avg = float(np.mean(a_ms)), float(np.mean(c_ms))
+    d8_avg = float(np.mean(d8_ms))
     log(f"[bench] prefill {p_avg:.3f} ms (min {min(p_ms):.3f}); decode {d_avg * 1e3:.1f} us "
-        f"(min {min(d_ms) * 1e3:.1f}); append {a_avg * 1e3:.1f} us; chunked prefill {c_avg * 1e3:.1f} us; "
+        f"(min {min(d_ms) * 1e3:.1f}); fp8 decode {d8_avg * 1e3:.1f} us; append {a_avg * 1e3:.1f} us; chunked prefill {c_avg * 1e3:.1f} us; "
         f"wall/step {wall / args.steps * 1e3:.2f} ms")
     if args.only:
-        print(json.dumps({"only": args.only, "prefill_ms": p_avg, "decode_ms": d_avg, "append_ms": a_avg,
+        print(json.dumps({"only": args.only, "prefill_ms": p_avg, "decode_ms": d_avg, "decode_fp8_ms": d8_avg,
+                          "append_ms": a_avg,
                           "chunked_prefill_ms": c_avg}))
         return
 
@@ -347,6 +387,7 @@ def main():
     d_gbs = dbytes / (d_avg * 1e-3) / 1e9
     c_tfs = cflops / (c_avg * 1e-3) / 1e12
     a_gbs = abytes / (a_avg * 1e-3) / 1e9
+    d8_gbs = d8bytes / (d8_avg * 1e-3) / 1e9
     out = {
         "metric": METRIC,
         "value": round(p_tfs, 2),
@@ -354,14 +395,15 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(p_avg + d_avg + APPEND_LAYERS * a_avg + c_avg, 4),
+        "ms_per_step": round(p_avg + d_avg + d8_avg + APPEND_LAYERS * a_avg + c_avg, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "causal bf16 prefill B=1 Hq=32 Hkv=8 T=16384 D=128 (value) + paged bf16 decode "
-                               "B=64 Hq=12 Hkv=2 D=128 ctx~U[512,4096] block=16 (decode) + chunked bf16 prefill "
+                               "B=64 Hq=12 Hkv=2 D=128 ctx~U[512,4096] block=16 (decode; again over an E4M3 cache: decode_fp8) + "
+                               "chunked bf16 prefill "
                                "B=4 Hq=32 Hkv=8 D=128 prefix~U[2048,8192] chunk=1024 through the block table "
                                "(chunked)",
                    "prefill_gflop_per_call": round(pflops / 1e9, 3),
@@ -377,6 +419,13 @@ def main():
                                 "frac": round(d_gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic("decode"),
                                 "kernels": "decode_split_kernel + decode_combine_kernel",
                                 "algorithmic_bytes_per_call": dbytes}},
+        "decode_fp8": {"value": round(d8_gbs, 1), "unit": "GB/s", "us_per_call": round(d8_avg * 1e3, 2),
+                       "k_scale": KS8, "v_scale": VS8,
+                       "roofline": {"bound": "hbm", "achieved": round(d8_gbs, 1), "peak": PEAK_HBM_GBS,
+                                    "unit": "GB/s", "frac": round(d8_gbs / PEAK_HBM_GBS, 4),
+                                    "traffic": measured_traffic("decode_fp8"),
+                                    "kernels": "decode_split_kernel<fp8> + decode_combine_kernel",
+                                    "algorithmic_bytes_per_call": d8bytes}},
         "chunked": {
             "workload": cc.name, "ctx_lens": [int(c) for c in xc["ctx_lens"]],
             "prefill": {"value": round(c_tfs, 2), "unit": "TFLOP/s", "us_per_call": round(c_avg * 1e3, 2),
@@ -397,6 +446,8 @@ def main():
         out["cpu_baseline"] = cpu_baseline_prefill(xp, pc)
         log("[bench] cpu baseline: float64 oracle on a sample of the decode workload")
         out["decode"]["cpu_baseline"] = cpu_baseline_decode(xd, dc)
+        log("[bench] cpu baseline: float64 oracle on the FP8 decode workload")
+        out["decode_fp8"]["cpu_baseline"] = cpu_baseline_decode_fp8(xd8, dc, KS8, VS8)
         log("[bench] cpu baseline: float64 oracle on a sample of the chunked-prefill workload")
         out["chunked"]["cpu_baseline"] = cpu_baseline_chunked(xc, cc)
     print(json.dumps(out), flush=True)

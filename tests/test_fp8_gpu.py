@@ -103,7 +103,9 @@ def test_fp8_decode_extreme_codes(ta):
 
 
 def test_fp8_decode_equals_16bit_decode_of_dequantized_cache(ta):
-    """Power-of-two scales: the FP8 decode and the 16-bit decode over the dequantized values agree bit for bit."""
+    """Power-of-two scales: the FP8 decode and the 16-bit decode over the dequantized values (exact in bf16)
+    agree bit for bit: both kernels take the same online-softmax steps, and the scales fold out of the
+    products exactly."""
     import torch
     case = W.DecodeCase("fp8 vs bf16", B=16, Hq=12, Hkv=2, D=128, dtype="bf16", ctx_lo=1, ctx_hi=3000, seed=86)
     x = W.decode_inputs_fp8(case, nan_fill=False)

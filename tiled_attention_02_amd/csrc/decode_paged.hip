@@ -13,15 +13,15 @@
 // key axis; the merge is the softmax-statistics update of blockwise attention.
 //
 // Decomposition: one wavefront per (split of 256 tokens = 16 cache blocks,
-// kv head, sequence). It streams its blocks two at a time (32 tokens per
-// step) with the next pair's loads in flight, and serves all G = Hq/Hkv query
-// heads of the kv head from one read of each block:
+// kv head, sequence). It streams its blocks two at a time (a step of 32
+// tokens) with the next step's loads in flight, and serves all G = Hq/Hkv
+// query heads of the kv head from one read of each block:
 //   S^T = K Q^T       v_mfma_f32_16x16x32: rows = 16 tokens of a block,
 //                     columns = query heads (G <= 16, the rest zero).
 //   O  += P V         v_mfma_f32_16x16x32: rows = heads, columns = 16 of D,
-//                     contraction = the 32 tokens of the two blocks.
+//                     contraction = 32 tokens (two blocks) per product.
 // Every (block, kv head) of K and V is 16*D contiguous elements, read once,
-// straight into LDS; the transposed scores of the two blocks are already the
+// straight into LDS; the transposed scores of two blocks are already the
 // A operand (P) of the second product, and V's operand comes from LDS through
 // the transposing reads. The split's partial (O normalised, log2 of its sum)
 // is written from registers; a second, light kernel merges the partials.
@@ -48,22 +48,26 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
-// LDS image of one pair of cache blocks: K block 0, K block 1, V block 0,
-// V block 1, each 16 token rows of RB bytes, row-major with a 16-byte-chunk
+// LDS image of one step's cache blocks: K blocks 0 .. NB-1, then V blocks
+// 0 .. NB-1, each 16 token rows of RB bytes, row-major with a 16-byte-chunk
 // XOR swizzle: chunk c of row r sits in slot c ^ f(r). LDS serves 256 bytes
 // per cycle (16 lanes of a 16-byte access, 32 lanes of an 8-byte one); f makes
 // the K operand reads and the transposing V reads of each lane group hit
 // distinct banks.
 template <int D, bool KV8>
-struct PairLds {
+struct StepLds {
+  // cache blocks per step; 4 for the E4M3 cache (the same 16 KiB per step as
+  // the 16-bit one) measured slower: twice the LDS per wavefront halves the
+  // wavefronts a CU keeps in flight
+  static constexpr int NB = 2;
   static constexpr int EB = KV8 ? 1 : 2;     // bytes per cache element
   static constexpr int RB = EB * D;          // bytes per token row
   static constexpr int BLK = 16 * RB;        // one (block, kv head) of K or V
-  static constexpr int BYTES = 4 * BLK;
+  static constexpr int BYTES = 2 * NB * BLK;
   static constexpr int RPI = 1024 / RB;      // rows filled by one wavefront load instruction
   static constexpr int NI = 16 / RPI;        // load instructions per block
   static constexpr int C8 = RB / 16;         // 16-byte chunks per row
-  static constexpr int LOADS = 4 * NI;       // load instructions per pair
+  static constexpr int LOADS = 2 * NB * NI;  // load instructions per step
 };
 
 // 16-bit cache: one swizzle for K and V. K reads: 16 rows at one chunk per
@@ -78,7 +82,7 @@ __device__ __forceinline__ int dswz(int row) {
 // two adjacent 8-byte chunks per 32 lanes): rows of equal parity (D = 128; of
 // equal row % 4 at D = 64) must take distinct chunk swaps. V reads
 // (ds_read_b64_tr_b8) take rows 0..7 of both V blocks at two adjacent 8-byte
-// chunks per 32 lanes, so the V swizzle also depends on the block.
+// chunks per 32 lanes, so the V swizzle also depends on the block's parity.
 template <int D>
 __device__ __forceinline__ int kswz8(int row) {
   if constexpr (D == 128) return (row >> 1) & 7;
@@ -100,18 +104,18 @@ __device__ __forceinline__ int vswz(int row, int blk) {
   else return dswz<D>(row);
 }
 
-// Per-lane byte offsets, identical for every pair.
+// Per-lane byte offsets, identical for every step.
 template <int D, bool KV8>
 struct DecOffs {
-  int ldk[PairLds<D, KV8>::NI];     // chunk fetched by load instruction i of a K block
-  int ldv[2][PairLds<D, KV8>::NI];  // ... of V block 0 / 1
+  int ldk[StepLds<D, KV8>::NI];     // chunk fetched by load instruction i of a K block
+  int ldv[2][StepLds<D, KV8>::NI];  // ... of an even / odd V block
   int k[D / 32];                    // K operand of k-step s
   int v[D / 16];                    // V operand of product n (16-bit: first of two reads; E4M3: the read)
 };
 
 template <int D, bool KV8>
 __device__ __forceinline__ void make_dec_offs(DecOffs<D, KV8>& o, int lane) {
-  using L = PairLds<D, KV8>;
+  using L = StepLds<D, KV8>;
   const int g = lane >> 4, c = lane & 15;
   // load instruction i writes rows RPI*i .. (1 KiB of consecutive LDS, lane l
   // at 16 l): lane l fetches the logical chunk its slot holds
@@ -142,28 +146,29 @@ __device__ __forceinline__ void make_dec_offs(DecOffs<D, KV8>& o, int lane) {
     // V operand of product n via ds_read_b64_tr_b8: within each 16-lane group,
     // lane j receives byte (j & 7) of the 8 bytes read by lanes 2e + (j >> 3),
     // e = 0..7. So lane s addresses token e = s >> 1 of the group's 8 (block
-    // e >> 2, row 4g + e % 4: P's contraction order) at columns 16n + 8(s & 1)
-    // .. +8, and lane j receives column 16n + j of the 8 tokens.
+    // e >> 2 of a block pair, row 4g + e % 4: P's contraction order) at
+    // columns 16n + 8(s & 1) .. +8, and lane j receives column 16n + j of the
+    // 8 tokens. Offsets of the step's first block pair; the next pair is 2 BLK on.
     const int e = c >> 1, bb = e >> 2, row = 4 * g + (e & 3);
 #pragma unroll
     for (int n = 0; n < D / 16; ++n)
-      o.v[n] = (2 + bb) * L::BLK + row * L::RB + 16 * (n ^ vswz8<D>(row, bb)) + 8 * (c & 1);
+      o.v[n] = (L::NB + bb) * L::BLK + row * L::RB + 16 * (n ^ vswz8<D>(row, bb)) + 8 * (c & 1);
   }
 }
 
-// Starts the loads of one pair of blocks (K and V of both) into an LDS pair
+// Starts the loads of one step's blocks (K and V of each) into an LDS step
 // buffer: buffer loads that write LDS directly, each instruction 1 KiB of
-// consecutive bytes of one block (whole rows). The second block may lie past
-// the sequence's last block (live1 == false): it then re-reads the first one
-// (a cache hit), since every token there is masked or zeroed anyway, which
-// keeps the number of loads per pair fixed for the in-order memory counter.
+// consecutive bytes of one block (whole rows). ph[j] is block j's physical
+// block; a block past the sequence's last one carries the step's first block
+// instead (a cache hit: every token there is masked or zeroed anyway), which
+// keeps the number of loads per step fixed for the in-order memory counter.
 template <int D, bool KV8>
-__device__ __forceinline__ void load_pair(char* buf, const char* kbase, const char* vbase, size_t block_stride,
-                                          int ph0, int ph1, bool live1, const DecOffs<D, KV8>& o) {
-  using L = PairLds<D, KV8>;
+__device__ __forceinline__ void load_step(char* buf, const char* kbase, const char* vbase, size_t block_stride,
+                                          const int (&ph)[StepLds<D, KV8>::NB], const DecOffs<D, KV8>& o) {
+  using L = StepLds<D, KV8>;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const size_t off = (size_t)(j && live1 ? ph1 : ph0) * block_stride;
+  for (int j = 0; j < L::NB; ++j) {
+    const size_t off = (size_t)ph[j] * block_stride;
 #pragma unroll
     for (int kv = 0; kv < 2; ++kv) {
       const uint64_t p = reinterpret_cast<uint64_t>((kv ? vbase : kbase) + off);
@@ -172,14 +177,14 @@ __device__ __forceinline__ void load_pair(char* buf, const char* kbase, const ch
                           (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
       const __amdgpu_buffer_rsrc_t rsrc =
           __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(pu), (short)0, L::BLK, kDecodeDword3);
-      char* dst = buf + (2 * kv + j) * L::BLK;
+      char* dst = buf + (L::NB * kv + j) * L::BLK;
       // the host compilation pass of this file does not know this builtin (it
       // would drop the kernels' host stubs); the function only runs on the device
 #if defined(__HIP_DEVICE_COMPILE__)
 #pragma unroll
       for (int i = 0; i < L::NI; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + i * 1024), 16,
-                                                 kv ? o.ldv[j][i] : o.ldk[i], 0, 0, /*non-temporal*/ 2);
+                                                 kv ? o.ldv[j & 1][i] : o.ldk[i], 0, 0, /*non-temporal*/ 2);
 #else
       (void)rsrc;
       (void)dst;
@@ -198,31 +203,32 @@ struct WaveState {
   float m, l, lr;
 };
 
-// One step: the 32 tokens starting at t0, from an LDS pair buffer. In the
-// sequence's last pair (TAIL) tokens >= ctx are masked, and their V rows are
-// zeroed in LDS first, since unused cache slots may hold anything, NaN
+// One step: the 16 * NB tokens starting at t0, from an LDS step buffer. In
+// the sequence's last step (TAIL) tokens >= ctx are masked, and their V rows
+// are zeroed in LDS first, since unused cache slots may hold anything, NaN
 // included.
 template <class T, int D, bool KV8, bool TAIL>
-__device__ __forceinline__ void pair_step(WaveState<D>& st, char* buf, const u32x4 (&qf)[D / 32],
-                                          const DecOffs<D, KV8>& o, int t0, int ctx, float cexp, int lane) {
-  using L = PairLds<D, KV8>;
+__device__ __forceinline__ void step_compute(WaveState<D>& st, char* buf, const u32x4 (&qf)[D / 32],
+                                             const DecOffs<D, KV8>& o, int t0, int ctx, float cexp, int lane) {
+  using L = StepLds<D, KV8>;
+  constexpr int NB = L::NB;
   constexpr int KS = D / 32;
   constexpr int VC = D / 16;
   const int g = lane >> 4;
   if constexpr (TAIL) {
     // whole rows: the swizzle only permutes chunks within a row
 #pragma unroll
-    for (int k = 0; k < 32 * L::C8 / 64; ++k) {
+    for (int k = 0; k < 16 * NB * L::C8 / 64; ++k) {
       const int idx = lane + 64 * k;
-      const int row = idx / L::C8;  // 0..31 over the two blocks
+      const int row = idx / L::C8;  // 0 .. 16 NB - 1 over the step's blocks
       if (t0 + row >= ctx)
-        *reinterpret_cast<u32x4*>(buf + 2 * L::BLK + (row >> 4) * L::BLK + (row & 15) * L::RB + 16 * (idx % L::C8)) =
-            u32x4{0, 0, 0, 0};
+        *reinterpret_cast<u32x4*>(buf + NB * L::BLK + (row >> 4) * L::BLK + (row & 15) * L::RB +
+                                  16 * (idx % L::C8)) = u32x4{0, 0, 0, 0};
     }
   }
-  f32x4 sacc[2];
+  f32x4 sacc[NB];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < NB; ++j) {
     sacc[j] = f32x4{};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -236,13 +242,15 @@ __device__ __forceinline__ void pair_step(WaveState<D>& st, char* buf, const u32
   }
   if constexpr (TAIL) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         sacc[j][r] = (t0 + 16 * j + 4 * g + r) >= ctx ? -__builtin_inff() : sacc[j][r];
   }
-  float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
-                   fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
+  float mx = -__builtin_inff();
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+    mx = fmaxf(mx, fmaxf(fmaxf(sacc[j][0], sacc[j][1]), fmaxf(sacc[j][2], sacc[j][3])));
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = half_swap_max(mx) * cexp;
   const bool grow = mx > st.m + kDecodeLazy;
@@ -261,44 +269,52 @@ __device__ __forceinline__ void pair_step(WaveState<D>& st, char* buf, const u32
     }
   }
   const float msub = st.m == -__builtin_inff() ? 0.f : st.m;
-  float pv[8];
+  float pv[4 * NB];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < NB; ++j)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       pv[4 * j + r] = fast_exp2(__builtin_fmaf(sacc[j][r], cexp, -msub));
       st.l += pv[4 * j + r];
     }
-  const u32x4 pf = {T::pack2(pv[0], pv[1]), T::pack2(pv[2], pv[3]), T::pack2(pv[4], pv[5]),
-                    T::pack2(pv[6], pv[7])};
-  // the running sum adds the rounded probabilities that the P.V product applies
+  // P of each block pair h: in lane group g, tokens 4g .. 4g+3 of block 2h,
+  // then of block 2h + 1; the transposing reads give V in the same order
+  u32x4 pf[NB / 2];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) st.lr = T::sum2(pf[e], st.lr);
-  // P's k order in lane group g: tokens 4g .. 4g+3 of block 0, then of block 1;
-  // the two transposing reads give V in the same order
+  for (int h = 0; h < NB / 2; ++h) {
+    const float* v = pv + 8 * h;
+    pf[h] = u32x4{T::pack2(v[0], v[1]), T::pack2(v[2], v[3]), T::pack2(v[4], v[5]), T::pack2(v[6], v[7])};
+    // the running sum adds the rounded probabilities that the P.V product applies
+#pragma unroll
+    for (int e = 0; e < 4; ++e) st.lr = T::sum2(pf[h][e], st.lr);
+  }
 #pragma unroll
   for (int n = 0; n < VC; ++n) {
     if constexpr (KV8) {
-      const i32x2 v8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(buf + o.v[n]));
-      st.o[n] = T::mfma16(pf, e4m3x8<T>(__builtin_bit_cast(u32x2, v8)), st.o[n]);
+#pragma unroll
+      for (int h = 0; h < NB / 2; ++h) {
+        const i32x2 v8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(buf + o.v[n] + 2 * h * L::BLK));
+        st.o[n] = T::mfma16(pf[h], e4m3x8<T>(__builtin_bit_cast(u32x2, v8)), st.o[n]);
+      }
     } else {
       const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(buf + 2 * L::BLK + o.v[n]));
       const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(buf + 3 * L::BLK + o.v[n]));
       const u32x2 a0 = __builtin_bit_cast(u32x2, v0);
       const u32x2 a1 = __builtin_bit_cast(u32x2, v1);
-      st.o[n] = T::mfma16(pf, u32x4{a0[0], a0[1], a1[0], a1[1]}, st.o[n]);
+      st.o[n] = T::mfma16(pf[0], u32x4{a0[0], a0[1], a1[0], a1[1]}, st.o[n]);
     }
   }
 }
 
 template <class T, int D, bool KV8>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
-  using L = PairLds<D, KV8>;
+  using L = StepLds<D, KV8>;
   constexpr int KS = D / 32;
   constexpr int VC = D / 16;
-  constexpr int NP = kSplitBlocks / 2;  // block pairs per split
+  constexpr int NB = L::NB;
+  constexpr int NS = kSplitBlocks / NB;  // steps per split
   static_assert(D == 128 || D == 64, "head size");
-  // two pair buffers, separate LDS arrays so that reads of one are never
+  // two step buffers, separate LDS arrays so that reads of one are never
   // ordered behind the loads into the other
   __shared__ __align__(16) char buf0[L::BYTES];
   __shared__ __align__(16) char buf1[L::BYTES];
@@ -337,7 +353,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     return;
   }
   const int nb = min(kSplitBlocks, nblk - blk0);  // blocks of this split, >= 1
-  const int np = (nb + 1) >> 1;
+  const int ns = (nb + NB - 1) / NB;  // live steps
 
   const size_t head_bytes = (size_t)L::BLK;  // one (block, kv head)
   const size_t block_stride = (size_t)a.Hkv * head_bytes;
@@ -350,7 +366,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 
   // ---- q^T operand: head c, columns 32s + 8g .. +8 (step s, lane group g);
   // loaded first: the memory counter is in order, so the first step then waits
-  // only for q and its own pair
+  // only for q and its own step
   u32x4 qf[KS];
   {
     const bool live = c < G && a.qmode != 2;
@@ -364,16 +380,35 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     }
   }
 
-  // Pair q's table entries; a pair beyond the split (q >= np) re-reads pair 0
-  // (cache hits) so that every pair issues the same loads.
-  auto ph = [&](int q, int j) { return q < np ? phys[2 * q + j] : phys[0]; };
-  // The scheduling barriers keep q's loads and the two pairs' loads in this
+  // Step q's physical blocks: a block past the split's last one carries the
+  // step's first block, and a step past the split re-reads step 0 (cache
+  // hits), so that every step issues the same loads. q is a compile-time
+  // index wherever this is used (the step loop is unrolled); the selection is
+  // made between values (readfirstlane), not between array elements, which
+  // the compiler would turn into one dynamically indexed load and so keep
+  // phys[] in scratch memory.
+  auto step_blocks = [&](int q, int (&ph)[NB]) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int i = NB * q + j;
+      const int own = __builtin_amdgcn_readfirstlane(phys[i]);
+      const int first = __builtin_amdgcn_readfirstlane(phys[NB * q]);
+      const int zero = __builtin_amdgcn_readfirstlane(phys[0]);
+      ph[j] = i < nb ? own : (q < ns ? first : zero);
+    }
+  };
+  // The scheduling barriers keep q's loads and the two steps' loads in this
   // order (the memory counter is in order; the waits below rely on it).
-  __builtin_amdgcn_sched_barrier(0);
-  load_pair<D, KV8>(buf0, kbase, vbase, block_stride, phys[0], phys[1], nb > 1, o);
-  __builtin_amdgcn_sched_barrier(0);
-  load_pair<D, KV8>(buf1, kbase, vbase, block_stride, ph(1, 0), ph(1, 1), 3 < nb, o);
-  __builtin_amdgcn_sched_barrier(0);
+  {
+    int ph[NB];
+    step_blocks(0, ph);
+    __builtin_amdgcn_sched_barrier(0);
+    load_step<D, KV8>(buf0, kbase, vbase, block_stride, ph, o);
+    __builtin_amdgcn_sched_barrier(0);
+    step_blocks(1, ph);
+    load_step<D, KV8>(buf1, kbase, vbase, block_stride, ph, o);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
   WaveState<D> st;
 #pragma unroll
@@ -383,24 +418,26 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   st.lr = 0.f;
 
 #pragma unroll
-  for (int p = 0; p < NP; ++p) {
-    if (p >= np) break;  // wave-uniform
+  for (int p = 0; p < NS; ++p) {
+    if (p >= ns) break;  // wave-uniform
     char* buf = (p & 1) ? buf1 : buf0;
-    // pair p has landed once at most the next pair's loads are outstanding
-    if (p + 1 < NP)
+    // step p has landed once at most the next step's loads are outstanding
+    if (p + 1 < NS)
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L::LOADS) : "memory");
     else
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    const int t0 = (blk0 + 2 * p) * kDecodeBlock;
-    if (t0 + 32 > ctx)
-      pair_step<T, D, KV8, true>(st, buf, qf, o, t0, ctx, cexp, lane);
+    const int t0 = (blk0 + NB * p) * kDecodeBlock;
+    if (t0 + 16 * NB > ctx)
+      step_compute<T, D, KV8, true>(st, buf, qf, o, t0, ctx, cexp, lane);
     else
-      pair_step<T, D, KV8, false>(st, buf, qf, o, t0, ctx, cexp, lane);
-    if (p + 2 < NP) {
+      step_compute<T, D, KV8, false>(st, buf, qf, o, t0, ctx, cexp, lane);
+    if (p + 2 < NS) {
       // every read of this buffer has returned before new data is written to it
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      const int q = p + 2 < NP ? p + 2 : 0;  // in range also where the branch is dead
-      load_pair<D, KV8>(buf, kbase, vbase, block_stride, ph(q, 0), ph(q, 1), 2 * q + 1 < nb, o);
+      const int q = p + 2 < NS ? p + 2 : 0;  // in range also where the branch is dead
+      int ph[NB];
+      step_blocks(q, ph);
+      load_step<D, KV8>(buf, kbase, vbase, block_stride, ph, o);
     }
   }
 
