@@ -222,6 +222,16 @@ def decode_inputs_fp8(case: DecodeCase, nan_fill: bool = False, ctx_lens=None):
     return dict(q=x["q"], k_cache=k8, v_cache=v8, block_table=x["block_table"], ctx_lens=x["ctx_lens"])
 
 
+def rope_table(max_pos: int, D: int, base: float = 500000.0) -> np.ndarray:
+    """Input table of a rotary embedding, float32 [max_pos, D]: cos(p * theta_i) in column i and
+    sin(p * theta_i) in column D/2 + i, theta_i = base^(-2i/D) (the Llama-3 frequencies), computed in
+    float64 and rounded to float32. An input like a weight: the kernels and the oracle only read it."""
+    i = np.arange(D // 2, dtype=np.float64)
+    theta = base ** (-2.0 * i / D)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * theta[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+
+
 def chunk_inputs(case: ChunkCase, nan_fill: bool = False, starts=None, lens=None):
     """Return dict(q, k_new, v_new, k_cache, v_cache, block_table, start_pos, new_lens, ctx_lens).
 
