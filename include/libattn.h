@@ -211,6 +211,47 @@ attn_status attn_decode_paged_fp8(const void* q, const void* k_cache, const void
                                   float scale, attn_dtype dtype, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Rotary position embedding fused into the paged path. The Llama3-8B trace of
+ * the comemg.com page (section "模型推理") shows RoPE among the small kernels
+ * between the products and attention; fusing such a step into its neighbour
+ * saves a round trip of the tensor through memory (the-ai.news page cited
+ * above, operator-fusion section). The rotation is the half-split rotary
+ * embedding of the Llama family: for a row x at position p and i < D/2,
+ *   x'[i] = x[i] c - x[i + D/2] s,   x'[i + D/2] = x[i + D/2] c + x[i] s,
+ * with c = rope[p, i] and s = rope[p, D/2 + i] from the caller's table
+ * `rope`: device fp32 [max_pos, D], 16-byte aligned (cos(p theta_i) in the
+ * first half of a row, sin in the second). Computed in fp32, rounded once to
+ * the 16-bit type. Positions >= max_pos read row max_pos - 1 (caller error).
+ *
+ * attn_cache_append_rope: attn_cache_append with each new K row rotated at its
+ *   position start_pos[b] + i before it is written (V rows unchanged), so the
+ *   cache holds rotated keys.
+ * attn_fwd_paged_rope: attn_fwd_paged with query row i rotated at its position
+ *   ctx_lens[b] - q_lens[b] + i as it is loaded.
+ * attn_decode_paged_rope: attn_decode_paged with the query rotated at position
+ *   ctx_lens[b] - 1 as it is loaded.
+ */
+attn_status attn_cache_append_rope(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                                   const float* rope, int max_pos, const int* block_table,
+                                   const int* start_pos, const int* new_lens, int B, int Hkv, int Tnew,
+                                   int D, int block_size, int max_blocks_per_seq, int num_blocks,
+                                   attn_dtype dtype, hipStream_t stream);
+
+attn_status attn_fwd_paged_rope(const void* q, const void* k_cache, const void* v_cache,
+                                const float* rope, int max_pos, const int* block_table,
+                                const int* ctx_lens, const int* q_lens, void* o, float* lse, int B,
+                                int Hq, int Hkv, int Tq, int D, int block_size, int max_blocks_per_seq,
+                                int num_blocks, float scale, int causal, attn_dtype dtype,
+                                hipStream_t stream);
+
+attn_status attn_decode_paged_rope(const void* q, const void* k_cache, const void* v_cache,
+                                   const float* rope, int max_pos, const int* block_table,
+                                   const int* ctx_lens, void* o, float* lse, int B, int Hq, int Hkv,
+                                   int D, int block_size, int max_blocks_per_seq, int num_blocks,
+                                   float scale, attn_dtype dtype, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
+
 /* Workspace bytes attn_decode_paged needs for these sizes (0 if they are invalid). */
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_blocks_per_seq, int block_size);
 

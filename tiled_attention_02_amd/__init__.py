@@ -13,13 +13,15 @@ import math
 import os
 
 __all__ = ["attn_fwd", "attn_decode_paged", "attn_fwd_paged", "attn_cache_append", "attn_cache_append_fp8",
-           "attn_decode_paged_fp8", "attn_decode_workspace_bytes",
+           "attn_decode_paged_fp8", "attn_cache_append_rope", "attn_fwd_paged_rope", "attn_decode_paged_rope",
+           "attn_decode_workspace_bytes",
            "attn_status_str", "attn_last_error", "AttnError", "lib", "LIB_PATH", "EXPORTS", "BLOCK_SIZE",
            "decode_workspace"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
 EXPORTS = ("attn_fwd", "attn_decode_paged", "attn_fwd_paged", "attn_cache_append", "attn_cache_append_fp8",
-           "attn_decode_paged_fp8", "attn_decode_workspace_bytes", "attn_status_str", "attn_last_error")
+           "attn_decode_paged_fp8", "attn_cache_append_rope", "attn_fwd_paged_rope", "attn_decode_paged_rope",
+           "attn_decode_workspace_bytes", "attn_status_str", "attn_last_error")
 BLOCK_SIZE = 16
 
 ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
@@ -56,6 +58,12 @@ def lib() -> ctypes.CDLL:
     L.attn_cache_append_fp8.restype = i
     L.attn_decode_paged_fp8.argtypes = [vp, vp, vp, f, f, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, sz, vp]
     L.attn_decode_paged_fp8.restype = i
+    L.attn_cache_append_rope.argtypes = [vp, vp, vp, vp, vp, i, vp, vp, vp, i, i, i, i, i, i, i, i, vp]
+    L.attn_cache_append_rope.restype = i
+    L.attn_fwd_paged_rope.argtypes = [vp, vp, vp, vp, i, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, i, vp]
+    L.attn_fwd_paged_rope.restype = i
+    L.attn_decode_paged_rope.argtypes = [vp, vp, vp, vp, i, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, sz, vp]
+    L.attn_decode_paged_rope.restype = i
     L.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
     L.attn_decode_workspace_bytes.restype = sz
     L.attn_status_str.argtypes = [i]
@@ -156,10 +164,11 @@ def decode_workspace(device, nbytes: int):
 
 
 def attn_decode_paged(q, k_cache, v_cache, block_table, ctx_lens, scale: float | None = None, out=None,
-                      lse=None, workspace=None, need_lse: bool = True):
+                      lse=None, workspace=None, need_lse: bool = True, rope=None):
     """Paged one-token decode. q [B,Hq,D]; caches [num_blocks,Hkv,16,D]; block_table int32
-    [B,max_blocks]; ctx_lens int32 [B]. Returns (o [B,Hq,D], lse [B,Hq] float32 or None)."""
-    return _decode(q, k_cache, v_cache, None, block_table, ctx_lens, scale, out, lse, workspace, need_lse)
+    [B,max_blocks]; ctx_lens int32 [B]. rope: optional float32 table [max_pos, D] (cos | sin halves):
+    the query is rotated at position ctx - 1. Returns (o [B,Hq,D], lse [B,Hq] float32 or None)."""
+    return _decode(q, k_cache, v_cache, None, block_table, ctx_lens, scale, out, lse, workspace, need_lse, rope)
 
 
 def attn_decode_paged_fp8(q, k_cache, v_cache, k_scale: float, v_scale: float, block_table, ctx_lens,
@@ -167,10 +176,17 @@ def attn_decode_paged_fp8(q, k_cache, v_cache, k_scale: float, v_scale: float, b
     """Paged one-token decode over E4M3 caches (uint8 [num_blocks,Hkv,16,D]; an entry means
     value(code) * k_scale or * v_scale). q, o bf16 or fp16."""
     return _decode(q, k_cache, v_cache, (k_scale, v_scale), block_table, ctx_lens, scale, out, lse, workspace,
-                   need_lse)
+                   need_lse, None)
 
 
-def _decode(q, k_cache, v_cache, scales, block_table, ctx_lens, scale, out, lse, workspace, need_lse):
+def _check_rope(rope, D):
+    import torch
+    _check(rope.is_cuda and rope.dtype == torch.float32 and rope.is_contiguous() and rope.dim() == 2
+           and rope.shape[1] == D, "rope must be a contiguous float32 GPU tensor [max_pos, D]")
+    return rope.shape[0]
+
+
+def _decode(q, k_cache, v_cache, scales, block_table, ctx_lens, scale, out, lse, workspace, need_lse, rope):
     import torch
     dt = _dtype_code(q)
     _check(q.dim() == 3 and k_cache.dim() == 4 and v_cache.shape == k_cache.shape, "bad q / cache rank or shape")
@@ -198,7 +214,10 @@ def _decode(q, k_cache, v_cache, scales, block_table, ctx_lens, scale, out, lse,
         workspace = decode_workspace(q.device, need)
     tail = (_ptr(out), _ptr(lse), B, Hq, Hkv, D, bs, maxb, NB, ctypes.c_float(scale), dt, _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream(q.device))
-    if scales is None:
+    if rope is not None:
+        st = lib().attn_decode_paged_rope(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(rope), _check_rope(rope, D),
+                                          _ptr(block_table), _ptr(ctx_lens), *tail)
+    elif scales is None:
         st = lib().attn_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(ctx_lens), *tail)
     else:
         st = lib().attn_decode_paged_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.c_float(scales[0]),
@@ -228,7 +247,7 @@ def _check_i32(t, n, name, optional=False):
 
 
 def attn_fwd_paged(q, k_cache, v_cache, block_table, ctx_lens, q_lens=None, scale: float | None = None,
-                   causal: bool = True, out=None, lse=None, need_lse: bool = True):
+                   causal: bool = True, out=None, lse=None, need_lse: bool = True, rope=None):
     """Chunked prefill through the paged cache. q [B,Hq,Tq,D]: row i of sequence b is position
     ctx_lens[b] - q_lens[b] + i (q_lens None: all Tq rows). Returns (o like q, lse [B,Hq,Tq] or None)."""
     import torch
@@ -249,14 +268,17 @@ def attn_fwd_paged(q, k_cache, v_cache, block_table, ctx_lens, q_lens=None, scal
         lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
     if lse is not None:
         _check(lse.shape == (B, Hq, Tq) and lse.dtype == torch.float32 and lse.is_contiguous(), "bad lse")
-    st = lib().attn_fwd_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(ctx_lens),
-                              _ptr(q_lens), _ptr(out), _ptr(lse), B, Hq, Hkv, Tq, D, bs, block_table.shape[1], NB,
-                              ctypes.c_float(scale), int(bool(causal)), dt, _stream(q.device))
+    tail = (_ptr(block_table), _ptr(ctx_lens), _ptr(q_lens), _ptr(out), _ptr(lse), B, Hq, Hkv, Tq, D, bs,
+            block_table.shape[1], NB, ctypes.c_float(scale), int(bool(causal)), dt, _stream(q.device))
+    if rope is not None:
+        st = lib().attn_fwd_paged_rope(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(rope), _check_rope(rope, D), *tail)
+    else:
+        st = lib().attn_fwd_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), *tail)
     _raise(st)
     return out, lse
 
 
-def attn_cache_append(k_new, v_new, k_cache, v_cache, block_table, start_pos, new_lens=None):
+def attn_cache_append(k_new, v_new, k_cache, v_cache, block_table, start_pos, new_lens=None, rope=None):
     """Write k_new/v_new [B,Hkv,Tnew,D] into the paged caches in place: token i < new_lens[b]
     becomes position start_pos[b] + i of sequence b (new_lens None: all Tnew tokens)."""
     dt = _dtype_code(k_new)
@@ -270,9 +292,13 @@ def attn_cache_append(k_new, v_new, k_cache, v_cache, block_table, start_pos, ne
     _check_i32(block_table, block_table.numel(), "block_table")
     _check_i32(start_pos, B, "start_pos")
     _check_i32(new_lens, B, "new_lens", optional=True)
-    st = lib().attn_cache_append(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
-                                 _ptr(start_pos), _ptr(new_lens), B, Hkv, Tnew, D, bs, block_table.shape[1], NB,
-                                 dt, _stream(k_new.device))
+    tail = (_ptr(block_table), _ptr(start_pos), _ptr(new_lens), B, Hkv, Tnew, D, bs, block_table.shape[1], NB, dt,
+            _stream(k_new.device))
+    if rope is not None:
+        st = lib().attn_cache_append_rope(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(rope),
+                                          _check_rope(rope, D), *tail)
+    else:
+        st = lib().attn_cache_append(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), *tail)
     _raise(st)
 
 

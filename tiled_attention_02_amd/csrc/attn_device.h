@@ -50,6 +50,9 @@ struct BF16 {
     const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), one, acc, false);
   }
+  // the two values of a packed pair as fp32 (exact)
+  static __device__ __forceinline__ float lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+  static __device__ __forceinline__ float hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
   // E4M3 codes in bytes 2*HI, 2*HI + 1 of w -> packed pair (low half from the
   // lower byte). Exact: every E4M3 value is a bf16 value.
   template <bool HI>
@@ -75,6 +78,8 @@ struct F16 {
     const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk), one, acc, false);
   }
+  static __device__ __forceinline__ float lo(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w)[0]; }
+  static __device__ __forceinline__ float hi(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w)[1]; }
   // E4M3 codes in bytes 2*HI, 2*HI + 1 of w -> packed pair. Exact: every E4M3
   // value is an fp16 value.
   template <bool HI>
@@ -89,6 +94,22 @@ template <class T>
 __device__ __forceinline__ u32x4 e4m3x8(u32x2 w) {
   return u32x4{T::template from_e4m3x2<false>(w[0]), T::template from_e4m3x2<true>(w[0]),
                T::template from_e4m3x2<false>(w[1]), T::template from_e4m3x2<true>(w[1])};
+}
+
+// Rotary embedding of 8 column pairs (i, i + D/2) of one row, in place: x1
+// holds columns i .. i+7, x2 columns i + D/2 .. i + D/2 + 7, c / s the
+// cosines and sines of those 8 frequencies at the row's position (fp32, from
+// the caller's table). Computed in fp32, rounded once to the 16-bit type:
+//   x1' = x1 c - x2 s,   x2' = x2 c + x1 s.
+template <class T>
+__device__ __forceinline__ void rope8(u32x4& x1, u32x4& x2, const float* c, const float* s) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float a0 = T::lo(x1[w]), a1 = T::hi(x1[w]), b0 = T::lo(x2[w]), b1 = T::hi(x2[w]);
+    const float c0 = c[2 * w], c1 = c[2 * w + 1], s0 = s[2 * w], s1 = s[2 * w + 1];
+    x1[w] = T::pack2(a0 * c0 - b0 * s0, a1 * c1 - b1 * s1);
+    x2[w] = T::pack2(b0 * c0 + a0 * s0, b1 * c1 + a1 * s1);
+  }
 }
 
 // Max / sum of a value with the same lane in the other half of the wavefront

@@ -368,16 +368,26 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   // loaded first: the memory counter is in order, so the first step then waits
   // only for q and its own step
   u32x4 qf[KS];
+  const bool q_live = c < G && a.qmode != 2;
   {
-    const bool live = c < G && a.qmode != 2;
-    const uint32_t flip = a.qmode == 1 ? 0x80008000u : 0u;
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + kvh * G + (live ? c : 0)) * D;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + kvh * G + (q_live ? c : 0)) * D;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      u32x4 x = *reinterpret_cast<const u32x4*>(qp + 32 * s + 8 * g);
-      x ^= flip;
-      qf[s] = live ? x : u32x4{0, 0, 0, 0};
-    }
+    for (int s = 0; s < KS; ++s) qf[s] = *reinterpret_cast<const u32x4*>(qp + 32 * s + 8 * g);
+  }
+  // rotary embedding (optional) at the query's position ctx - 1: fragment
+  // s < KS/2 holds columns 32s + 8g .. +8 of the first half, s + KS/2 their
+  // partners; the table values are loaded here and applied once the K/V loads
+  // are under way
+  f32x4 rcs[KS / 2][2], rsn[KS / 2][2];
+  if (a.rope) {
+    const float* tr = a.rope + (size_t)min(ctx - 1, a.max_pos - 1) * D + 8 * g;
+#pragma unroll
+    for (int s = 0; s < KS / 2; ++s)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        rcs[s][u] = *reinterpret_cast<const f32x4*>(tr + 32 * s + 4 * u);
+        rsn[s][u] = *reinterpret_cast<const f32x4*>(tr + D / 2 + 32 * s + 4 * u);
+      }
   }
 
   // Step q's physical blocks: a block past the split's last one carries the
@@ -408,6 +418,22 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     step_blocks(1, ph);
     load_step<D, KV8>(buf1, kbase, vbase, block_stride, ph, o);
     __builtin_amdgcn_sched_barrier(0);
+  }
+
+  if (a.rope) {
+#pragma unroll
+    for (int s = 0; s < KS / 2; ++s) {
+      const float cs[8] = {rcs[s][0][0], rcs[s][0][1], rcs[s][0][2], rcs[s][0][3],
+                           rcs[s][1][0], rcs[s][1][1], rcs[s][1][2], rcs[s][1][3]};
+      const float sn[8] = {rsn[s][0][0], rsn[s][0][1], rsn[s][0][2], rsn[s][0][3],
+                           rsn[s][1][0], rsn[s][1][1], rsn[s][1][2], rsn[s][1][3]};
+      rope8<T>(qf[s], qf[s + KS / 2], cs, sn);
+    }
+  }
+  {
+    const uint32_t flip = a.qmode == 1 ? 0x80008000u : 0u;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = q_live ? (qf[s] ^ flip) : u32x4{0, 0, 0, 0};
   }
 
   WaveState<D> st;

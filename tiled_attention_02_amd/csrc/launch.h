@@ -27,6 +27,10 @@ struct PrefillArgs {
   const int* ctx_lens;  // [B] keys per sequence
   const int* q_lens;    // [B] query rows per sequence, or null (all Tq)
   int max_blocks, num_blocks;
+  // rotary embedding of the query rows (paged form), or null: table [max_pos][D]
+  // fp32, cosines in columns 0 .. D/2-1, sines in D/2 .. D-1
+  const float* rope;
+  int max_pos;
 };
 
 struct AppendArgs {
@@ -40,6 +44,9 @@ struct AppendArgs {
   int B, Hkv, Tnew, D, max_blocks, num_blocks;
   // fp8 form: the caches hold E4M3 codes of x / scale
   float k_scale, v_scale;
+  // rope form: K rows rotated at their positions (table as in PrefillArgs)
+  const float* rope;
+  int max_pos;
 };
 
 constexpr int kMaxPagedPrefillBlocks = 2048;  // block-table entries a chunked prefill keeps in LDS
@@ -60,6 +67,9 @@ struct DecodeArgs {
   int qmode;
   // E4M3 caches (fp8 form): an entry means code value * scale
   float k_scale, v_scale;
+  // rotary embedding of the query at position ctx - 1, or null (table as in PrefillArgs)
+  const float* rope;
+  int max_pos;
 };
 
 constexpr int kDecodeBlock = 16;        // tokens per cache block
@@ -69,6 +79,7 @@ hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int D, bool causal, h
 hipError_t launch_prefill_paged(const PrefillArgs& a, bool bf16, int D, bool causal, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_append_fp8(const AppendArgs& a, bool bf16, hipStream_t stream);
+hipError_t launch_append_rope(const AppendArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_decode_fp8(const DecodeArgs& a, bool bf16, hipStream_t stream);
 

@@ -13,6 +13,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "attn_device.h"
 #include "launch.h"
 
 namespace attn {
@@ -143,7 +144,93 @@ static hipError_t launch_mode(const AppendArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Rotary form: K rows are rotated at their positions (start + i) on the way
+// into the cache, V rows copied. A thread owns the column pairs (i, i + D/2)
+// of one 8-column chunk i = 8c of RPT rows: K chunks c and c + C8/2, the
+// table's cosines and sines of those 8 frequencies, and the same two V chunks.
+template <int D, bool HAS_LENS, class T>
+__global__ __launch_bounds__(256) void append_rope_kernel(AppendArgs a) {
+  constexpr int C8 = D / 8;        // 16-byte chunks per row
+  constexpr int CPR = C8 / 2;      // threads per row
+  constexpr int RPT = kAppendRowsPerThread;
+  constexpr int STRIDE = 256 / CPR;
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int c = threadIdx.x % CPR;
+  const int t0 = blockIdx.x * (STRIDE * RPT) + threadIdx.x / CPR;
+  const int start = a.start[b];
+  const int n = HAS_LENS ? min(a.new_lens[b], a.Tnew) : a.Tnew;
+  asm volatile("" ::"s"(start), "s"(n));  // both scalars in one round trip
+  if (t0 >= n) return;
+  const size_t row0 = (size_t)(b * a.Hkv + kvh) * a.Tnew;
+  const int* trow = a.table + (size_t)b * a.max_blocks;
+  u32x4_t kx[RPT][2], vx[RPT][2];
+  f32x4 cs[RPT][2], sn[RPT][2];
+  int phys[RPT];
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) {
+    const int t = min(t0 + j * STRIDE, n - 1);  // rows past the chunk: in bounds, dropped below
+    const size_t src = (row0 + t) * D + 8 * c;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      kx[j][h] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.k_new) + src + h * (D / 2)));
+      vx[j][h] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.v_new) + src + h * (D / 2)));
+    }
+    const float* tr = a.rope + (size_t)min(max(start + t, 0), a.max_pos - 1) * D + 8 * c;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      cs[j][u] = *reinterpret_cast<const f32x4*>(tr + 4 * u);
+      sn[j][u] = *reinterpret_cast<const f32x4*>(tr + D / 2 + 4 * u);
+    }
+    phys[j] = trow[min(max((start + t) / kDecodeBlock, 0), a.max_blocks - 1)];
+  }
+#pragma unroll
+  for (int j = 0; j < RPT; ++j)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) asm volatile("" ::"v"(kx[j][h]), "v"(vx[j][h]));
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) {
+    const int t = t0 + j * STRIDE;
+    const int pos = start + t;
+    if (t >= n || pos < 0 || pos / kDecodeBlock >= a.max_blocks || phys[j] < 0 || phys[j] >= a.num_blocks) continue;
+    const float c8[8] = {cs[j][0][0], cs[j][0][1], cs[j][0][2], cs[j][0][3], cs[j][1][0], cs[j][1][1], cs[j][1][2],
+                         cs[j][1][3]};
+    const float s8[8] = {sn[j][0][0], sn[j][0][1], sn[j][0][2], sn[j][0][3], sn[j][1][0], sn[j][1][1], sn[j][1][2],
+                         sn[j][1][3]};
+    u32x4 k1 = kx[j][0], k2 = kx[j][1];
+    rope8<T>(k1, k2, c8, s8);
+    const size_t dst = (((size_t)phys[j] * a.Hkv + kvh) * kDecodeBlock + pos % kDecodeBlock) * D + 8 * c;
+    uint16_t* kc = static_cast<uint16_t*>(a.kc) + dst;
+    uint16_t* vc = static_cast<uint16_t*>(a.vc) + dst;
+    *reinterpret_cast<u32x4*>(kc) = k1;
+    *reinterpret_cast<u32x4*>(kc + D / 2) = k2;
+    *reinterpret_cast<u32x4_t*>(vc) = vx[j][0];
+    *reinterpret_cast<u32x4_t*>(vc + D / 2) = vx[j][1];
+  }
+}
+
+template <int D, class T>
+static void launch_rope_d(const AppendArgs& a, dim3 grid, hipStream_t stream) {
+  if (a.new_lens)
+    hipLaunchKernelGGL((append_rope_kernel<D, true, T>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((append_rope_kernel<D, false, T>), grid, dim3(256), 0, stream, a);
+}
+
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream) { return launch_mode<0>(a, stream); }
+
+hipError_t launch_append_rope(const AppendArgs& a, bool bf16, hipStream_t stream) {
+  const long long rows_per_wg = (256 / (a.D / 16)) * kAppendRowsPerThread;
+  const long long gx = (a.Tnew + rows_per_wg - 1) / rows_per_wg;
+  if (gx > 0x7fffffffLL || a.Hkv > 65535 || a.B > 65535) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)gx, (unsigned)a.Hkv, (unsigned)a.B);
+  if (a.D == 128)
+    bf16 ? launch_rope_d<128, BF16>(a, grid, stream) : launch_rope_d<128, F16>(a, grid, stream);
+  else
+    bf16 ? launch_rope_d<64, BF16>(a, grid, stream) : launch_rope_d<64, F16>(a, grid, stream);
+  return hipGetLastError();
+}
 
 hipError_t launch_append_fp8(const AppendArgs& a, bool bf16, hipStream_t stream) {
   return bf16 ? launch_mode<1>(a, stream) : launch_mode<2>(a, stream);

@@ -142,17 +142,34 @@ struct Acc {
   float m, l, lr;      // running max (log2 units), fp32 sum, sum of the rounded p
 };
 
-template <int D>
-__device__ __forceinline__ void load_q(Acc<D>& st, const Geo& g, int qmode, int qrow, int h) {
+template <class T, int D>
+__device__ __forceinline__ void load_q(Acc<D>& st, const Geo& g, int qmode, int qrow, int h, const float* rope,
+                                       int max_pos) {
   const bool live = qrow < g.Lq;
   const uint32_t flip = qmode == 1 ? 0x80008000u : 0u;
   const bool zero = qmode == 2 || !live;
   const u32x4* src = reinterpret_cast<const u32x4*>(g.Qg + (size_t)(live ? qrow : 0) * D + 8 * h);
+  u32x4 x[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) x[s] = src[2 * s];
+  if (rope) {
+    // rotary embedding at the row's position (Lk - Lq + row): fragment s < D/32
+    // holds columns 16s + 8h .. +8 of the first half, fragment s + D/32 their partners
+    const float* tr = rope + (size_t)min(max(g.off + qrow, 0), max_pos - 1) * D + 8 * h;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+      float c[8], sn[8];
+      *reinterpret_cast<f32x4*>(c) = *reinterpret_cast<const f32x4*>(tr + 16 * s);
+      *reinterpret_cast<f32x4*>(c + 4) = *reinterpret_cast<const f32x4*>(tr + 16 * s + 4);
+      *reinterpret_cast<f32x4*>(sn) = *reinterpret_cast<const f32x4*>(tr + D / 2 + 16 * s);
+      *reinterpret_cast<f32x4*>(sn + 4) = *reinterpret_cast<const f32x4*>(tr + D / 2 + 16 * s + 4);
+      rope8<T>(x[s], x[s + D / 32], c, sn);
+    }
+  }
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
-    u32x4 x = src[2 * s];
-    x ^= flip;
-    st.qf[s] = zero ? u32x4{0, 0, 0, 0} : x;
+    x[s] ^= flip;
+    st.qf[s] = zero ? u32x4{0, 0, 0, 0} : x[s];
   }
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) st.oacc[i] = f32x16{};
@@ -566,7 +583,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   const int w_lo = g.q_lo + w * 32;
   const int qrow = w_lo + (lane & 31);
   Acc<D> st;
-  load_q(st, g, a.qmode, qrow, h);
+  load_q<T, D>(st, g, a.qmode, qrow, h, PAGED ? a.rope : nullptr, a.max_pos);
   Offs<D, BK> o;
   make_offs(o, lane);
   Stager<D, BK, THREADS, PAGED> ks, vs;
