@@ -10,7 +10,8 @@ One step = one pass of the whole hot path on seeded synthetic inputs:
   * a chunked prefill through the paged cache: 1024-token chunks of 4
     sequences with cached prefixes ~ U[2048, 8192], Llama3-8B heads
     (attn_cache_append of the chunk's K/V into each of 8 layers' caches,
-    then attn_fwd_paged on one of them).
+    then attn_fwd_paged on one of them), once plain and once with the rotary
+    embedding fused in (rotating append, rotated queries).
 Each call is timed with HIP events on the stream it runs on. Before each call
 (outside its events) a read pass over a 1 GiB buffer evicts the inputs from
 the 256 MB Infinity Cache and the L2s, so the timed call reads its inputs from
@@ -47,6 +48,7 @@ KERNEL_SOURCES = {
     "chunked_prefill": ["tiled_attention_02_amd/csrc/prefill_fwd.hip", "tiled_attention_02_amd/csrc/attn_device.h"],
     "append": ["tiled_attention_02_amd/csrc/paged_cache.hip"],
     "decode_fp8": ["tiled_attention_02_amd/csrc/decode_paged.hip", "tiled_attention_02_amd/csrc/attn_device.h"],
+    "append_rope": ["tiled_attention_02_amd/csrc/paged_cache.hip", "tiled_attention_02_amd/csrc/attn_device.h"],
 }
 APPEND_LAYERS = 8
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
@@ -155,14 +157,19 @@ def cpu_baseline_decode_fp8(x, case, ks, vs, nseq=64, min_seconds=5.0):
                       f"sequences), repeated {reps} times; {dt:.1f} s wall"}
 
 
-def cpu_baseline_chunked(x, case, nseq=1):
+def cpu_baseline_chunked(x, case, nseq=1, rope=None):
     """Time the float64 oracle on the first sequence(s) of the chunked-prefill batch (all heads, all rows)."""
     import workloads as W
     from oracle import oracle as O
+    from oracle import rope as R
     sl = slice(0, nseq)
     t0 = time.perf_counter()
-    O.prefill_paged(x["q"][sl], x["k_cache"], x["v_cache"], x["block_table"][sl], x["ctx_lens"][sl],
-                    x["new_lens"][sl], case.scale, True)
+    if rope is None:
+        O.prefill_paged(x["q"][sl], x["k_cache"], x["v_cache"], x["block_table"][sl], x["ctx_lens"][sl],
+                        x["new_lens"][sl], case.scale, True)
+    else:
+        R.prefill_paged_rope(x["q"][sl], x["k_cache"], x["v_cache"], x["block_table"][sl], x["ctx_lens"][sl],
+                             x["new_lens"][sl], rope, case.scale, case.dtype, True)
     dt = time.perf_counter() - t0
     flops = W.chunk_flops(x["ctx_lens"][sl], x["new_lens"][sl], case.Hq, case.D, True)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _oracle_threads(), "kind": "oracle",
@@ -309,15 +316,45 @@ def main():
     app_sets = [(ckn, cvn, ckc, cvc)] + [tuple(t.clone() for t in (ckn, cvn, ckc, cvc))
                                          for _ in range(APPEND_LAYERS - 1)]
 
+    # the rotary leg: the same chunk with RoPE fused into the append and the
+    # query load (its own caches, so each leg keeps its own cache contents)
+    rope_tab = torch.from_numpy(W.rope_table(16384, cc.D)).to(dev)
+    rope_sets = [tuple(t.clone() for t in (ckn, cvn, ckc, cvc)) for _ in range(APPEND_LAYERS)]
+
     pflops = W.prefill_flops(pc.B, pc.Hq, pc.T, pc.T, pc.D, True)
     dbytes = W.decode_bytes(xd["ctx_lens"], dc.Hq, dc.Hkv, dc.D)
     d8bytes = W.decode_bytes(xd8["ctx_lens"], dc.Hq, dc.Hkv, dc.D, kv_elem=1)
     cflops = W.chunk_flops(xc["ctx_lens"], xc["new_lens"], cc.Hq, cc.D, True)
     abytes = W.append_bytes(xc["new_lens"], cc.Hkv, cc.D)
-    run_p = args.only in (None, "prefill")
-    run_d = args.only in (None, "decode")
-    run_c = args.only in (None, "chunked")
-    run_d8 = args.only in (None, "decode_fp8")
+    # The step's timed parts, in order: (name, call, calls per event pair).
+    # Each part starts after the eviction pass and sits between two events on
+    # the stream it runs on.
+    parts = []
+    if args.only in (None, "prefill"):
+        parts.append(("prefill", lambda: ta.attn_fwd(q, k, v, scale=pc.scale, causal=True, out=o, lse=lse), 1))
+    if args.only in (None, "decode"):
+        parts.append(("decode", lambda: ta.attn_decode_paged(dq, kc, vc, bt, cl, scale=dc.scale, out=do, lse=dlse,
+                                                             workspace=ws), 1))
+    if args.only in (None, "decode_fp8"):
+        parts.append(("decode_fp8", lambda: ta.attn_decode_paged_fp8(dq, kc8, vc8, KS8, VS8, bt, cl, scale=dc.scale,
+                                                                     out=do8, lse=dlse8, workspace=ws), 1))
+    for rope, tag in ((None, ""), (rope_tab, "_rope")):
+        if args.only not in (None, "chunked"):
+            break
+        sets = app_sets if rope is None else rope_sets
+
+        def appends(sets=sets, rope=rope):
+            # the chunk's K/V go into every layer's cache
+            for kn_, vn_, kc_, vc_ in sets:
+                ta.attn_cache_append(kn_, vn_, kc_, vc_, cbt, cst, cnl, rope=rope)
+
+        def chunk_prefill(sets=sets, rope=rope):
+            # then the chunk attends to prefix + itself (first layer's cache)
+            ta.attn_fwd_paged(cq, sets[0][2], sets[0][3], cbt, ccl, cnl, scale=cc.scale, causal=True, out=co,
+                              lse=clse, rope=rope)
+
+        parts.append(("append" + tag, appends, APPEND_LAYERS))
+        parts.append(("chunked_prefill" + tag, chunk_prefill, 1))
 
     def evict():
         # read-only pass over 1 GiB: pushes the inputs out of every cache level
@@ -326,35 +363,13 @@ def main():
             torch.sum(flush_rows, dim=1, out=flush_dst)
 
     def step(evs):
-        if run_p:
+        for i, (_, call, _) in enumerate(parts):
             evict()
-            evs[0].record()
-            ta.attn_fwd(q, k, v, scale=pc.scale, causal=True, out=o, lse=lse)
-            evs[1].record()
-        if run_d:
-            evict()
-            evs[2].record()
-            ta.attn_decode_paged(dq, kc, vc, bt, cl, scale=dc.scale, out=do, lse=dlse, workspace=ws)
-            evs[3].record()
-        if run_d8:
-            evict()
-            evs[8].record()
-            ta.attn_decode_paged_fp8(dq, kc8, vc8, KS8, VS8, bt, cl, scale=dc.scale, out=do8, lse=dlse8, workspace=ws)
-            evs[9].record()
-        if run_c:
-            # the chunk's K/V go into the cache (every layer), then the chunk
-            # attends to prefix + itself (first layer's cache)
-            evict()
-            evs[4].record()
-            for kn_, vn_, kc_, vc_ in app_sets:
-                ta.attn_cache_append(kn_, vn_, kc_, vc_, cbt, cst, cnl)
-            evs[5].record()
-            evict()
-            evs[6].record()
-            ta.attn_fwd_paged(cq, ckc, cvc, cbt, ccl, cnl, scale=cc.scale, causal=True, out=co, lse=clse)
-            evs[7].record()
+            evs[2 * i].record()
+            call()
+            evs[2 * i + 1].record()
 
-    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(10)]  # noqa: E731
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(parts))]  # noqa: E731
     for i in range(args.warmup):
         step(mk())
     torch.cuda.synchronize()
@@ -366,28 +381,27 @@ def main():
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    p_ms = [e[0].elapsed_time(e[1]) for e in evs] if run_p else [float("nan")]
-    d_ms = [e[2].elapsed_time(e[3]) for e in evs] if run_d else [float("nan")]
-    a_ms = [e[4].elapsed_time(e[5]) / APPEND_LAYERS for e in evs] if run_c else [float("nan")]
-    c_ms = [e[6].elapsed_time(e[7]) for e in evs] if run_c else [float("nan")]
-    d8_ms = [e[8].elapsed_time(e[9]) for e in evs] if run_d8 else [float("nan")]
-    p_avg, d_avg = float(np.mean(p_ms)), float(np.mean(d_ms))
-    a_avg, c_avg = float(np.mean(a_ms)), float(np.mean(c_ms))
-    d8_avg = float(np.mean(d8_ms))
-    log(f"[bench] prefill {p_avg:.3f} ms (min {min(p_ms):.3f}); decode {d_avg * 1e3:.1f} us "
-        f"(min {min(d_ms) * 1e3:.1f}); fp8 decode {d8_avg * 1e3:.1f} us; append {a_avg * 1e3:.1f} us; chunked prefill {c_avg * 1e3:.1f} us; "
-        f"wall/step {wall / args.steps * 1e3:.2f} ms")
+    # per-call mean (ms) of every part; a burst counts as n calls
+    ms = {name: float(np.mean([e[2 * i].elapsed_time(e[2 * i + 1]) / n for e in evs]))
+          for i, (name, _, n) in enumerate(parts)}
+    ms_min = {name: float(np.min([e[2 * i].elapsed_time(e[2 * i + 1]) / n for e in evs]))
+              for i, (name, _, n) in enumerate(parts)}
+    log("[bench] " + "; ".join(f"{k} {v * 1e3:.1f} us (min {ms_min[k] * 1e3:.1f})" for k, v in ms.items()) +
+        f"; wall/step {wall / args.steps * 1e3:.2f} ms")
     if args.only:
-        print(json.dumps({"only": args.only, "prefill_ms": p_avg, "decode_ms": d_avg, "decode_fp8_ms": d8_avg,
-                          "append_ms": a_avg,
-                          "chunked_prefill_ms": c_avg}))
+        print(json.dumps({"only": args.only, "ms_per_call": ms}))
         return
+    p_avg, d_avg, d8_avg = ms["prefill"], ms["decode"], ms["decode_fp8"]
+    a_avg, c_avg = ms["append"], ms["chunked_prefill"]
+    ar_avg, cr_avg = ms["append_rope"], ms["chunked_prefill_rope"]
 
     p_tfs = pflops / (p_avg * 1e-3) / 1e12
     d_gbs = dbytes / (d_avg * 1e-3) / 1e9
     c_tfs = cflops / (c_avg * 1e-3) / 1e12
     a_gbs = abytes / (a_avg * 1e-3) / 1e9
     d8_gbs = d8bytes / (d8_avg * 1e-3) / 1e9
+    cr_tfs = cflops / (cr_avg * 1e-3) / 1e12
+    ar_gbs = abytes / (ar_avg * 1e-3) / 1e9
     out = {
         "metric": METRIC,
         "value": round(p_tfs, 2),
@@ -395,7 +409,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(p_avg + d_avg + d8_avg + APPEND_LAYERS * a_avg + c_avg, 4),
+        "ms_per_step": round(sum(ms[name] * n for name, _, n in parts), 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -405,7 +419,7 @@ def main():
                                "B=64 Hq=12 Hkv=2 D=128 ctx~U[512,4096] block=16 (decode; again over an E4M3 cache: decode_fp8) + "
                                "chunked bf16 prefill "
                                "B=4 Hq=32 Hkv=8 D=128 prefix~U[2048,8192] chunk=1024 through the block table "
-                               "(chunked)",
+                               "(chunked; again with RoPE fused: chunked_rope)",
                    "prefill_gflop_per_call": round(pflops / 1e9, 3),
                    "decode_mb_per_call": round(dbytes / 1e6, 3),
                    "cache_eviction_before_each_call": "none" if args.no_flush else "1 GiB read pass",
@@ -439,6 +453,21 @@ def main():
                        "roofline": {"bound": "hbm", "achieved": round(a_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                     "frac": round(a_gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic("append"),
                                     "kernel": "append_kernel", "algorithmic_bytes_per_launch": abytes}}},
+        "chunked_rope": {
+            "workload": cc.name + ", rotary embedding fused (K rotated in the append, Q in the prefill's Q load)",
+            "prefill": {"value": round(cr_tfs, 2), "unit": "TFLOP/s", "us_per_call": round(cr_avg * 1e3, 2),
+                        "roofline": {"bound": "mfma", "achieved": round(cr_tfs, 2), "peak": PEAK_BF16_TFLOPS,
+                                     "unit": "TFLOP/s", "frac": round(cr_tfs / PEAK_BF16_TFLOPS, 4),
+                                     "traffic": measured_traffic("chunked_prefill"),
+                                     "kernel": "prefill_kernel (paged form, rotated queries)",
+                                     "algorithmic_flops_per_launch": cflops}},
+            "append": {"value": round(ar_gbs, 1), "unit": "GB/s", "us_per_call": round(ar_avg * 1e3, 2),
+                       "timing": f"a burst of {APPEND_LAYERS} appends, as for chunked.append",
+                       "roofline": {"bound": "hbm", "achieved": round(ar_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                    "frac": round(ar_gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic("append_rope"),
+                                    "kernel": "append_rope_kernel", "algorithmic_bytes_per_launch": abytes,
+                                    "note": "bytes: the chunk's K and V read and written once; the table rows "
+                                            "read are not counted"}}},
     }
     out["context"] = context_measurements(ta, W, torch, np, dev, flush_rows, flush_dst, evict)
     if not args.no_cpu_baseline:
@@ -450,6 +479,8 @@ def main():
         out["decode_fp8"]["cpu_baseline"] = cpu_baseline_decode_fp8(xd8, dc, KS8, VS8)
         log("[bench] cpu baseline: float64 oracle on a sample of the chunked-prefill workload")
         out["chunked"]["cpu_baseline"] = cpu_baseline_chunked(xc, cc)
+        log("[bench] cpu baseline: float64 oracle on a sample of the rotary chunked-prefill workload")
+        out["chunked_rope"]["cpu_baseline"] = cpu_baseline_chunked(xc, cc, rope=W.rope_table(16384, cc.D))
     print(json.dumps(out), flush=True)
 
 
