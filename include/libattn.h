@@ -212,6 +212,20 @@ attn_status attn_decode_paged_fp8(const void* q, const void* k_cache, const void
                                   size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * attn_fwd_paged_fp8: the chunked prefill of attn_fwd_paged over uint8 E4M3
+ * caches with scales k_scale, v_scale (as for attn_decode_paged_fp8): the
+ * result is the chunked prefill of the dequantized cache. q, o stay bf16 or
+ * fp16 (`dtype`). `rope` (may be NULL) and max_pos: as for
+ * attn_fwd_paged_rope below (query rows rotated at their positions).
+ */
+attn_status attn_fwd_paged_fp8(const void* q, const void* k_cache, const void* v_cache,
+                               float k_scale, float v_scale, const float* rope, int max_pos,
+                               const int* block_table, const int* ctx_lens, const int* q_lens,
+                               void* o, float* lse, int B, int Hq, int Hkv, int Tq, int D,
+                               int block_size, int max_blocks_per_seq, int num_blocks, float scale,
+                               int causal, attn_dtype dtype, hipStream_t stream);
+
+/*
  * Rotary position embedding fused into the paged path. The Llama3-8B trace of
  * the comemg.com page (section "模型推理") shows RoPE among the small kernels
  * between the products and attention; fusing such a step into its neighbour

@@ -177,3 +177,91 @@ def test_fp8_rejects_bad_scales(ta):
     for ks, vs in ((0.0, 1.0), (1.0, -1.0), (float("nan"), 1.0), (1.0, float("inf"))):
         with pytest.raises(ta.AttnError, match="k_scale and v_scale"):
             ta.attn_decode_paged_fp8(q, kc, kc, ks, vs, bt, cl)
+
+
+# ---------------------------------------------------------------- chunked prefill over an E4M3 cache
+def _fp8_chunk_inputs(case, seed):
+    """chunk_inputs' q, table and lengths over E4M3 caches whose slots at or past each sequence's context
+    (and the spare blocks) hold the NaN code; every position < ctx holds a finite code."""
+    x = W.chunk_inputs(case)
+    rng = np.random.default_rng(seed)
+    shape = x["k_cache"].shape
+    k8 = W.e4m3_codes(rng, shape)
+    v8 = W.e4m3_codes(rng, shape)
+    used = np.zeros(shape[0] * 16, dtype=bool)
+    for b in range(case.B):
+        pos = np.arange(int(x["ctx_lens"][b]))
+        used[x["block_table"][b, pos // 16] * 16 + pos % 16] = True
+    unused = ~used.reshape(shape[0], 16)
+    for a in (k8, v8):
+        a.transpose(0, 2, 1, 3)[unused] = W.E4M3_NAN
+    return x, k8, v8
+
+
+@pytest.mark.parametrize("D,dtype", [(128, "bf16"), (64, "fp16"), (128, "fp16"), (64, "bf16")])
+@pytest.mark.parametrize("causal", [True, False])
+def test_fp8_chunked_prefill(ta, D, dtype, causal):
+    import torch
+    case = W.ChunkCase("fp8 chunk", B=3, Hq=8, Hkv=2, D=D, dtype=dtype, ctx_lo=0, ctx_hi=900, chunk_lo=1,
+                       chunk_hi=300, seed=94)
+    x, k8, v8 = _fp8_chunk_inputs(case, 95)
+    ks, vs = 0.0625, 0.11
+    what = f"fp8 chunked prefill D={D} {dtype} causal={causal}"
+    _note(f"[case] {what} ctx={x['ctx_lens'].tolist()} n={x['new_lens'].tolist()}")
+    o, lse = ta.attn_fwd_paged_fp8(_dev(x["q"], dtype), _u8(k8), _u8(v8), ks, vs, _i32(x["block_table"]),
+                                   _i32(x["ctx_lens"]), _i32(x["new_lens"]), scale=case.scale, causal=causal)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = F8.prefill_paged_fp8(x["q"], k8, v8, ks, vs, x["block_table"], x["ctx_lens"], x["new_lens"],
+                                          case.scale, causal)
+    _compare(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, dtype, what=what)
+
+
+def test_fp8_append_then_chunked_prefill_with_rope(ta):
+    """The FP8 serving path for a prompt chunk: the chunk's K/V quantized into the cache, then the chunk's
+    attention over the E4M3 cache with rotated queries."""
+    import torch
+    from oracle import rope as R
+    case = W.ChunkCase("fp8 chunk+rope", B=3, Hq=12, Hkv=2, D=128, dtype="bf16", ctx_lo=0, ctx_hi=1200, chunk_lo=1,
+                       chunk_hi=260, seed=96)
+    x = W.chunk_inputs(case, nan_fill=True)
+    rng = np.random.default_rng(97)
+    k8 = W.e4m3_codes(rng, x["k_cache"].shape)
+    v8 = W.e4m3_codes(rng, x["v_cache"].shape)
+    ks, vs = 0.02, 0.03
+    tab = W.rope_table(2048, case.D)
+    kc, vc = _u8(k8), _u8(v8)
+    ta.attn_cache_append_fp8(_dev(x["k_new"], "bf16"), _dev(x["v_new"], "bf16"), kc, vc, ks, vs,
+                             _i32(x["block_table"]), _i32(x["start_pos"]), _i32(x["new_lens"]))
+    o, lse = ta.attn_fwd_paged_fp8(_dev(x["q"], "bf16"), kc, vc, ks, vs, _i32(x["block_table"]), _i32(x["ctx_lens"]),
+                                   _i32(x["new_lens"]), scale=case.scale, causal=True,
+                                   rope=torch.from_numpy(tab).cuda())
+    torch.cuda.synchronize()
+    kref, vref = F8.cache_append_fp8(x["k_new"], x["v_new"], k8, v8, x["block_table"], x["start_pos"], ks, vs,
+                                     x["new_lens"])
+    assert np.array_equal(kc.cpu().numpy(), kref) and np.array_equal(vc.cpu().numpy(), vref)
+    o_ref, lse_ref = R.prefill_paged_rope(x["q"], F8.dequantize(kref, ks), F8.dequantize(vref, vs),
+                                          x["block_table"], x["ctx_lens"], x["new_lens"], tab, case.scale, "bf16")
+    _compare(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, "bf16", what="fp8 append + chunk + rope")
+
+
+def test_fp8_chunked_prefill_long_prefix_sampled(ta):
+    """A 20,000-token prefix over an E4M3 cache plus a 512-row chunk; oracle on sampled rows."""
+    import torch
+    case = W.ChunkCase("fp8 long", B=1, Hq=8, Hkv=2, D=128, dtype="bf16", ctx_lo=20000, ctx_hi=20000, chunk_lo=512,
+                       chunk_hi=512, seed=98)
+    x, k8, v8 = _fp8_chunk_inputs(case, 99)
+    ks, vs = 0.125, 0.25
+    o, lse = ta.attn_fwd_paged_fp8(_dev(x["q"], "bf16"), _u8(k8), _u8(v8), ks, vs, _i32(x["block_table"]),
+                                   _i32(x["ctx_lens"]), _i32(x["new_lens"]), scale=case.scale, causal=True)
+    torch.cuda.synchronize()
+    o, lse = o.float().cpu().numpy(), lse.cpu().numpy()
+    from oracle import oracle as O
+    L = int(x["ctx_lens"][0])
+    kd, vd = F8.dequantize(k8, ks), F8.dequantize(v8, vs)
+    K = np.stack([O.gather_paged(kd, vd, x["block_table"], L, 0, h)[0] for h in range(case.Hkv)])[None]
+    V = np.stack([O.gather_paged(kd, vd, x["block_table"], L, 0, h)[1] for h in range(case.Hkv)])[None]
+    rows = np.array([0, 1, 63, 64, 127, 128, 255, 256, 300, 511])
+    picks = np.array([(0, hq, i) for hq in range(case.Hq) for i in rows])
+    o_ref, lse_ref = O.prefill_rows(x["q"], K, V, case.scale, True, None, picks)
+    _compare(o[0][picks[:, 1], picks[:, 2]], lse[0][picks[:, 1], picks[:, 2]], o_ref, lse_ref, "bf16",
+             what="fp8 long prefix sampled")

@@ -13,15 +13,15 @@ import math
 import os
 
 __all__ = ["attn_fwd", "attn_decode_paged", "attn_fwd_paged", "attn_cache_append", "attn_cache_append_fp8",
-           "attn_decode_paged_fp8", "attn_cache_append_rope", "attn_fwd_paged_rope", "attn_decode_paged_rope",
-           "attn_decode_workspace_bytes",
+           "attn_decode_paged_fp8", "attn_fwd_paged_fp8", "attn_cache_append_rope", "attn_fwd_paged_rope",
+           "attn_decode_paged_rope", "attn_decode_workspace_bytes",
            "attn_status_str", "attn_last_error", "AttnError", "lib", "LIB_PATH", "EXPORTS", "BLOCK_SIZE",
            "decode_workspace"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
 EXPORTS = ("attn_fwd", "attn_decode_paged", "attn_fwd_paged", "attn_cache_append", "attn_cache_append_fp8",
-           "attn_decode_paged_fp8", "attn_cache_append_rope", "attn_fwd_paged_rope", "attn_decode_paged_rope",
-           "attn_decode_workspace_bytes", "attn_status_str", "attn_last_error")
+           "attn_decode_paged_fp8", "attn_fwd_paged_fp8", "attn_cache_append_rope", "attn_fwd_paged_rope",
+           "attn_decode_paged_rope", "attn_decode_workspace_bytes", "attn_status_str", "attn_last_error")
 BLOCK_SIZE = 16
 
 ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
@@ -58,6 +58,9 @@ def lib() -> ctypes.CDLL:
     L.attn_cache_append_fp8.restype = i
     L.attn_decode_paged_fp8.argtypes = [vp, vp, vp, f, f, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, sz, vp]
     L.attn_decode_paged_fp8.restype = i
+    L.attn_fwd_paged_fp8.argtypes = [vp, vp, vp, f, f, vp, i, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, i,
+                                     vp]
+    L.attn_fwd_paged_fp8.restype = i
     L.attn_cache_append_rope.argtypes = [vp, vp, vp, vp, vp, i, vp, vp, vp, i, i, i, i, i, i, i, i, vp]
     L.attn_cache_append_rope.restype = i
     L.attn_fwd_paged_rope.argtypes = [vp, vp, vp, vp, i, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, i, vp]
@@ -249,12 +252,26 @@ def _check_i32(t, n, name, optional=False):
 def attn_fwd_paged(q, k_cache, v_cache, block_table, ctx_lens, q_lens=None, scale: float | None = None,
                    causal: bool = True, out=None, lse=None, need_lse: bool = True, rope=None):
     """Chunked prefill through the paged cache. q [B,Hq,Tq,D]: row i of sequence b is position
-    ctx_lens[b] - q_lens[b] + i (q_lens None: all Tq rows). Returns (o like q, lse [B,Hq,Tq] or None)."""
+    ctx_lens[b] - q_lens[b] + i (q_lens None: all Tq rows). rope: optional float32 table [max_pos, D]
+    (query rows rotated at their positions). Returns (o like q, lse [B,Hq,Tq] or None)."""
+    return _fwd_paged(q, k_cache, v_cache, None, block_table, ctx_lens, q_lens, scale, causal, out, lse, need_lse,
+                      rope)
+
+
+def attn_fwd_paged_fp8(q, k_cache, v_cache, k_scale: float, v_scale: float, block_table, ctx_lens, q_lens=None,
+                       scale: float | None = None, causal: bool = True, out=None, lse=None, need_lse: bool = True,
+                       rope=None):
+    """Chunked prefill over E4M3 caches (uint8 [num_blocks,Hkv,16,D]; an entry means value(code) * scale)."""
+    return _fwd_paged(q, k_cache, v_cache, (k_scale, v_scale), block_table, ctx_lens, q_lens, scale, causal, out,
+                      lse, need_lse, rope)
+
+
+def _fwd_paged(q, k_cache, v_cache, scales, block_table, ctx_lens, q_lens, scale, causal, out, lse, need_lse, rope):
     import torch
     dt = _dtype_code(q)
     _check(q.is_cuda and q.dim() == 4 and q.is_contiguous(), "q must be a contiguous 4-D GPU tensor")
     B, Hq, Tq, D = q.shape
-    NB, Hkv, bs = _check_paged((k_cache, v_cache), q.dtype, D)
+    NB, Hkv, bs = _check_paged((k_cache, v_cache), q.dtype if scales is None else torch.uint8, D)
     _check(block_table.dim() == 2 and block_table.shape[0] == B, "block_table must be [B, max_blocks]")
     _check_i32(block_table, block_table.numel(), "block_table")
     _check_i32(ctx_lens, B, "ctx_lens")
@@ -270,7 +287,11 @@ def attn_fwd_paged(q, k_cache, v_cache, block_table, ctx_lens, q_lens=None, scal
         _check(lse.shape == (B, Hq, Tq) and lse.dtype == torch.float32 and lse.is_contiguous(), "bad lse")
     tail = (_ptr(block_table), _ptr(ctx_lens), _ptr(q_lens), _ptr(out), _ptr(lse), B, Hq, Hkv, Tq, D, bs,
             block_table.shape[1], NB, ctypes.c_float(scale), int(bool(causal)), dt, _stream(q.device))
-    if rope is not None:
+    if scales is not None:
+        max_pos = _check_rope(rope, D) if rope is not None else 0
+        st = lib().attn_fwd_paged_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.c_float(scales[0]),
+                                      ctypes.c_float(scales[1]), _ptr(rope), max_pos, *tail)
+    elif rope is not None:
         st = lib().attn_fwd_paged_rope(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(rope), _check_rope(rope, D), *tail)
     else:
         st = lib().attn_fwd_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), *tail)

@@ -174,8 +174,8 @@ attn_status append_impl(const char* fn, bool fp8, const void* k_new, const void*
   return ok();
 }
 
-attn_status fwd_paged_impl(const char* fn, const void* q, const void* k_cache, const void* v_cache,
-                           const float* rope, int max_pos, const int* block_table, const int* ctx_lens,
+attn_status fwd_paged_impl(const char* fn, bool fp8, const void* q, const void* k_cache, const void* v_cache,
+                           float k_scale, float v_scale, const float* rope, int max_pos, const int* block_table, const int* ctx_lens,
                            const int* q_lens, void* o, float* lse, int B, int Hq, int Hkv, int Tq, int D,
                            int block_size, int max_blocks_per_seq, int num_blocks, float scale, int causal,
                            attn_dtype dtype, hipStream_t stream) {
@@ -202,6 +202,8 @@ attn_status fwd_paged_impl(const char* fn, const void* q, const void* k_cache, c
       (reinterpret_cast<uintptr_t>(ctx_lens) & 3u) || (q_lens && (reinterpret_cast<uintptr_t>(q_lens) & 3u)))
     return fail(ATTN_ERR_INVALID, "%s: lse, block_table, ctx_lens and q_lens must be 4-byte aligned", fn);
 
+  if (fp8 && !(isfinite(k_scale) && isfinite(v_scale) && k_scale > 0.f && v_scale > 0.f))
+    return fail(ATTN_ERR_INVALID, "%s: k_scale and v_scale must be finite and > 0", fn);
   if (attn_status st = check_rope(fn, rope, max_pos, D); st != ATTN_OK) return st;
 
   attn::PrefillArgs a;
@@ -226,8 +228,11 @@ attn_status fwd_paged_impl(const char* fn, const void* q, const void* k_cache, c
   a.num_blocks = num_blocks;
   a.rope = rope;
   a.max_pos = max_pos;
+  a.k_scale = fp8 ? k_scale : 1.f;
+  a.v_scale = fp8 ? v_scale : 1.f;
   scale_mode(scale, &a.c, &a.qmode);
-  hipError_t e = attn::launch_prefill_paged(a, dtype == ATTN_BF16, D, causal != 0, stream);
+  hipError_t e = fp8 ? attn::launch_prefill_paged_fp8(a, dtype == ATTN_BF16, D, causal != 0, stream)
+                     : attn::launch_prefill_paged(a, dtype == ATTN_BF16, D, causal != 0, stream);
   if (e != hipSuccess) return fail(ATTN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
 }
@@ -338,7 +343,7 @@ attn_status attn_fwd_paged(const void* q, const void* k_cache, const void* v_cac
                            const int* ctx_lens, const int* q_lens, void* o, float* lse, int B, int Hq, int Hkv,
                            int Tq, int D, int block_size, int max_blocks_per_seq, int num_blocks, float scale,
                            int causal, attn_dtype dtype, hipStream_t stream) {
-  return fwd_paged_impl("attn_fwd_paged", q, k_cache, v_cache, nullptr, 0, block_table, ctx_lens, q_lens, o, lse, B,
+  return fwd_paged_impl("attn_fwd_paged", false, q, k_cache, v_cache, 1.f, 1.f, nullptr, 0, block_table, ctx_lens, q_lens, o, lse, B,
                         Hq, Hkv, Tq, D, block_size, max_blocks_per_seq, num_blocks, scale, causal, dtype, stream);
 }
 
@@ -348,9 +353,19 @@ attn_status attn_fwd_paged_rope(const void* q, const void* k_cache, const void* 
                                 int max_blocks_per_seq, int num_blocks, float scale, int causal, attn_dtype dtype,
                                 hipStream_t stream) {
   if (!rope) return fail(ATTN_ERR_INVALID, "attn_fwd_paged_rope: the rotary table must be non-null");
-  return fwd_paged_impl("attn_fwd_paged_rope", q, k_cache, v_cache, rope, max_pos, block_table, ctx_lens, q_lens, o,
+  return fwd_paged_impl("attn_fwd_paged_rope", false, q, k_cache, v_cache, 1.f, 1.f, rope, max_pos, block_table, ctx_lens, q_lens, o,
                         lse, B, Hq, Hkv, Tq, D, block_size, max_blocks_per_seq, num_blocks, scale, causal, dtype,
                         stream);
+}
+
+attn_status attn_fwd_paged_fp8(const void* q, const void* k_cache, const void* v_cache, float k_scale,
+                               float v_scale, const float* rope, int max_pos, const int* block_table,
+                               const int* ctx_lens, const int* q_lens, void* o, float* lse, int B, int Hq, int Hkv,
+                               int Tq, int D, int block_size, int max_blocks_per_seq, int num_blocks, float scale,
+                               int causal, attn_dtype dtype, hipStream_t stream) {
+  return fwd_paged_impl("attn_fwd_paged_fp8", true, q, k_cache, v_cache, k_scale, v_scale, rope, max_pos,
+                        block_table, ctx_lens, q_lens, o, lse, B, Hq, Hkv, Tq, D, block_size, max_blocks_per_seq,
+                        num_blocks, scale, causal, dtype, stream);
 }
 
 attn_status attn_cache_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,

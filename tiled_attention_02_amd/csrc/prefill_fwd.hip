@@ -48,6 +48,16 @@
 // tile: tile j+1 travels HBM -> LDS directly (buffer loads that write LDS)
 // while tile j is consumed. LDS operand reads are issued ahead of the MFMAs
 // that consume them (register double buffering).
+//
+// E4M3 form (chunked prefill over an FP8 cache, paged only): K/V tiles hold
+// one byte per element; operand fragments are converted to the 16-bit type
+// right after their LDS reads (exact), k_scale folds into the exponent factor
+// and v_scale into the final normalisation. A K read takes 16 codes = the
+// fragments of two k-steps (each k-step's 16 dims are split over the two lane
+// halves in another order than in the 16-bit form, and Q's fragments follow
+// the same order); a V^T fragment is one ds_read_b64_tr_b8 (8 keys of one
+// column). K and V tiles use different swizzles, each conflict-free for its
+// read pattern.
 #include "attn_device.h"
 #include "launch.h"
 
@@ -57,6 +67,8 @@ constexpr float kLazyRescale = 8.0f;
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 // 16-byte chunk slot of (row, chunk c) inside an LDS row: c ^ f(row). LDS
 // serves 256 bytes per cycle: 16 lanes of a 16-byte access, 32 lanes of an
@@ -70,14 +82,38 @@ __device__ __forceinline__ int swz(int row) {
   else return ((row >> 3) & 1) | (((row >> 2) & 1) << 1) | (((row >> 1) & 1) << 2);
 }
 
-template <int D, int BK>
+// E4M3 tiles (rows of D bytes). K is read 16 bytes per lane at 16 rows x one
+// chunk per 16 lanes: rows sharing the same 256-byte bank phase (equal parity
+// at D = 128, equal row % 4 at D = 64) take distinct chunk swaps. V is read
+// 8 bytes per lane (ds_read_b64_tr_b8) at rows {0-3, 8-11} (or {4-7, 12-15})
+// x 4 chunk halves per 32 lanes; the swap (always even, whole 16-byte chunks
+// stay together for the LDS-direct loads) is spread over row bits 1 and 3.
+template <int D>
+__device__ __forceinline__ int kswz8(int row) {
+  if constexpr (D == 128) return (row >> 1) & 7;
+  else return (row >> 2) & 3;
+}
+template <int D>
+__device__ __forceinline__ int vswz8(int row) {
+  if constexpr (D == 128) return 2 * (((row >> 1) & 1) | (((row >> 3) & 1) << 1));
+  else return 2 * ((row >> 3) & 1);
+}
+// the swizzle of a K (V = false) or V (V = true) tile
+template <int D, bool KV8, bool V>
+__device__ __forceinline__ int tswz(int row) {
+  if constexpr (!KV8) return swz<D>(row);
+  else if constexpr (V) return vswz8<D>(row);
+  else return kswz8<D>(row);
+}
+
+template <int D, int BK, bool KV8 = false>
 struct Shape {
   static constexpr int KS = D / 16;   // k-steps of S^T = K Q^T
   static constexpr int DB = D / 32;   // 32-row blocks of O^T
   static constexpr int KB = BK / 32;  // 32-key blocks of S^T
   static constexpr int PS = BK / 16;  // k-steps of O^T += V^T P^T
-  static constexpr int RB = D * 2;    // bytes per tile row
-  static constexpr int C8 = D / 8;    // 16-byte chunks per row
+  static constexpr int RB = KV8 ? D : 2 * D;  // bytes per tile row
+  static constexpr int C8 = RB / 16;  // 16-byte chunks per row
   static constexpr int TILE = BK * RB;
 };
 
@@ -110,9 +146,9 @@ __device__ __forceinline__ Geo make_geo(const PrefillArgs& a) {
     // (clamped to what the table and q can hold, which keeps every access in bounds)
     g.Lk = min(a.ctx_lens[g.b], a.max_blocks * 16);
     g.Lq = a.q_lens ? min(a.q_lens[g.b], a.Tq) : a.Tq;
-    // block 0 of the kv head; the stager adds physical block offsets
-    g.Kg = static_cast<const uint16_t*>(a.k) + (size_t)g.kvh * 16 * D;
-    g.Vg = static_cast<const uint16_t*>(a.v) + (size_t)g.kvh * 16 * D;
+    // (the stagers address the cache blocks themselves)
+    g.Kg = nullptr;
+    g.Vg = nullptr;
   } else {
     g.Lq = a.Tq;
     g.Lk = a.Tk;
@@ -142,27 +178,37 @@ struct Acc {
   float m, l, lr;      // running max (log2 units), fp32 sum, sum of the rounded p
 };
 
-template <class T, int D>
+// Column of the 8 dims lane half h holds in k-step s: 16s + 8h in the 16-bit
+// form; in the E4M3 form k-steps 2p and 2p + 1 share one 32-dim group, lane
+// half h holding dims 32p + 16h .. +16 (the first 8 in step 2p). In both,
+// step s + D/32 holds the partner columns (+ D/2) of step s.
+template <int D, bool KV8>
+__device__ __forceinline__ int q_col(int s, int h) {
+  return KV8 ? 32 * (s >> 1) + 16 * h + 8 * (s & 1) : 16 * s + 8 * h;
+}
+
+template <class T, int D, bool KV8>
 __device__ __forceinline__ void load_q(Acc<D>& st, const Geo& g, int qmode, int qrow, int h, const float* rope,
                                        int max_pos) {
   const bool live = qrow < g.Lq;
   const uint32_t flip = qmode == 1 ? 0x80008000u : 0u;
   const bool zero = qmode == 2 || !live;
-  const u32x4* src = reinterpret_cast<const u32x4*>(g.Qg + (size_t)(live ? qrow : 0) * D + 8 * h);
+  const uint16_t* src = g.Qg + (size_t)(live ? qrow : 0) * D;
   u32x4 x[D / 16];
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) x[s] = src[2 * s];
+  for (int s = 0; s < D / 16; ++s) x[s] = *reinterpret_cast<const u32x4*>(src + q_col<D, KV8>(s, h));
   if (rope) {
     // rotary embedding at the row's position (Lk - Lq + row): fragment s < D/32
-    // holds columns 16s + 8h .. +8 of the first half, fragment s + D/32 their partners
-    const float* tr = rope + (size_t)min(max(g.off + qrow, 0), max_pos - 1) * D + 8 * h;
+    // holds 8 columns of the first half, fragment s + D/32 their partners
+    const float* tr = rope + (size_t)min(max(g.off + qrow, 0), max_pos - 1) * D;
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
+      const int col = q_col<D, KV8>(s, h);
       float c[8], sn[8];
-      *reinterpret_cast<f32x4*>(c) = *reinterpret_cast<const f32x4*>(tr + 16 * s);
-      *reinterpret_cast<f32x4*>(c + 4) = *reinterpret_cast<const f32x4*>(tr + 16 * s + 4);
-      *reinterpret_cast<f32x4*>(sn) = *reinterpret_cast<const f32x4*>(tr + D / 2 + 16 * s);
-      *reinterpret_cast<f32x4*>(sn + 4) = *reinterpret_cast<const f32x4*>(tr + D / 2 + 16 * s + 4);
+      *reinterpret_cast<f32x4*>(c) = *reinterpret_cast<const f32x4*>(tr + col);
+      *reinterpret_cast<f32x4*>(c + 4) = *reinterpret_cast<const f32x4*>(tr + col + 4);
+      *reinterpret_cast<f32x4*>(sn) = *reinterpret_cast<const f32x4*>(tr + D / 2 + col);
+      *reinterpret_cast<f32x4*>(sn + 4) = *reinterpret_cast<const f32x4*>(tr + D / 2 + col + 4);
       rope8<T>(x[s], x[s + D / 32], c, sn);
     }
   }
@@ -185,10 +231,28 @@ struct Offs {
   int v[D / 32][2];
 };
 
-template <int D, int BK>
+template <int D, int BK, bool KV8>
 __device__ __forceinline__ void make_offs(Offs<D, BK>& o, int lane) {
-  using S = Shape<D, BK>;
+  using S = Shape<D, BK, KV8>;
   const int h = lane >> 5, c32 = lane & 31, g16 = lane >> 4, i16 = lane & 15;
+  if constexpr (KV8) {
+    // K: k-steps 2p, 2p + 1 from one 16-byte read of row c32 at chunk 2p + h
+#pragma unroll
+    for (int p = 0; p < S::KS / 2; ++p) o.k[p] = c32 * S::RB + 16 * ((2 * p + h) ^ kswz8<D>(c32));
+    // V^T via ds_read_b64_tr_b8: in each 16-lane group, lane j receives byte
+    // (j & 7) of the 8 bytes read by lanes 2e + (j >> 3). Element e of lane
+    // half h is key 8(e >> 2) + 4h + (e & 3) of the k-step (P^T's order), so
+    // lane i addresses that key for e = i >> 1 at columns
+    // 32db + 16(g16 % 2) + 8(i & 1) .. +8 and receives column 32db + 16(g16 % 2) + i.
+    const int e = i16 >> 1;
+    const int row = 8 * (e >> 2) + 4 * h + (e & 3);  // plus 16s per k-step (keeps the swizzle)
+#pragma unroll
+    for (int db = 0; db < S::DB; ++db) {
+      o.v[db][0] = row * S::RB + 16 * ((2 * db + (g16 & 1)) ^ vswz8<D>(row)) + 8 * (i16 & 1);
+      o.v[db][1] = o.v[db][0];
+    }
+    return;
+  }
   // K operand of k-step s: row kb*32 + c32, chunk (2s + h) ^ swz(row); swz(row)
   // does not depend on kb because kb*32 is a multiple of 16.
   const int sw = swz<D>(c32);
@@ -216,10 +280,35 @@ __device__ __forceinline__ void make_offs(Offs<D, BK>& o, int lane) {
 // directives: callers add the pattern they want.
 constexpr int kQkDepth = 2;
 
-template <class T, int D, int BK>
+template <class T, int D, int BK, bool KV8 = false>
 __device__ __forceinline__ void tile_qk_plain(f32x16 (&sacc)[BK / 32], const char* Ks, const Offs<D, BK>& o,
                                               const Acc<D>& st) {
-  using S = Shape<D, BK>;
+  using S = Shape<D, BK, KV8>;
+  if constexpr (KV8) {
+    // one 16-byte read per (key block, k-step pair) = the two steps' fragments
+    // as 16 codes; the next pair's reads go out before this pair's MFMAs
+    u32x4 raw[2][S::KB];
+#pragma unroll
+    for (int kb = 0; kb < S::KB; ++kb) {
+      sacc[kb] = f32x16{};
+      raw[0][kb] = *reinterpret_cast<const u32x4*>(Ks + kb * 32 * S::RB + o.k[0]);
+    }
+#pragma unroll
+    for (int p = 0; p < S::KS / 2; ++p) {
+      if (p + 1 < S::KS / 2) {
+#pragma unroll
+        for (int kb = 0; kb < S::KB; ++kb)
+          raw[(p + 1) & 1][kb] = *reinterpret_cast<const u32x4*>(Ks + kb * 32 * S::RB + o.k[p + 1]);
+      }
+#pragma unroll
+      for (int kb = 0; kb < S::KB; ++kb) {
+        const u32x4 r = raw[p & 1][kb];
+        sacc[kb] = T::mfma32(e4m3x8<T>(u32x2{r[0], r[1]}), st.qf[2 * p], sacc[kb]);
+        sacc[kb] = T::mfma32(e4m3x8<T>(u32x2{r[2], r[3]}), st.qf[2 * p + 1], sacc[kb]);
+      }
+    }
+    return;
+  }
   constexpr int DEPTH = kQkDepth;
   u32x4 fr[DEPTH + 1][S::KB];
 #pragma unroll
@@ -241,11 +330,12 @@ __device__ __forceinline__ void tile_qk_plain(f32x16 (&sacc)[BK / 32], const cha
   }
 }
 
-template <class T, int D, int BK>
+template <class T, int D, int BK, bool KV8 = false>
 __device__ __forceinline__ void tile_qk(f32x16 (&sacc)[BK / 32], const char* Ks, const Offs<D, BK>& o,
                                         const Acc<D>& st) {
   using S = Shape<D, BK>;
-  tile_qk_plain<T, D, BK>(sacc, Ks, o, st);
+  tile_qk_plain<T, D, BK, KV8>(sacc, Ks, o, st);
+  if constexpr (KV8) return;  // compiler-scheduled
   // schedule: the reads of step s+DEPTH go out before the MFMAs of step s
   __builtin_amdgcn_sched_group_barrier(0x100, kQkDepth * S::KB, 0);
 #pragma unroll
@@ -256,9 +346,13 @@ __device__ __forceinline__ void tile_qk(f32x16 (&sacc)[BK / 32], const char* Ks,
 }
 
 // Two transposing reads give the 8-element V^T operand of one MFMA.
-template <int D, int BK>
+template <class T, int D, int BK, bool KV8 = false>
 __device__ __forceinline__ u32x4 vt_frag(const char* Vs, const Offs<D, BK>& o, int db, int s) {
-  using S = Shape<D, BK>;
+  using S = Shape<D, BK, KV8>;
+  if constexpr (KV8) {
+    const i32x2 v8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(Vs + 16 * s * S::RB + o.v[db][0]));
+    return e4m3x8<T>(__builtin_bit_cast(u32x2, v8));
+  }
   const i16x4 p0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vs + 16 * s * S::RB + o.v[db][0]));
   const i16x4 p1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vs + 16 * s * S::RB + o.v[db][1]));
   const u32x2 a0 = __builtin_bit_cast(u32x2, p0);
@@ -268,18 +362,18 @@ __device__ __forceinline__ u32x4 vt_frag(const char* Vs, const Offs<D, BK>& o, i
 
 // O^T += V^T P^T for one tile in LDS; fragments of k-step s+1 are read while
 // the DB independent MFMAs of step s run.
-template <class T, int D, int BK>
+template <class T, int D, int BK, bool KV8 = false>
 __device__ __forceinline__ void tile_pv(Acc<D>& st, const u32x4 (&pf)[BK / 16], const char* Vs,
                                         const Offs<D, BK>& o) {
   using S = Shape<D, BK>;
   u32x4 fr[2][S::DB];
 #pragma unroll
-  for (int db = 0; db < S::DB; ++db) fr[0][db] = vt_frag<D, BK>(Vs, o, db, 0);
+  for (int db = 0; db < S::DB; ++db) fr[0][db] = vt_frag<T, D, BK, KV8>(Vs, o, db, 0);
 #pragma unroll
   for (int s = 0; s < S::PS; ++s) {
     if (s + 1 < S::PS) {
 #pragma unroll
-      for (int db = 0; db < S::DB; ++db) fr[(s + 1) & 1][db] = vt_frag<D, BK>(Vs, o, db, s + 1);
+      for (int db = 0; db < S::DB; ++db) fr[(s + 1) & 1][db] = vt_frag<T, D, BK, KV8>(Vs, o, db, s + 1);
     }
 #pragma unroll
     for (int db = 0; db < S::DB; ++db) st.oacc[db] = T::mfma32(fr[s & 1][db], pf[s], st.oacc[db]);
@@ -359,12 +453,13 @@ __device__ __forceinline__ void softmax_exp(const f32x16 (&sacc)[BK / 32], u32x4
 
 // O = O^T / l, lse = (m + log2 l) ln 2; padding rows -> 0, -inf.
 template <class T, int D>
-__device__ __forceinline__ void epilogue(const Acc<D>& st, const Geo& g, int Tq, int qrow, int h) {
+__device__ __forceinline__ void epilogue(const Acc<D>& st, const Geo& g, int Tq, int qrow, int h,
+                                         float vscale = 1.f) {
   const float l_tot = half_swap_sum(st.l);
   const float lr_tot = half_swap_sum(st.lr);
   if (qrow >= Tq) return;
   const bool has = qrow < g.Lq && l_tot > 0.f;
-  const float inv = has ? 1.f / lr_tot : 0.f;
+  const float inv = has ? vscale / lr_tot : 0.f;
   uint16_t* orow = g.Og + (size_t)qrow * D + 4 * h;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -390,9 +485,9 @@ constexpr int kBufferDword3 = 0x00020000;  // raw (untyped) buffer, 32-bit data
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int D, int BK, int THREADS, bool PAGED>
+template <int D, int BK, int THREADS, bool PAGED, bool KV8 = false, bool V = false>
 struct Stager {
-  using S = Shape<D, BK>;
+  using S = Shape<D, BK, KV8>;
   static constexpr int NW = THREADS / 64;
   static constexpr int RPI = 1024 / S::RB;      // rows per wavefront instruction
   static constexpr int CPT = BK / (RPI * NW);   // instructions per wavefront per tile
@@ -403,11 +498,11 @@ struct Stager {
   int voff[CPT];  // per-lane byte offset of the fetched chunk (within the tile, or within the cache block)
   int loff[CPT];  // wave-uniform LDS byte offset of the instruction within the tile
   int wblk;       // paged: the wave's share of an instruction's block index, in [0, JW)
-  const uint16_t* base;
-  size_t bstride;   // paged: elements per physical block (all kv heads)
+  const char* base;
+  size_t bstride;   // paged: bytes per physical block (all kv heads)
   const int* tbl;   // paged: the sequence's block-table row, in LDS
 
-  __device__ __forceinline__ void init(const uint16_t* b, int tid, size_t block_stride = 0,
+  __device__ __forceinline__ void init(const char* b, int tid, size_t block_stride = 0,
                                        const int* table = nullptr) {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l = tid & 63;
@@ -415,7 +510,7 @@ struct Stager {
     for (int i = 0; i < CPT; ++i) {
       const int n = i * NW + w;
       const int row = n * RPI + l / S::C8;
-      const int chunk = 16 * ((l % S::C8) ^ swz<D>(row));
+      const int chunk = 16 * ((l % S::C8) ^ tswz<D, KV8, V>(row));
       voff[i] = (PAGED ? row % 16 : row) * S::RB + chunk;
       loff[i] = n * RPI * S::RB;
     }
@@ -450,7 +545,7 @@ struct Stager {
       // descriptor in vector registers would need a loop per load)
       const int rows = __builtin_amdgcn_readfirstlane(min(max(Lk - k0, 0), BK));
       const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-          uniform_ptr(base + (size_t)k0 * D), (short)0, rows * S::RB, kBufferDword3);
+          uniform_ptr(base + (size_t)k0 * S::RB), (short)0, rows * S::RB, kBufferDword3);
 #pragma unroll
       for (int i = 0; i < CPT; ++i) load_lds(rsrc, tile + loff[i], voff[i]);
       (void)e;
@@ -472,7 +567,7 @@ struct Stager {
       }
     }
   }
-  static __device__ __forceinline__ void* uniform_ptr(const uint16_t* ptr) {
+  static __device__ __forceinline__ void* uniform_ptr(const char* ptr) {
     const uint64_t p = reinterpret_cast<uint64_t>(ptr);
     return reinterpret_cast<void*>(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(p >> 32)) << 32) |
                                    (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p));
@@ -507,23 +602,23 @@ __device__ __forceinline__ void staged_barrier() {
 //     the wavefront work at the same time;
 //   * accumulates O^T += V^T P^T for tile kt (MFMA);
 // and ends with the wait for its loads and a barrier.
-template <class T, int D, int BK, bool CAUSAL, class Stg>
+template <class T, int D, int BK, bool CAUSAL, bool KV8, class KStg, class VStg>
 __device__ __forceinline__ void pipe_step(int kt, const char* kcur, const char* vcur, char* kload, char* vload,
                                           f32x16 (&s_cur)[BK / 32], f32x16 (&s_nxt)[BK / 32],
-                                          const Stg& ks, const Stg& vs,
-                                          int (&ecar)[Stg::EPT], Acc<D>& st, const Offs<D, BK>& o,
+                                          const KStg& ks, const VStg& vs,
+                                          int (&ecar)[KStg::EPT], Acc<D>& st, const Offs<D, BK>& o,
                                           const Geo& g, bool wave_live, int w_last, int w_lo, int qrow, int h,
                                           float cexp) {
   using S = Shape<D, BK>;
   // (paged form) ecar: the physical blocks of tile kt+1, read one step earlier
   // for its K and reused now for its V
   if (kt + 2 < g.nkt) {
-    int enew[Stg::EPT];
+    int enew[KStg::EPT];
     ks.entries(kt + 2, enew);
     ks.load(kt + 2, g.Lk, kload, enew);
     if (kt + 1 < g.nkt) vs.load(kt + 1, g.Lk, vload, ecar);
 #pragma unroll
-    for (int i = 0; i < Stg::EPT; ++i) ecar[i] = enew[i];
+    for (int i = 0; i < KStg::EPT; ++i) ecar[i] = enew[i];
   } else if (kt + 1 < g.nkt) {
     vs.load(kt + 1, g.Lk, vload, ecar);
   }
@@ -534,7 +629,11 @@ __device__ __forceinline__ void pipe_step(int kt, const char* kcur, const char* 
   if (work) {
     u32x4 pf[S::PS];
     const float msub = softmax_stats<T, D, BK, CAUSAL>(s_cur, st, g, kt * BK, qrow, w_lo, h, cexp);
-    if (work_next) {
+    if (work_next && KV8) {
+      // E4M3 tiles: the compiler schedules the converted reads and the exponentials
+      tile_qk_plain<T, D, BK, KV8>(s_nxt, kcur, o, st);
+      softmax_exp<T, D, BK>(s_cur, pf, st, msub, cexp);
+    } else if (work_next) {
       tile_qk_plain<T, D, BK>(s_nxt, kcur, o, st);
       softmax_exp<T, D, BK>(s_cur, pf, st, msub, cexp);
       // interleave: each MFMA of the next tile's S is followed by a share of
@@ -556,7 +655,7 @@ __device__ __forceinline__ void pipe_step(int kt, const char* kcur, const char* 
       softmax_exp<T, D, BK>(s_cur, pf, st, msub, cexp);
     }
     __builtin_amdgcn_s_setprio(2);
-    tile_pv<T, D, BK>(st, pf, vcur, o);
+    tile_pv<T, D, BK, KV8>(st, pf, vcur, o);
     __builtin_amdgcn_s_setprio(0);
   }
   staged_barrier();
@@ -564,9 +663,10 @@ __device__ __forceinline__ void pipe_step(int kt, const char* kcur, const char* 
 
 // ---------------------------------------------------------------------------
 // 4 wavefronts x 32 rows, pipelined key steps over double-buffered K and V.
-template <class T, int D, int BQ, int BK, bool CAUSAL, bool PAGED>
+template <class T, int D, int BQ, int BK, bool CAUSAL, bool PAGED, bool KV8>
 __global__ __launch_bounds__(BQ * 2, 2) void prefill_kernel(PrefillArgs a) {
-  using S = Shape<D, BK>;
+  static_assert(PAGED || !KV8, "E4M3 tiles come from the paged cache");
+  using S = Shape<D, BK, KV8>;
   constexpr int THREADS = (BQ / 32) * 64;
   // K of tile t lives in kb[t & 1], V of tile t in vb[t & 1]; separate LDS
   // arrays, so reads of one are never ordered behind the loads into another
@@ -583,26 +683,32 @@ __global__ __launch_bounds__(BQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   const int w_lo = g.q_lo + w * 32;
   const int qrow = w_lo + (lane & 31);
   Acc<D> st;
-  load_q<T, D>(st, g, a.qmode, qrow, h, PAGED ? a.rope : nullptr, a.max_pos);
+  load_q<T, D, KV8>(st, g, a.qmode, qrow, h, PAGED ? a.rope : nullptr, a.max_pos);
   Offs<D, BK> o;
-  make_offs(o, lane);
-  Stager<D, BK, THREADS, PAGED> ks, vs;
+  make_offs<D, BK, KV8>(o, lane);
+  using KStg = Stager<D, BK, THREADS, PAGED, KV8, false>;
+  using VStg = Stager<D, BK, THREADS, PAGED, KV8, true>;
+  KStg ks;
+  VStg vs;
+  // E4M3 caches: k_scale multiplies every score, v_scale every value
+  const float cexp = KV8 ? a.c * a.k_scale : a.c;
   if constexpr (PAGED) {
-    const size_t bstride = (size_t)a.Hkv * 16 * D;
-    ks.init(g.Kg, tid, bstride, tbl);
-    vs.init(g.Vg, tid, bstride, tbl);
+    // byte offsets: kv head kvh of physical block 0, and one physical block
+    const size_t head = (size_t)g.kvh * 16 * S::RB, bstride = (size_t)a.Hkv * 16 * S::RB;
+    ks.init(static_cast<const char*>(a.k) + head, tid, bstride, tbl);
+    vs.init(static_cast<const char*>(a.v) + head, tid, bstride, tbl);
     const int nb = min((g.Lk + 15) / 16, kMaxPagedPrefillBlocks);
     const int* trow = a.table + (size_t)g.b * a.max_blocks;
     for (int i = tid; i < nb; i += THREADS) tbl[i] = min(max(trow[i], 0), a.num_blocks - 1);
     __syncthreads();
   } else {
-    ks.init(g.Kg, tid);
-    vs.init(g.Vg, tid);
+    ks.init(reinterpret_cast<const char*>(g.Kg), tid);
+    vs.init(reinterpret_cast<const char*>(g.Vg), tid);
   }
 
-  int ecar[Stager<D, BK, THREADS, PAGED>::EPT] = {};  // physical blocks of the tile after the current one
+  int ecar[KStg::EPT] = {};  // physical blocks of the tile after the current one
   if (g.nkt > 0) {
-    int e0[Stager<D, BK, THREADS, PAGED>::EPT];
+    int e0[KStg::EPT];
     ks.entries(0, e0);
     ks.load(0, g.Lk, kb0, e0);
     vs.load(0, g.Lk, vb0, e0);
@@ -615,35 +721,36 @@ __global__ __launch_bounds__(BQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   const bool wave_live = w_lo < g.Lq;
   const int w_last = min(w_lo + 31, g.Lq - 1) + g.off;  // last key any row of this wavefront sees
   f32x16 s0[S::KB], s1[S::KB];
-  if (g.nkt > 0 && wave_live && (!CAUSAL || 0 <= w_last)) tile_qk<T, D, BK>(s0, kb0, o, st);
+  if (g.nkt > 0 && wave_live && (!CAUSAL || 0 <= w_last)) tile_qk<T, D, BK, KV8>(s0, kb0, o, st);
   for (int kt = 0; kt < g.nkt; kt += 2) {
-    pipe_step<T, D, BK, CAUSAL>(kt, kb1, vb0, kb0, vb1, s0, s1, ks, vs, ecar, st, o, g, wave_live, w_last, w_lo,
-                                qrow, h, a.c);
+    pipe_step<T, D, BK, CAUSAL, KV8>(kt, kb1, vb0, kb0, vb1, s0, s1, ks, vs, ecar, st, o, g, wave_live, w_last,
+                                     w_lo, qrow, h, cexp);
     if (kt + 1 < g.nkt)
-      pipe_step<T, D, BK, CAUSAL>(kt + 1, kb0, vb1, kb1, vb0, s1, s0, ks, vs, ecar, st, o, g, wave_live, w_last,
-                                  w_lo, qrow, h, a.c);
+      pipe_step<T, D, BK, CAUSAL, KV8>(kt + 1, kb0, vb1, kb1, vb0, s1, s0, ks, vs, ecar, st, o, g, wave_live,
+                                       w_last, w_lo, qrow, h, cexp);
   }
-  epilogue<T, D>(st, g, a.Tq, qrow, h);
+  epilogue<T, D>(st, g, a.Tq, qrow, h, KV8 ? a.v_scale : 1.f);
 }
 
 // ---------------------------------------------------------------------------
-template <class T, int D, int BK, bool CAUSAL, bool PAGED>
+template <class T, int D, int BK, bool CAUSAL, bool PAGED, bool KV8 = false>
 static hipError_t launch_D(const PrefillArgs& a, hipStream_t stream) {
   PrefillArgs x = a;
   x.nqt = (a.Tq + 127) / 128;
   const long long blocks = (long long)x.nqt * a.Hq * a.B;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   x.xcd_remap = (blocks % (8LL * a.G) == 0) ? 1 : 0;
-  hipLaunchKernelGGL((prefill_kernel<T, D, 128, BK, CAUSAL, PAGED>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                     x);
+  hipLaunchKernelGGL((prefill_kernel<T, D, 128, BK, CAUSAL, PAGED, KV8>), dim3((unsigned)blocks), dim3(256), 0,
+                     stream, x);
   return hipGetLastError();
 }
 
-template <class T, bool PAGED>
+template <class T, bool PAGED, bool KV8 = false>
 static hipError_t launch_t(const PrefillArgs& a, int D, bool causal, hipStream_t stream) {
   if (D == 128)
-    return causal ? launch_D<T, 128, 64, true, PAGED>(a, stream) : launch_D<T, 128, 64, false, PAGED>(a, stream);
-  return causal ? launch_D<T, 64, 64, true, PAGED>(a, stream) : launch_D<T, 64, 64, false, PAGED>(a, stream);
+    return causal ? launch_D<T, 128, 64, true, PAGED, KV8>(a, stream)
+                  : launch_D<T, 128, 64, false, PAGED, KV8>(a, stream);
+  return causal ? launch_D<T, 64, 64, true, PAGED, KV8>(a, stream) : launch_D<T, 64, 64, false, PAGED, KV8>(a, stream);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int D, bool causal, hipStream_t stream) {
@@ -652,6 +759,10 @@ hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int D, bool causal, h
 
 hipError_t launch_prefill_paged(const PrefillArgs& a, bool bf16, int D, bool causal, hipStream_t stream) {
   return bf16 ? launch_t<BF16, true>(a, D, causal, stream) : launch_t<F16, true>(a, D, causal, stream);
+}
+
+hipError_t launch_prefill_paged_fp8(const PrefillArgs& a, bool bf16, int D, bool causal, hipStream_t stream) {
+  return bf16 ? launch_t<BF16, true, true>(a, D, causal, stream) : launch_t<F16, true, true>(a, D, causal, stream);
 }
 
 }  // namespace attn
