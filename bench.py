@@ -49,6 +49,9 @@ KERNEL_SOURCES = {
     "append": ["tiled_attention_02_amd/csrc/paged_cache.hip"],
     "decode_fp8": ["tiled_attention_02_amd/csrc/decode_paged.hip", "tiled_attention_02_amd/csrc/attn_device.h"],
     "append_rope": ["tiled_attention_02_amd/csrc/paged_cache.hip", "tiled_attention_02_amd/csrc/attn_device.h"],
+    "append_fp8": ["tiled_attention_02_amd/csrc/paged_cache.hip", "tiled_attention_02_amd/csrc/attn_device.h"],
+    "chunked_prefill_fp8": ["tiled_attention_02_amd/csrc/prefill_fwd.hip",
+                            "tiled_attention_02_amd/csrc/attn_device.h"],
 }
 APPEND_LAYERS = 8
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
@@ -175,6 +178,21 @@ def cpu_baseline_chunked(x, case, nseq=1, rope=None):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _oracle_threads(), "kind": "oracle",
             "sample": f"float64 oracle (prefill through the block table) on {nseq} of {case.B} sequences, "
                       f"all {case.Hq} heads and rows; {dt:.1f} s wall"}
+
+
+def cpu_baseline_chunked_fp8(x, case, k8, v8, ks, vs, nseq=1):
+    """Time the float64 oracle (dequantize, then the chunked prefill) on the first sequence of the batch."""
+    import workloads as W
+    from oracle import fp8 as F8
+    sl = slice(0, nseq)
+    t0 = time.perf_counter()
+    F8.prefill_paged_fp8(x["q"][sl], k8, v8, ks, vs, x["block_table"][sl], x["ctx_lens"][sl], x["new_lens"][sl],
+                         case.scale, True)
+    dt = time.perf_counter() - t0
+    flops = W.chunk_flops(x["ctx_lens"][sl], x["new_lens"][sl], case.Hq, case.D, True)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _oracle_threads(), "kind": "oracle",
+            "sample": f"float64 oracle (dequantize the E4M3 cache, then the chunked prefill) on {nseq} of "
+                      f"{case.B} sequences, all {case.Hq} heads and rows; {dt:.1f} s wall"}
 
 
 def context_measurements(ta, W, torch, np, dev, flush_rows, flush_dst, evict):
@@ -320,6 +338,12 @@ def main():
     # query load (its own caches, so each leg keeps its own cache contents)
     rope_tab = torch.from_numpy(W.rope_table(16384, cc.D)).to(dev)
     rope_sets = [tuple(t.clone() for t in (ckn, cvn, ckc, cvc)) for _ in range(APPEND_LAYERS)]
+    # the FP8 leg: the chunk quantized into E4M3 caches, then the chunked prefill over them
+    c8 = np.random.default_rng(cc.seed + 1000)
+    ck8 = torch.from_numpy(W.e4m3_codes(c8, xc["k_cache"].shape)).to(dev)
+    cv8 = torch.from_numpy(W.e4m3_codes(c8, xc["v_cache"].shape)).to(dev)
+    fp8_sets = [(ckn, cvn, ck8, cv8)] + [tuple(t.clone() for t in (ckn, cvn, ck8, cv8))
+                                         for _ in range(APPEND_LAYERS - 1)]
 
     pflops = W.prefill_flops(pc.B, pc.Hq, pc.T, pc.T, pc.D, True)
     dbytes = W.decode_bytes(xd["ctx_lens"], dc.Hq, dc.Hkv, dc.D)
@@ -355,6 +379,17 @@ def main():
 
         parts.append(("append" + tag, appends, APPEND_LAYERS))
         parts.append(("chunked_prefill" + tag, chunk_prefill, 1))
+    if args.only in (None, "chunked"):
+        def appends8():
+            for kn_, vn_, kc_, vc_ in fp8_sets:
+                ta.attn_cache_append_fp8(kn_, vn_, kc_, vc_, KS8, VS8, cbt, cst, cnl)
+
+        def chunk_prefill8():
+            ta.attn_fwd_paged_fp8(cq, ck8, cv8, KS8, VS8, cbt, ccl, cnl, scale=cc.scale, causal=True, out=co,
+                                  lse=clse)
+
+        parts.append(("append_fp8", appends8, APPEND_LAYERS))
+        parts.append(("chunked_prefill_fp8", chunk_prefill8, 1))
 
     def evict():
         # read-only pass over 1 GiB: pushes the inputs out of every cache level
@@ -394,6 +429,7 @@ def main():
     p_avg, d_avg, d8_avg = ms["prefill"], ms["decode"], ms["decode_fp8"]
     a_avg, c_avg = ms["append"], ms["chunked_prefill"]
     ar_avg, cr_avg = ms["append_rope"], ms["chunked_prefill_rope"]
+    a8_avg, c8_avg = ms["append_fp8"], ms["chunked_prefill_fp8"]
 
     p_tfs = pflops / (p_avg * 1e-3) / 1e12
     d_gbs = dbytes / (d_avg * 1e-3) / 1e9
@@ -402,6 +438,9 @@ def main():
     d8_gbs = d8bytes / (d8_avg * 1e-3) / 1e9
     cr_tfs = cflops / (cr_avg * 1e-3) / 1e12
     ar_gbs = abytes / (ar_avg * 1e-3) / 1e9
+    c8_tfs = cflops / (c8_avg * 1e-3) / 1e12
+    a8bytes = abytes * 3 // 4  # the chunk's K and V read as 16-bit values, written as 1-byte codes
+    a8_gbs = a8bytes / (a8_avg * 1e-3) / 1e9
     out = {
         "metric": METRIC,
         "value": round(p_tfs, 2),
@@ -419,7 +458,8 @@ def main():
                                "B=64 Hq=12 Hkv=2 D=128 ctx~U[512,4096] block=16 (decode; again over an E4M3 cache: decode_fp8) + "
                                "chunked bf16 prefill "
                                "B=4 Hq=32 Hkv=8 D=128 prefix~U[2048,8192] chunk=1024 through the block table "
-                               "(chunked; again with RoPE fused: chunked_rope)",
+                               "(chunked; again with RoPE fused: chunked_rope; again over E4M3 caches: "
+                               "chunked_fp8)",
                    "prefill_gflop_per_call": round(pflops / 1e9, 3),
                    "decode_mb_per_call": round(dbytes / 1e6, 3),
                    "cache_eviction_before_each_call": "none" if args.no_flush else "1 GiB read pass",
@@ -468,6 +508,19 @@ def main():
                                     "kernel": "append_rope_kernel", "algorithmic_bytes_per_launch": abytes,
                                     "note": "bytes: the chunk's K and V read and written once; the table rows "
                                             "read are not counted"}}},
+        "chunked_fp8": {
+            "workload": cc.name + ", over E4M3 caches (k_scale, v_scale as decode_fp8)",
+            "prefill": {"value": round(c8_tfs, 2), "unit": "TFLOP/s", "us_per_call": round(c8_avg * 1e3, 2),
+                        "roofline": {"bound": "mfma", "achieved": round(c8_tfs, 2), "peak": PEAK_BF16_TFLOPS,
+                                     "unit": "TFLOP/s", "frac": round(c8_tfs / PEAK_BF16_TFLOPS, 4),
+                                     "traffic": measured_traffic("chunked_prefill_fp8"),
+                                     "kernel": "prefill_kernel (paged form, E4M3 tiles; bf16 products)",
+                                     "algorithmic_flops_per_launch": cflops}},
+            "append": {"value": round(a8_gbs, 1), "unit": "GB/s", "us_per_call": round(a8_avg * 1e3, 2),
+                       "timing": f"a burst of {APPEND_LAYERS} quantizing appends, as for chunked.append",
+                       "roofline": {"bound": "hbm", "achieved": round(a8_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                    "frac": round(a8_gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic("append_fp8"),
+                                    "kernel": "append_kernel (E4M3 codes)", "algorithmic_bytes_per_launch": a8bytes}}},
     }
     out["context"] = context_measurements(ta, W, torch, np, dev, flush_rows, flush_dst, evict)
     if not args.no_cpu_baseline:
@@ -479,6 +532,9 @@ def main():
         out["decode_fp8"]["cpu_baseline"] = cpu_baseline_decode_fp8(xd8, dc, KS8, VS8)
         log("[bench] cpu baseline: float64 oracle on a sample of the chunked-prefill workload")
         out["chunked"]["cpu_baseline"] = cpu_baseline_chunked(xc, cc)
+        log("[bench] cpu baseline: float64 oracle on a sample of the FP8 chunked-prefill workload")
+        out["chunked_fp8"]["cpu_baseline"] = cpu_baseline_chunked_fp8(xc, cc, ck8.cpu().numpy(), cv8.cpu().numpy(),
+                                                                      KS8, VS8)
         log("[bench] cpu baseline: float64 oracle on a sample of the rotary chunked-prefill workload")
         out["chunked_rope"]["cpu_baseline"] = cpu_baseline_chunked(xc, cc, rope=W.rope_table(16384, cc.D))
     print(json.dumps(out), flush=True)
