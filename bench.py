@@ -41,6 +41,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attention TFLOP/s (bf16 causal prefill) + decode HBM GB/s, % of MI355X peak"
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP8_TFLOPS = 5000.0
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = {
     "prefill": ["tiled_attention_02_amd/csrc/prefill_fwd.hip", "tiled_attention_02_amd/csrc/attn_device.h"],
@@ -49,6 +50,7 @@ KERNEL_SOURCES = {
     "append": ["tiled_attention_02_amd/csrc/paged_cache.hip"],
     "decode_fp8": ["tiled_attention_02_amd/csrc/decode_paged.hip", "tiled_attention_02_amd/csrc/attn_device.h"],
     "append_rope": ["tiled_attention_02_amd/csrc/paged_cache.hip", "tiled_attention_02_amd/csrc/attn_device.h"],
+    "prefill_fp8": ["tiled_attention_02_amd/csrc/prefill_fwd.hip", "tiled_attention_02_amd/csrc/attn_device.h"],
     "append_fp8": ["tiled_attention_02_amd/csrc/paged_cache.hip", "tiled_attention_02_amd/csrc/attn_device.h"],
     "chunked_prefill_fp8": ["tiled_attention_02_amd/csrc/prefill_fwd.hip",
                             "tiled_attention_02_amd/csrc/attn_device.h"],
@@ -84,7 +86,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-flush", action="store_true", help="skip the cache flush between calls")
-    p.add_argument("--only", choices=["prefill", "decode", "decode_fp8", "chunked"], default=None,
+    p.add_argument("--only", choices=["prefill", "prefill_fp8", "decode", "decode_fp8", "chunked"], default=None,
                    help="profile helper: run only one of the two calls (not a benchmark line)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="run a plain device copy of this many MiB (counter calibration) and exit")
@@ -120,6 +122,26 @@ def cpu_baseline_prefill(x, case, budget_heads=32, row_stride=8):
             "sample": f"float64 oracle on {len(heads)} of {case.Hq} heads x {len(rows)} query rows "
                       f"(every {row_stride}th) of the 16384-token causal prefill; {dt:.1f} s wall; "
                       f"algorithmic flops of the sampled rows / wall time"}
+
+
+def cpu_baseline_prefill_fp8(x, case, qs, ks, vs, budget_heads=8, row_stride=16):
+    """Time the float64 oracle (dequantize, then the definition) on a bounded sample of the FP8 prefill."""
+    import numpy as np
+    from oracle import fp8 as F8
+    from oracle import oracle as O
+    threads = _oracle_threads()
+    heads = list(range(0, case.Hq, max(1, case.Hq // budget_heads)))[:budget_heads]
+    rows = np.arange(0, case.T, row_stride)
+    picks = np.array([(0, h, i) for h in heads for i in rows])
+    t0 = time.perf_counter()
+    qd, kd, vd = F8.dequantize(x["q"], qs), F8.dequantize(x["k"], ks), F8.dequantize(x["v"], vs)
+    O.prefill_rows(qd, kd, vd, case.scale, True, None, picks)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * case.D * float((rows + 1).sum()) * len(heads)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"float64 oracle (dequantize, then the definition) on {len(heads)} of {case.Hq} heads x "
+                      f"{len(rows)} query rows (every {row_stride}th) of the 16384-token causal prefill; "
+                      f"{dt:.1f} s wall"}
 
 
 def cpu_baseline_decode(x, case, nseq=64, min_seconds=5.0):
@@ -308,6 +330,13 @@ def main():
     flush_rows = flush_src.view(-1, 4096)
     flush_dst = torch.empty(flush_rows.shape[0], dtype=torch.float32, device=dev)
 
+    # the long prefill again on E4M3 inputs (both products on the fp8 matrix cores)
+    xp8 = W.prefill_inputs_fp8(pc)
+    QS8, KSP8, VSP8 = 0.25, 0.25, 0.5
+    q8, k8p, v8p = (torch.from_numpy(xp8[n]).to(dev) for n in ("q", "k", "v"))
+    o8 = torch.empty_like(o)
+    lse8 = torch.empty_like(lse)
+
     # the decode batch again, over an E4M3 cache (same q, table and lengths)
     xd8 = W.decode_inputs_fp8(dc)
     KS8, VS8 = 0.25, 0.0625
@@ -356,6 +385,9 @@ def main():
     parts = []
     if args.only in (None, "prefill"):
         parts.append(("prefill", lambda: ta.attn_fwd(q, k, v, scale=pc.scale, causal=True, out=o, lse=lse), 1))
+    if args.only in (None, "prefill_fp8"):
+        parts.append(("prefill_fp8", lambda: ta.attn_fwd_fp8(q8, k8p, v8p, QS8, KSP8, VSP8, scale=pc.scale,
+                                                             causal=True, out=o8, lse=lse8), 1))
     if args.only in (None, "decode"):
         parts.append(("decode", lambda: ta.attn_decode_paged(dq, kc, vc, bt, cl, scale=dc.scale, out=do, lse=dlse,
                                                              workspace=ws), 1))
@@ -427,11 +459,13 @@ def main():
         print(json.dumps({"only": args.only, "ms_per_call": ms}))
         return
     p_avg, d_avg, d8_avg = ms["prefill"], ms["decode"], ms["decode_fp8"]
+    p8_avg = ms["prefill_fp8"]
     a_avg, c_avg = ms["append"], ms["chunked_prefill"]
     ar_avg, cr_avg = ms["append_rope"], ms["chunked_prefill_rope"]
     a8_avg, c8_avg = ms["append_fp8"], ms["chunked_prefill_fp8"]
 
     p_tfs = pflops / (p_avg * 1e-3) / 1e12
+    p8_tfs = pflops / (p8_avg * 1e-3) / 1e12
     d_gbs = dbytes / (d_avg * 1e-3) / 1e9
     c_tfs = cflops / (c_avg * 1e-3) / 1e12
     a_gbs = abytes / (a_avg * 1e-3) / 1e9
@@ -454,7 +488,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "causal bf16 prefill B=1 Hq=32 Hkv=8 T=16384 D=128 (value) + paged bf16 decode "
+        "config": {"workload": "causal bf16 prefill B=1 Hq=32 Hkv=8 T=16384 D=128 (value; again on E4M3 inputs: "
+                               "prefill_fp8) + paged bf16 decode "
                                "B=64 Hq=12 Hkv=2 D=128 ctx~U[512,4096] block=16 (decode; again over an E4M3 cache: decode_fp8) + "
                                "chunked bf16 prefill "
                                "B=4 Hq=32 Hkv=8 D=128 prefix~U[2048,8192] chunk=1024 through the block table "
@@ -468,6 +503,13 @@ def main():
                      "frac": round(p_tfs / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic("prefill"),
                      "kernel": "prefill_kernel", "ms_per_launch": round(p_avg, 4),
                      "algorithmic_flops_per_launch": pflops},
+        "prefill_fp8": {"value": round(p8_tfs, 2), "unit": "TFLOP/s", "ms_per_call": round(p8_avg, 4),
+                        "workload": pc.name + ", E4M3 q/k/v (scales 0.25, 0.25, 0.5), bf16 output",
+                        "roofline": {"bound": "mfma", "achieved": round(p8_tfs, 2), "peak": PEAK_FP8_TFLOPS,
+                                     "unit": "TFLOP/s", "frac": round(p8_tfs / PEAK_FP8_TFLOPS, 4),
+                                     "traffic": measured_traffic("prefill_fp8"),
+                                     "kernel": "prefill_kernel (FP8 form: fp8 x fp8 products)",
+                                     "algorithmic_flops_per_launch": pflops}},
         "decode": {"value": round(d_gbs, 1), "unit": "GB/s", "us_per_call": round(d_avg * 1e3, 2),
                    "roofline": {"bound": "hbm", "achieved": round(d_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                 "frac": round(d_gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic("decode"),
@@ -526,6 +568,8 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline: float64 oracle on a sample of the prefill workload")
         out["cpu_baseline"] = cpu_baseline_prefill(xp, pc)
+        log("[bench] cpu baseline: float64 oracle on a sample of the FP8 prefill workload")
+        out["prefill_fp8"]["cpu_baseline"] = cpu_baseline_prefill_fp8(xp8, pc, QS8, KSP8, VSP8)
         log("[bench] cpu baseline: float64 oracle on a sample of the decode workload")
         out["decode"]["cpu_baseline"] = cpu_baseline_decode(xd, dc)
         log("[bench] cpu baseline: float64 oracle on the FP8 decode workload")

@@ -212,6 +212,23 @@ attn_status attn_decode_paged_fp8(const void* q, const void* k_cache, const void
                                   size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * attn_fwd_fp8: prefill attention (attn_fwd) on E4M3 inputs: q, k, v are uint8
+ * codes in attn_fwd's layouts with scales q_scale, k_scale, v_scale (finite,
+ * > 0); o is `dtype` (bf16 or fp16), lse fp32. Both products run on the fp8
+ * matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4), twice the bf16 rate; the
+ * scores are exact up to fp32 accumulation. The probabilities enter the P.V
+ * product as E4M3 values (p * 2^8 rounded to nearest; p <= 1 since the running
+ * max is kept exact), and O is divided by the fp32 sum of the unrounded p: per
+ * output element the error against attention over the dequantized inputs is
+ * at most (2^-4 + L * 2^-18) * max |v| for L visible keys, plus the output
+ * rounding. Same masking, ragged and GQA rules as attn_fwd.
+ */
+attn_status attn_fwd_fp8(const void* q, const void* k, const void* v, float q_scale, float k_scale,
+                         float v_scale, void* o, float* lse, int B, int Hq, int Hkv, int Tq, int Tk,
+                         int D, float scale, int causal, const int* seq_lens, attn_dtype dtype,
+                         hipStream_t stream);
+
+/*
  * attn_fwd_paged_fp8: the chunked prefill of attn_fwd_paged over uint8 E4M3
  * caches with scales k_scale, v_scale (as for attn_decode_paged_fp8): the
  * result is the chunked prefill of the dequantized cache. q, o stay bf16 or

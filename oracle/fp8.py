@@ -31,7 +31,7 @@ import numpy as np
 from . import oracle as O
 
 __all__ = ["E4M3_MAX", "e4m3_to_float", "float_to_e4m3", "quantize", "dequantize", "cache_append_fp8",
-           "decode_paged_fp8", "prefill_paged_fp8"]
+           "decode_paged_fp8", "prefill_paged_fp8", "prefill_fp8", "prefill_fp8_bound"]
 
 E4M3_MAX = 448.0
 
@@ -106,3 +106,19 @@ def prefill_paged_fp8(q, k_cache, v_cache, k_scale, v_scale, block_table, ctx_le
     """Chunked prefill over E4M3 caches: the chunked-prefill definition on the dequantized cache."""
     return O.prefill_paged(q, dequantize(k_cache, k_scale), dequantize(v_cache, v_scale), block_table, ctx_lens,
                            q_lens, scale, causal)
+
+
+def prefill_fp8(q8, k8, v8, q_scale, k_scale, v_scale, scale, causal=False, seq_lens=None):
+    """Prefill attention on E4M3 inputs: the prefill definition on the dequantized q, k, v."""
+    return O.prefill(dequantize(q8, q_scale), dequantize(k8, k_scale), dequantize(v8, v_scale), scale, causal,
+                     seq_lens)
+
+
+def prefill_fp8_bound(v8, v_scale, Lk):
+    """Bound on |O_fp8 - O| per (b, hq) for a computation that rounds the probabilities to E4M3 (after
+    scaling the largest to 2^8) and divides by the exact sum: each weight p_j is off by at most 2^-4 p_j
+    (normal range) or 2^-18 (subnormal range, p_j < 2^-14), and sum p_j >= 1, so
+    |dO| <= (2^-4 + L * 2^-18) * max_j |v_j| with L keys. Returns [B, Hkv] (max over each kv head's V)."""
+    vd = np.abs(dequantize(v8, v_scale))
+    vmax = np.nanmax(vd.reshape(vd.shape[0], vd.shape[1], -1), axis=2)
+    return (2.0 ** -4 + Lk * 2.0 ** -18) * vmax

@@ -13,15 +13,15 @@ import math
 import os
 
 __all__ = ["attn_fwd", "attn_decode_paged", "attn_fwd_paged", "attn_cache_append", "attn_cache_append_fp8",
-           "attn_decode_paged_fp8", "attn_fwd_paged_fp8", "attn_cache_append_rope", "attn_fwd_paged_rope",
-           "attn_decode_paged_rope", "attn_decode_workspace_bytes",
+           "attn_decode_paged_fp8", "attn_fwd_paged_fp8", "attn_fwd_fp8", "attn_cache_append_rope",
+           "attn_fwd_paged_rope", "attn_decode_paged_rope", "attn_decode_workspace_bytes",
            "attn_status_str", "attn_last_error", "AttnError", "lib", "LIB_PATH", "EXPORTS", "BLOCK_SIZE",
            "decode_workspace"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
 EXPORTS = ("attn_fwd", "attn_decode_paged", "attn_fwd_paged", "attn_cache_append", "attn_cache_append_fp8",
-           "attn_decode_paged_fp8", "attn_fwd_paged_fp8", "attn_cache_append_rope", "attn_fwd_paged_rope",
-           "attn_decode_paged_rope", "attn_decode_workspace_bytes", "attn_status_str", "attn_last_error")
+           "attn_decode_paged_fp8", "attn_fwd_paged_fp8", "attn_fwd_fp8", "attn_cache_append_rope",
+           "attn_fwd_paged_rope", "attn_decode_paged_rope", "attn_decode_workspace_bytes", "attn_status_str", "attn_last_error")
 BLOCK_SIZE = 16
 
 ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
@@ -58,6 +58,8 @@ def lib() -> ctypes.CDLL:
     L.attn_cache_append_fp8.restype = i
     L.attn_decode_paged_fp8.argtypes = [vp, vp, vp, f, f, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, sz, vp]
     L.attn_decode_paged_fp8.restype = i
+    L.attn_fwd_fp8.argtypes = [vp, vp, vp, f, f, f, vp, vp, i, i, i, i, i, i, f, i, vp, i, vp]
+    L.attn_fwd_fp8.restype = i
     L.attn_fwd_paged_fp8.argtypes = [vp, vp, vp, f, f, vp, i, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, i,
                                      vp]
     L.attn_fwd_paged_fp8.restype = i
@@ -143,6 +145,37 @@ def attn_fwd(q, k, v, scale: float | None = None, causal: bool = False, seq_lens
                and seq_lens.is_contiguous(), "seq_lens must be a contiguous int32 GPU tensor [B]")
     st = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Tq, Tk, D,
                         ctypes.c_float(scale), int(bool(causal)), _ptr(seq_lens), dt, _stream(q.device))
+    _raise(st)
+    return out, lse
+
+
+def attn_fwd_fp8(q, k, v, q_scale: float, k_scale: float, v_scale: float, scale: float | None = None,
+                 causal: bool = False, seq_lens=None, out_dtype=None, out=None, lse=None, need_lse: bool = True):
+    """Prefill attention on E4M3 inputs: q [B,Hq,Tq,D], k/v [B,Hkv,Tk,D] uint8 codes (an entry means
+    value(code) * its scale). Returns (o [B,Hq,Tq,D] in out_dtype (bfloat16 default), lse float32 or None)."""
+    import torch
+    _check(q.is_cuda and k.is_cuda and v.is_cuda, "q, k, v must be GPU tensors")
+    _check(q.dtype == torch.uint8 and k.dtype == torch.uint8 and v.dtype == torch.uint8, "q, k, v: uint8 E4M3 codes")
+    _check(q.dim() == 4 and k.dim() == 4 and v.shape == k.shape, "q, k, v must be 4-D [B,H,T,D]")
+    _check(q.is_contiguous() and k.is_contiguous() and v.is_contiguous(), "q, k, v must be contiguous")
+    B, Hq, Tq, D = q.shape
+    _check(k.shape[0] == B and k.shape[3] == D, "k/v shape mismatch")
+    Hkv, Tk = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    od = torch.bfloat16 if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((B, Hq, Tq, D), dtype=od, device=q.device)
+    dt = _dtype_code(out)
+    _check(out.shape == (B, Hq, Tq, D) and out.is_contiguous() and out.is_cuda, "bad out")
+    if need_lse and lse is None:
+        lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
+    if seq_lens is not None:
+        _check(seq_lens.is_cuda and seq_lens.dtype == torch.int32 and seq_lens.numel() == B
+               and seq_lens.is_contiguous(), "seq_lens must be a contiguous int32 GPU tensor [B]")
+    st = lib().attn_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), ctypes.c_float(q_scale), ctypes.c_float(k_scale),
+                            ctypes.c_float(v_scale), _ptr(out), _ptr(lse), B, Hq, Hkv, Tq, Tk, D, ctypes.c_float(scale),
+                            int(bool(causal)), _ptr(seq_lens), dt, _stream(q.device))
     _raise(st)
     return out, lse
 

@@ -31,8 +31,8 @@ struct PrefillArgs {
   // fp32, cosines in columns 0 .. D/2-1, sines in D/2 .. D-1
   const float* rope;
   int max_pos;
-  // E4M3 caches (fp8 paged form): an entry means code value * scale
-  float k_scale, v_scale;
+  // E4M3 inputs (fp8 forms): an entry means code value * scale
+  float k_scale, v_scale, q_scale;
 };
 
 struct AppendArgs {
@@ -80,6 +80,7 @@ constexpr int kSplitBlocks = 16;        // cache blocks per split (256 tokens)
 hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int D, bool causal, hipStream_t stream);
 hipError_t launch_prefill_paged(const PrefillArgs& a, bool bf16, int D, bool causal, hipStream_t stream);
 hipError_t launch_prefill_paged_fp8(const PrefillArgs& a, bool bf16, int D, bool causal, hipStream_t stream);
+hipError_t launch_prefill_fp8(const PrefillArgs& a, bool bf16, int D, bool causal, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_append_fp8(const AppendArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_append_rope(const AppendArgs& a, bool bf16, hipStream_t stream);

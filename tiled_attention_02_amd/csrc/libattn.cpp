@@ -302,6 +302,51 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
   return ok();
 }
 
+attn_status attn_fwd_fp8(const void* q, const void* k, const void* v, float q_scale, float k_scale, float v_scale,
+                         void* o, float* lse, int B, int Hq, int Hkv, int Tq, int Tk, int D, float scale, int causal,
+                         const int* seq_lens, attn_dtype dtype, hipStream_t stream) {
+  const char* fn = "attn_fwd_fp8";
+  if (!q || !k || !v || !o) return fail(ATTN_ERR_INVALID, "%s: q, k, v and o must be non-null", fn);
+  if (B < 1 || Hq < 1 || Hkv < 1 || Tq < 1 || Tk < 1 || D < 1)
+    return fail(ATTN_ERR_INVALID, "%s: sizes must be >= 1", fn);
+  if (Hq % Hkv != 0) return fail(ATTN_ERR_INVALID, "%s: Hq=%d is not a multiple of Hkv=%d", fn, Hq, Hkv);
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, (int)dtype);
+  if (D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "%s: head size D=%d (supported: 64, 128)", fn, D);
+  if (!isfinite(scale)) return fail(ATTN_ERR_INVALID, "%s: scale must be finite", fn);
+  if (!(isfinite(q_scale) && isfinite(k_scale) && isfinite(v_scale) && q_scale > 0.f && k_scale > 0.f &&
+        v_scale > 0.f))
+    return fail(ATTN_ERR_INVALID, "%s: q_scale, k_scale and v_scale must be finite and > 0", fn);
+  if (seq_lens && Tq != Tk) return fail(ATTN_ERR_INVALID, "%s: seq_lens requires Tq == Tk (got %d, %d)", fn, Tq, Tk);
+  const double nq = (double)B * Hq * Tq * D, nk = (double)B * Hkv * Tk * D;
+  if (nq >= 2147483648.0 || nk >= 2147483648.0)
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: tensors must hold fewer than 2^31 elements", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(ATTN_ERR_INVALID, "%s: q, k, v and o must be 16-byte aligned", fn);
+  if ((lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) || (seq_lens && (reinterpret_cast<uintptr_t>(seq_lens) & 3u)))
+    return fail(ATTN_ERR_INVALID, "%s: lse / seq_lens must be 4-byte aligned", fn);
+
+  attn::PrefillArgs a = {};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.seq_lens = seq_lens;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Tq = Tq;
+  a.Tk = Tk;
+  a.G = Hq / Hkv;
+  a.q_scale = q_scale;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  scale_mode(scale, &a.c, &a.qmode);
+  hipError_t e = attn::launch_prefill_fp8(a, dtype == ATTN_BF16, D, causal != 0, stream);
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_blocks_per_seq, int block_size) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_blocks_per_seq < 1 || block_size != attn::kDecodeBlock ||
       (D != 64 && D != 128))

@@ -49,6 +49,16 @@
 // while tile j is consumed. LDS operand reads are issued ahead of the MFMAs
 // that consume them (register double buffering).
 //
+// FP8 form (contiguous E4M3 q, k, v; KV8 without PAGED): both products run on
+// v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales), twice the bf16 rate.
+// A lane's 32 contraction slots are 32 consecutive dims of its row for S^T,
+// and for O^T += V^T P^T the lane's own 32 keys of the tile (the B operand P^T
+// is the lane's 32 probabilities, rounded to E4M3 after scaling by 2^8; the
+// A operand V^T is 4 ds_read_b64_tr_b8 in the same key order). The running
+// max is exact (no lazy margin) so the scaled p stay <= 2^8; O is divided by
+// the fp32 sum of the unrounded scaled p. Error of the rounding of P: at most
+// (2^-4 + L * 2^-18) * max |v| per output element for L keys.
+//
 // E4M3 form (chunked prefill over an FP8 cache, paged only): K/V tiles hold
 // one byte per element; operand fragments are converted to the 16-bit type
 // right after their LDS reads (exact), k_scale folds into the exponent factor
@@ -187,10 +197,29 @@ __device__ __forceinline__ int q_col(int s, int h) {
   return KV8 ? 32 * (s >> 1) + 16 * h + 8 * (s & 1) : 16 * s + 8 * h;
 }
 
-template <class T, int D, bool KV8>
+template <class T, int D, bool KV8, bool F8 = false>
 __device__ __forceinline__ void load_q(Acc<D>& st, const Geo& g, int qmode, int qrow, int h, const float* rope,
-                                       int max_pos) {
+                                       int max_pos, const uint8_t* q8 = nullptr) {
   const bool live = qrow < g.Lq;
+  if constexpr (F8) {
+    // k-step p (64 dims): lane half h holds dims 64p + 32h .. +32 (32 codes)
+    const uint32_t flip8 = qmode == 1 ? 0x80808080u : 0u;
+    const bool zero8 = qmode == 2 || !live;
+    const uint8_t* src8 = q8 + (size_t)(live ? qrow : 0) * D + 32 * h;
+#pragma unroll
+    for (int p = 0; p < D / 64; ++p)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(src8 + 64 * p + 16 * u) ^ flip8;
+        st.qf[2 * p + u] = zero8 ? u32x4{0, 0, 0, 0} : x;
+      }
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) st.oacc[i] = f32x16{};
+    st.m = -__builtin_inff();
+    st.l = 0.f;
+    st.lr = 0.f;
+    return;
+  }
   const uint32_t flip = qmode == 1 ? 0x80008000u : 0u;
   const bool zero = qmode == 2 || !live;
   const uint16_t* src = g.Qg + (size_t)(live ? qrow : 0) * D;
@@ -231,14 +260,22 @@ struct Offs {
   int v[D / 32][2];
 };
 
-template <int D, int BK, bool KV8>
+template <int D, int BK, bool KV8, bool F8 = false>
 __device__ __forceinline__ void make_offs(Offs<D, BK>& o, int lane) {
   using S = Shape<D, BK, KV8>;
   const int h = lane >> 5, c32 = lane & 31, g16 = lane >> 4, i16 = lane & 15;
   if constexpr (KV8) {
-    // K: k-steps 2p, 2p + 1 from one 16-byte read of row c32 at chunk 2p + h
+    if constexpr (F8) {
+      // K: 64-dim step p from two 16-byte reads of row c32 at chunks 4p + 2h, +1
 #pragma unroll
-    for (int p = 0; p < S::KS / 2; ++p) o.k[p] = c32 * S::RB + 16 * ((2 * p + h) ^ kswz8<D>(c32));
+      for (int p = 0; p < D / 64; ++p)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) o.k[2 * p + u] = c32 * S::RB + 16 * ((4 * p + 2 * h + u) ^ kswz8<D>(c32));
+    } else {
+      // K: k-steps 2p, 2p + 1 from one 16-byte read of row c32 at chunk 2p + h
+#pragma unroll
+      for (int p = 0; p < S::KS / 2; ++p) o.k[p] = c32 * S::RB + 16 * ((2 * p + h) ^ kswz8<D>(c32));
+    }
     // V^T via ds_read_b64_tr_b8: in each 16-lane group, lane j receives byte
     // (j & 7) of the 8 bytes read by lanes 2e + (j >> 3). Element e of lane
     // half h is key 8(e >> 2) + 4h + (e & 3) of the k-step (P^T's order), so
@@ -280,10 +317,35 @@ __device__ __forceinline__ void make_offs(Offs<D, BK>& o, int lane) {
 // directives: callers add the pattern they want.
 constexpr int kQkDepth = 2;
 
-template <class T, int D, int BK, bool KV8 = false>
+// fp8 x fp8 -> fp32, 32x32x64, unit block scales (E8M0 127 = 2^0)
+__device__ __forceinline__ f32x16 mfma_f8(u32x4 a0, u32x4 a1, u32x4 b0, u32x4 b1, f32x16 c) {
+  typedef int i32x8 __attribute__((ext_vector_type(8)));
+  const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+  const i32x8 b = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0x7f7f7f7f, 0, 0x7f7f7f7f);
+}
+
+template <class T, int D, int BK, bool KV8 = false, bool F8 = false>
 __device__ __forceinline__ void tile_qk_plain(f32x16 (&sacc)[BK / 32], const char* Ks, const Offs<D, BK>& o,
                                               const Acc<D>& st) {
   using S = Shape<D, BK, KV8>;
+  if constexpr (F8) {
+    u32x4 fr[D / 64][S::KB][2];
+#pragma unroll
+    for (int p = 0; p < D / 64; ++p)
+#pragma unroll
+      for (int kb = 0; kb < S::KB; ++kb)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) fr[p][kb][u] = *reinterpret_cast<const u32x4*>(Ks + kb * 32 * S::RB + o.k[2 * p + u]);
+#pragma unroll
+    for (int kb = 0; kb < S::KB; ++kb) {
+      sacc[kb] = f32x16{};
+#pragma unroll
+      for (int p = 0; p < D / 64; ++p)
+        sacc[kb] = mfma_f8(fr[p][kb][0], fr[p][kb][1], st.qf[2 * p], st.qf[2 * p + 1], sacc[kb]);
+    }
+    return;
+  }
   if constexpr (KV8) {
     // one 16-byte read per (key block, k-step pair) = the two steps' fragments
     // as 16 codes; the next pair's reads go out before this pair's MFMAs
@@ -330,11 +392,11 @@ __device__ __forceinline__ void tile_qk_plain(f32x16 (&sacc)[BK / 32], const cha
   }
 }
 
-template <class T, int D, int BK, bool KV8 = false>
+template <class T, int D, int BK, bool KV8 = false, bool F8 = false>
 __device__ __forceinline__ void tile_qk(f32x16 (&sacc)[BK / 32], const char* Ks, const Offs<D, BK>& o,
                                         const Acc<D>& st) {
   using S = Shape<D, BK>;
-  tile_qk_plain<T, D, BK, KV8>(sacc, Ks, o, st);
+  tile_qk_plain<T, D, BK, KV8, F8>(sacc, Ks, o, st);
   if constexpr (KV8) return;  // compiler-scheduled
   // schedule: the reads of step s+DEPTH go out before the MFMAs of step s
   __builtin_amdgcn_sched_group_barrier(0x100, kQkDepth * S::KB, 0);
@@ -362,10 +424,25 @@ __device__ __forceinline__ u32x4 vt_frag(const char* Vs, const Offs<D, BK>& o, i
 
 // O^T += V^T P^T for one tile in LDS; fragments of k-step s+1 are read while
 // the DB independent MFMAs of step s run.
-template <class T, int D, int BK, bool KV8 = false>
+template <class T, int D, int BK, bool KV8 = false, bool F8 = false>
 __device__ __forceinline__ void tile_pv(Acc<D>& st, const u32x4 (&pf)[BK / 16], const char* Vs,
                                         const Offs<D, BK>& o) {
   using S = Shape<D, BK>;
+  if constexpr (F8) {
+    static_assert(BK == 64, "one 64-key product per tile");
+    // V^T: the lane's 32 keys of the tile in P^T's byte order (4 transposing reads)
+#pragma unroll
+    for (int db = 0; db < S::DB; ++db) {
+      u32x2 v[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        v[t] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                                             (lds_i32x2*)(Vs + 16 * t * D + o.v[db][0])));
+      st.oacc[db] = mfma_f8(u32x4{v[0][0], v[0][1], v[1][0], v[1][1]}, u32x4{v[2][0], v[2][1], v[3][0], v[3][1]},
+                            pf[0], pf[1], st.oacc[db]);
+    }
+    return;
+  }
   u32x4 fr[2][S::DB];
 #pragma unroll
   for (int db = 0; db < S::DB; ++db) fr[0][db] = vt_frag<T, D, BK, KV8>(Vs, o, db, 0);
@@ -383,9 +460,11 @@ __device__ __forceinline__ void tile_pv(Acc<D>& st, const u32x4 (&pf)[BK / 16], 
 // Mask and online-softmax statistics for one tile of scores: the tile max,
 // and the (lazy) rescale of the running sums and of O. Returns the max to
 // subtract in the exponentials.
-template <class T, int D, int BK, bool CAUSAL>
+template <class T, int D, int BK, bool CAUSAL, bool F8 = false>
 __device__ __forceinline__ float softmax_stats(f32x16 (&sacc)[BK / 32], Acc<D>& st, const Geo& g, int k0, int qrow,
                                                int w_lo, int h, float cexp) {
+  // FP8 form: the max moves whenever it grows, so the scaled p stay <= 2^8
+  constexpr float kMargin = F8 ? 0.f : kLazyRescale;
   using S = Shape<D, BK>;
   const bool need_mask = (k0 + BK > g.Lk) || (CAUSAL && k0 + BK - 1 > w_lo + g.off);
   if (need_mask) {
@@ -406,7 +485,7 @@ __device__ __forceinline__ float softmax_stats(f32x16 (&sacc)[BK / 32], Acc<D>& 
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
   mx = half_swap_max(mx) * cexp;  // -inf stays -inf (cexp > 0)
   // lazy rescale: move m only when the max grows by more than the margin
-  const bool grow = mx > st.m + kLazyRescale;
+  const bool grow = mx > st.m + kMargin;
   if (__builtin_amdgcn_ballot_w64(grow)) {
     const float m_new = grow ? mx : st.m;
     const float alpha = grow ? fast_exp2(st.m - m_new) : 1.f;  // m = -inf -> 0
@@ -420,10 +499,30 @@ __device__ __forceinline__ float softmax_stats(f32x16 (&sacc)[BK / 32], Acc<D>& 
 }
 
 // p = 2^(s*c - m), the two running sums, and the P^T operand (no branches).
-template <class T, int D, int BK>
+template <class T, int D, int BK, bool F8 = false>
 __device__ __forceinline__ void softmax_exp(const f32x16 (&sacc)[BK / 32], u32x4 (&pf)[BK / 16], Acc<D>& st,
                                             float msub, float cexp) {
   using S = Shape<D, BK>;
+  if constexpr (F8) {
+    // p * 2^8 (<= 2^8), rounded to E4M3: byte 16 kb + r of the lane's P^T
+    // operand is key kb*32 + 8(r/4) + 4h + r%4, as in the scores' layout
+    float ls = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < S::KB; ++kb)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        float p[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[e] = fast_exp2(__builtin_fmaf(sacc[kb][4 * w + e], cexp, 8.f - msub));
+        ls += (p[0] + p[1]) + (p[2] + p[3]);
+        int r = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+        r = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], r, true);
+        pf[kb][w] = (uint32_t)r;
+      }
+    st.l += ls;
+    st.lr = st.l;
+    return;
+  }
   // one partial sum per 8 probabilities keeps the dependency chains short, so
   // the work interleaves with the matrix instructions of the next tile
   float lsum[S::PS], lrsum[S::PS];
@@ -454,7 +553,7 @@ __device__ __forceinline__ void softmax_exp(const f32x16 (&sacc)[BK / 32], u32x4
 // O = O^T / l, lse = (m + log2 l) ln 2; padding rows -> 0, -inf.
 template <class T, int D>
 __device__ __forceinline__ void epilogue(const Acc<D>& st, const Geo& g, int Tq, int qrow, int h,
-                                         float vscale = 1.f) {
+                                         float vscale = 1.f, float lse_shift = 0.f) {
   const float l_tot = half_swap_sum(st.l);
   const float lr_tot = half_swap_sum(st.lr);
   if (qrow >= Tq) return;
@@ -469,7 +568,7 @@ __device__ __forceinline__ void epilogue(const Acc<D>& st, const Geo& g, int Tq,
                   T::pack2(st.oacc[db][4 * q4 + 2] * inv, st.oacc[db][4 * q4 + 3] * inv)};
       *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * q4) = pk;
     }
-  if (g.Lg && h == 0) g.Lg[qrow] = has ? (st.m + fast_log2(l_tot)) * kLn2 : -__builtin_inff();
+  if (g.Lg && h == 0) g.Lg[qrow] = has ? (st.m + fast_log2(l_tot) - lse_shift) * kLn2 : -__builtin_inff();
 }
 
 // Global -> LDS staging of K or V tiles (row-major, swizzled) with buffer
@@ -602,7 +701,7 @@ __device__ __forceinline__ void staged_barrier() {
 //     the wavefront work at the same time;
 //   * accumulates O^T += V^T P^T for tile kt (MFMA);
 // and ends with the wait for its loads and a barrier.
-template <class T, int D, int BK, bool CAUSAL, bool KV8, class KStg, class VStg>
+template <class T, int D, int BK, bool CAUSAL, bool KV8, bool F8, class KStg, class VStg>
 __device__ __forceinline__ void pipe_step(int kt, const char* kcur, const char* vcur, char* kload, char* vload,
                                           f32x16 (&s_cur)[BK / 32], f32x16 (&s_nxt)[BK / 32],
                                           const KStg& ks, const VStg& vs,
@@ -628,11 +727,11 @@ __device__ __forceinline__ void pipe_step(int kt, const char* kcur, const char* 
   const bool work_next = kt + 1 < g.nkt && wave_live && (!CAUSAL || (kt + 1) * BK <= w_last);
   if (work) {
     u32x4 pf[S::PS];
-    const float msub = softmax_stats<T, D, BK, CAUSAL>(s_cur, st, g, kt * BK, qrow, w_lo, h, cexp);
+    const float msub = softmax_stats<T, D, BK, CAUSAL, F8>(s_cur, st, g, kt * BK, qrow, w_lo, h, cexp);
     if (work_next && KV8) {
-      // E4M3 tiles: the compiler schedules the converted reads and the exponentials
-      tile_qk_plain<T, D, BK, KV8>(s_nxt, kcur, o, st);
-      softmax_exp<T, D, BK>(s_cur, pf, st, msub, cexp);
+      // E4M3 tiles: the compiler schedules the reads and the exponentials
+      tile_qk_plain<T, D, BK, KV8, F8>(s_nxt, kcur, o, st);
+      softmax_exp<T, D, BK, F8>(s_cur, pf, st, msub, cexp);
     } else if (work_next) {
       tile_qk_plain<T, D, BK>(s_nxt, kcur, o, st);
       softmax_exp<T, D, BK>(s_cur, pf, st, msub, cexp);
@@ -652,10 +751,10 @@ __device__ __forceinline__ void pipe_step(int kt, const char* kcur, const char* 
         }
       }
     } else {
-      softmax_exp<T, D, BK>(s_cur, pf, st, msub, cexp);
+      softmax_exp<T, D, BK, F8>(s_cur, pf, st, msub, cexp);
     }
     __builtin_amdgcn_s_setprio(2);
-    tile_pv<T, D, BK, KV8>(st, pf, vcur, o);
+    tile_pv<T, D, BK, KV8, F8>(st, pf, vcur, o);
     __builtin_amdgcn_s_setprio(0);
   }
   staged_barrier();
@@ -665,7 +764,8 @@ __device__ __forceinline__ void pipe_step(int kt, const char* kcur, const char* 
 // 4 wavefronts x 32 rows, pipelined key steps over double-buffered K and V.
 template <class T, int D, int BQ, int BK, bool CAUSAL, bool PAGED, bool KV8>
 __global__ __launch_bounds__(BQ * 2, 2) void prefill_kernel(PrefillArgs a) {
-  static_assert(PAGED || !KV8, "E4M3 tiles come from the paged cache");
+  // E4M3 tiles: from the paged cache (16-bit products), or, contiguous, the FP8 form
+  constexpr bool F8 = KV8 && !PAGED;
   using S = Shape<D, BK, KV8>;
   constexpr int THREADS = (BQ / 32) * 64;
   // K of tile t lives in kb[t & 1], V of tile t in vb[t & 1]; separate LDS
@@ -683,15 +783,16 @@ __global__ __launch_bounds__(BQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   const int w_lo = g.q_lo + w * 32;
   const int qrow = w_lo + (lane & 31);
   Acc<D> st;
-  load_q<T, D, KV8>(st, g, a.qmode, qrow, h, PAGED ? a.rope : nullptr, a.max_pos);
+  load_q<T, D, KV8, F8>(st, g, a.qmode, qrow, h, PAGED ? a.rope : nullptr, a.max_pos,
+                        static_cast<const uint8_t*>(a.q) + (size_t)(g.b * a.Hq + g.hq) * a.Tq * D);
   Offs<D, BK> o;
-  make_offs<D, BK, KV8>(o, lane);
+  make_offs<D, BK, KV8, F8>(o, lane);
   using KStg = Stager<D, BK, THREADS, PAGED, KV8, false>;
   using VStg = Stager<D, BK, THREADS, PAGED, KV8, true>;
   KStg ks;
   VStg vs;
-  // E4M3 caches: k_scale multiplies every score, v_scale every value
-  const float cexp = KV8 ? a.c * a.k_scale : a.c;
+  // E4M3 inputs: the scales multiply every score (q_scale k_scale) and every value (v_scale)
+  const float cexp = KV8 ? a.c * a.k_scale * (F8 ? a.q_scale : 1.f) : a.c;
   if constexpr (PAGED) {
     // byte offsets: kv head kvh of physical block 0, and one physical block
     const size_t head = (size_t)g.kvh * 16 * S::RB, bstride = (size_t)a.Hkv * 16 * S::RB;
@@ -701,6 +802,10 @@ __global__ __launch_bounds__(BQ * 2, 2) void prefill_kernel(PrefillArgs a) {
     const int* trow = a.table + (size_t)g.b * a.max_blocks;
     for (int i = tid; i < nb; i += THREADS) tbl[i] = min(max(trow[i], 0), a.num_blocks - 1);
     __syncthreads();
+  } else if constexpr (F8) {
+    const size_t head = (size_t)(g.b * a.Hkv + g.kvh) * a.Tk * D;  // bytes: 1 per element
+    ks.init(static_cast<const char*>(a.k) + head, tid);
+    vs.init(static_cast<const char*>(a.v) + head, tid);
   } else {
     ks.init(reinterpret_cast<const char*>(g.Kg), tid);
     vs.init(reinterpret_cast<const char*>(g.Vg), tid);
@@ -721,15 +826,15 @@ __global__ __launch_bounds__(BQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   const bool wave_live = w_lo < g.Lq;
   const int w_last = min(w_lo + 31, g.Lq - 1) + g.off;  // last key any row of this wavefront sees
   f32x16 s0[S::KB], s1[S::KB];
-  if (g.nkt > 0 && wave_live && (!CAUSAL || 0 <= w_last)) tile_qk<T, D, BK, KV8>(s0, kb0, o, st);
+  if (g.nkt > 0 && wave_live && (!CAUSAL || 0 <= w_last)) tile_qk<T, D, BK, KV8, F8>(s0, kb0, o, st);
   for (int kt = 0; kt < g.nkt; kt += 2) {
-    pipe_step<T, D, BK, CAUSAL, KV8>(kt, kb1, vb0, kb0, vb1, s0, s1, ks, vs, ecar, st, o, g, wave_live, w_last,
-                                     w_lo, qrow, h, cexp);
+    pipe_step<T, D, BK, CAUSAL, KV8, F8>(kt, kb1, vb0, kb0, vb1, s0, s1, ks, vs, ecar, st, o, g, wave_live, w_last,
+                                         w_lo, qrow, h, cexp);
     if (kt + 1 < g.nkt)
-      pipe_step<T, D, BK, CAUSAL, KV8>(kt + 1, kb0, vb1, kb1, vb0, s1, s0, ks, vs, ecar, st, o, g, wave_live,
-                                       w_last, w_lo, qrow, h, cexp);
+      pipe_step<T, D, BK, CAUSAL, KV8, F8>(kt + 1, kb0, vb1, kb1, vb0, s1, s0, ks, vs, ecar, st, o, g, wave_live,
+                                           w_last, w_lo, qrow, h, cexp);
   }
-  epilogue<T, D>(st, g, a.Tq, qrow, h, KV8 ? a.v_scale : 1.f);
+  epilogue<T, D>(st, g, a.Tq, qrow, h, KV8 ? a.v_scale : 1.f, F8 ? 8.f : 0.f);
 }
 
 // ---------------------------------------------------------------------------
@@ -763,6 +868,10 @@ hipError_t launch_prefill_paged(const PrefillArgs& a, bool bf16, int D, bool cau
 
 hipError_t launch_prefill_paged_fp8(const PrefillArgs& a, bool bf16, int D, bool causal, hipStream_t stream) {
   return bf16 ? launch_t<BF16, true, true>(a, D, causal, stream) : launch_t<F16, true, true>(a, D, causal, stream);
+}
+
+hipError_t launch_prefill_fp8(const PrefillArgs& a, bool bf16, int D, bool causal, hipStream_t stream) {
+  return bf16 ? launch_t<BF16, false, true>(a, D, causal, stream) : launch_t<F16, false, true>(a, D, causal, stream);
 }
 
 }  // namespace attn

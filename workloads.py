@@ -232,6 +232,20 @@ def rope_table(max_pos: int, D: int, base: float = 500000.0) -> np.ndarray:
     return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
 
 
+def prefill_inputs_fp8(case: PrefillCase, Tq: int | None = None, Tk: int | None = None):
+    """prefill_inputs' shapes and ragged lengths with E4M3 codes for q, k, v (e4m3_codes, generator seeded
+    with seed + 2000); padding positions (>= seq_lens[b]) hold the NaN code."""
+    x = prefill_inputs(case, nan_padding=True, Tq=Tq, Tk=Tk)
+    rng = np.random.default_rng(case.seed + 2000)
+    out = {}
+    for n in ("q", "k", "v"):
+        c = e4m3_codes(rng, x[n].shape)
+        c[np.isnan(x[n])] = E4M3_NAN
+        out[n] = c
+    out["seq_lens"] = x["seq_lens"]
+    return out
+
+
 def chunk_inputs(case: ChunkCase, nan_fill: bool = False, starts=None, lens=None):
     """Return dict(q, k_new, v_new, k_cache, v_cache, block_table, start_pos, new_lens, ctx_lens).
 
