@@ -2,7 +2,7 @@
 
 Reference: the float64 prefill definition on the dequantized inputs (oracle/fp8.py). The kernel rounds
 the probabilities to E4M3 for the P.V product, so the tolerance is the bound that rounding allows (derived
-in oracle/fp8.prefill_fp8_bound): per output element |dO| <= (2^-4 + L * 2^-18) * max |v| of the kv
+in oracle/fp8.prefill_fp8_bound): per output element |dO| <= (2^-4 + L * 2^-17) * max |v| of the kv
 head, plus one unit in the last place of the output type; lse (computed from the unrounded
 probabilities and the fp32 scores) within 1e-4 * max(1, |lse|); padded rows exactly 0 / -inf. The mean
 error, far below the bound, is printed for each case.

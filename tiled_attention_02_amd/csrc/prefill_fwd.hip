@@ -53,11 +53,12 @@
 // v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales), twice the bf16 rate.
 // A lane's 32 contraction slots are 32 consecutive dims of its row for S^T,
 // and for O^T += V^T P^T the lane's own 32 keys of the tile (the B operand P^T
-// is the lane's 32 probabilities, rounded to E4M3 after scaling by 2^8; the
+// is the lane's 32 probabilities, rounded to E4M3 after scaling by 2^7; the
 // A operand V^T is 4 ds_read_b64_tr_b8 in the same key order). The running
-// max is exact (no lazy margin) so the scaled p stay <= 2^8; O is divided by
-// the fp32 sum of the unrounded scaled p. Error of the rounding of P: at most
-// (2^-4 + L * 2^-18) * max |v| per output element for L keys.
+// max moves once it grows by more than 1 (log2), so p <= 2 and the scaled p
+// stay <= 2^8; O is divided by the fp32 sum of the unrounded scaled p. Error
+// of the rounding of P: at most (2^-4 + L * 2^-17) * max |v| per output
+// element for L keys.
 //
 // E4M3 form (chunked prefill over an FP8 cache, paged only): K/V tiles hold
 // one byte per element; operand fragments are converted to the 16-bit type
@@ -74,6 +75,9 @@
 namespace attn {
 
 constexpr float kLazyRescale = 8.0f;
+// FP8 form: lazy margin of the running max and the matching scale 2^(8 - margin) of p
+constexpr float kF8Margin = 1.0f;
+constexpr float kF8PScaleLog2 = 8.0f - kF8Margin;
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -463,8 +467,9 @@ __device__ __forceinline__ void tile_pv(Acc<D>& st, const u32x4 (&pf)[BK / 16], 
 template <class T, int D, int BK, bool CAUSAL, bool F8 = false>
 __device__ __forceinline__ float softmax_stats(f32x16 (&sacc)[BK / 32], Acc<D>& st, const Geo& g, int k0, int qrow,
                                                int w_lo, int h, float cexp) {
-  // FP8 form: the max moves whenever it grows, so the scaled p stay <= 2^8
-  constexpr float kMargin = F8 ? 0.f : kLazyRescale;
+  // FP8 form: the max moves once it grows by more than 1 (log2 units), so
+  // p <= 2 and the scaled p * 2^7 stay <= 2^8, inside E4M3's range
+  constexpr float kMargin = F8 ? kF8Margin : kLazyRescale;
   using S = Shape<D, BK>;
   const bool need_mask = (k0 + BK > g.Lk) || (CAUSAL && k0 + BK - 1 > w_lo + g.off);
   if (need_mask) {
@@ -504,7 +509,7 @@ __device__ __forceinline__ void softmax_exp(const f32x16 (&sacc)[BK / 32], u32x4
                                             float msub, float cexp) {
   using S = Shape<D, BK>;
   if constexpr (F8) {
-    // p * 2^8 (<= 2^8), rounded to E4M3: byte 16 kb + r of the lane's P^T
+    // p * 2^7 (<= 2^8), rounded to E4M3: byte 16 kb + r of the lane's P^T
     // operand is key kb*32 + 8(r/4) + 4h + r%4, as in the scores' layout
     float ls = 0.f;
 #pragma unroll
@@ -513,7 +518,7 @@ __device__ __forceinline__ void softmax_exp(const f32x16 (&sacc)[BK / 32], u32x4
       for (int w = 0; w < 4; ++w) {
         float p[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) p[e] = fast_exp2(__builtin_fmaf(sacc[kb][4 * w + e], cexp, 8.f - msub));
+        for (int e = 0; e < 4; ++e) p[e] = fast_exp2(__builtin_fmaf(sacc[kb][4 * w + e], cexp, kF8PScaleLog2 - msub));
         ls += (p[0] + p[1]) + (p[2] + p[3]);
         int r = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
         r = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], r, true);
@@ -834,7 +839,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void prefill_kernel(PrefillArgs a) {
       pipe_step<T, D, BK, CAUSAL, KV8, F8>(kt + 1, kb0, vb1, kb1, vb0, s1, s0, ks, vs, ecar, st, o, g, wave_live,
                                            w_last, w_lo, qrow, h, cexp);
   }
-  epilogue<T, D>(st, g, a.Tq, qrow, h, KV8 ? a.v_scale : 1.f, F8 ? 8.f : 0.f);
+  epilogue<T, D>(st, g, a.Tq, qrow, h, KV8 ? a.v_scale : 1.f, F8 ? kF8PScaleLog2 : 0.f);
 }
 
 // ---------------------------------------------------------------------------
