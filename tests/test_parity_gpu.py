@@ -304,3 +304,48 @@ def test_decode_explicit_workspace_reused_across_shapes(ta):
         torch.cuda.synchronize()
         o_ref, lse_ref = O.decode_paged(x["q"], x["k_cache"], x["v_cache"], x["block_table"], x["ctx_lens"], c.scale)
         _compare(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, c.dtype, what=c.name)
+
+
+# ---------------------------------------------------------------- large batch, graph replays
+def test_decode_large_batch(ta):
+    """8200 sequences (16400 (sequence, kv head) pairs, grid z = 8200): most contexts are short (one
+    256-token range), every 64th spans up to three ranges."""
+    case = W.DecodeCase("many-seq", B=8200, Hq=4, Hkv=2, D=64, dtype="bf16", ctx_lo=1, ctx_hi=700, seed=45)
+    rng = np.random.default_rng(46)
+    ctx = rng.integers(1, 48, case.B)
+    ctx[::64] = rng.integers(257, 701, len(ctx[::64]))
+    _decode_check(ta, case, ctx_lens=ctx, what="decode B=8200")
+
+
+def test_decode_graph_replays(ta):
+    """attn_decode_paged captured into a HIP graph on a side stream, replayed several times with new
+    queries and eager calls on the default stream in between; every replay equals the eager result bit
+    for bit and the oracle to tolerance."""
+    import torch
+    case = W.DecodeCase("graph", B=16, Hq=12, Hkv=2, D=128, dtype="bf16", ctx_lo=300, ctx_hi=3000, seed=47)
+    x = W.decode_inputs(case, nan_fill=True)
+    kc = _dev(x["k_cache"], case.dtype)
+    vc = _dev(x["v_cache"], case.dtype)
+    bt = torch.from_numpy(x["block_table"]).cuda()
+    cl = torch.from_numpy(x["ctx_lens"]).cuda()
+    q = _dev(x["q"], case.dtype)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        o_g, lse_g = ta.attn_decode_paged(q, kc, vc, bt, cl, scale=case.scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(48)
+    for rep in range(4):
+        qn = W.round_to(rng.standard_normal(x["q"].shape, dtype=np.float32), case.dtype)
+        q.copy_(_dev(qn, case.dtype))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        o_e, lse_e = ta.attn_decode_paged(q, kc, vc, bt, cl, scale=case.scale)
+        torch.cuda.synchronize()
+        _note(f"[case] graph replay {rep}")
+        assert torch.equal(o_g, o_e) and torch.equal(lse_g, lse_e), f"replay {rep} differs from eager"
+        o_ref, lse_ref = O.decode_paged(qn, x["k_cache"], x["v_cache"], x["block_table"], x["ctx_lens"], case.scale)
+        _compare(o_g.float().cpu().numpy(), lse_g.cpu().numpy(), o_ref, lse_ref, case.dtype,
+                 what=f"graph replay {rep}")

@@ -14,7 +14,7 @@
 //
 // Decomposition: one wavefront per (split of 256 tokens = 16 cache blocks,
 // kv head, sequence). It streams its blocks two at a time (a step of 32
-// tokens) with the next step's loads in flight, and serves all G = Hq/Hkv
+// tokens) through one 16 KiB LDS buffer, and serves all G = Hq/Hkv
 // query heads of the kv head from one read of each block:
 //   S^T = K Q^T       v_mfma_f32_16x16x32: rows = 16 tokens of a block,
 //                     columns = query heads (G <= 16, the rest zero).
@@ -58,7 +58,7 @@ template <int D, bool KV8>
 struct StepLds {
   // cache blocks per step; 4 for the E4M3 cache (the same 16 KiB per step as
   // the 16-bit one) measured slower: twice the LDS per wavefront halves the
-  // wavefronts a CU keeps in flight
+  // wavefronts a CU keeps resident
   static constexpr int NB = 2;
   static constexpr int EB = KV8 ? 1 : 2;     // bytes per cache element
   static constexpr int RB = EB * D;          // bytes per token row
@@ -67,7 +67,6 @@ struct StepLds {
   static constexpr int RPI = 1024 / RB;      // rows filled by one wavefront load instruction
   static constexpr int NI = 16 / RPI;        // load instructions per block
   static constexpr int C8 = RB / 16;         // 16-byte chunks per row
-  static constexpr int LOADS = 2 * NB * NI;  // load instructions per step
 };
 
 // 16-bit cache: one swizzle for K and V. K reads: 16 rows at one chunk per
@@ -160,8 +159,7 @@ __device__ __forceinline__ void make_dec_offs(DecOffs<D, KV8>& o, int lane) {
 // buffer: buffer loads that write LDS directly, each instruction 1 KiB of
 // consecutive bytes of one block (whole rows). ph[j] is block j's physical
 // block; a block past the sequence's last one carries the step's first block
-// instead (a cache hit: every token there is masked or zeroed anyway), which
-// keeps the number of loads per step fixed for the in-order memory counter.
+// instead (a cache hit: every token there is masked or zeroed anyway).
 template <int D, bool KV8>
 __device__ __forceinline__ void load_step(char* buf, const char* kbase, const char* vbase, size_t block_stride,
                                           const int (&ph)[StepLds<D, KV8>::NB], const DecOffs<D, KV8>& o) {
@@ -306,6 +304,11 @@ __device__ __forceinline__ void step_compute(WaveState<D>& st, char* buf, const 
   }
 }
 
+// One step buffer per wavefront (16 KiB at D = 128), loaded after the previous
+// step's reads: ten wavefronts per CU stay resident, so every workgroup of a
+// typical batch starts at once and the memory system has far more than the
+// bytes in flight it needs. A second buffer (the next step's loads in flight
+// during the math) halves the resident wavefronts and measured 4 % slower.
 template <class T, int D, bool KV8>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   using L = StepLds<D, KV8>;
@@ -314,14 +317,17 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   constexpr int NB = L::NB;
   constexpr int NS = kSplitBlocks / NB;  // steps per split
   static_assert(D == 128 || D == 64, "head size");
-  // two step buffers, separate LDS arrays so that reads of one are never
-  // ordered behind the loads into the other
-  __shared__ __align__(16) char buf0[L::BYTES];
-  __shared__ __align__(16) char buf1[L::BYTES];
+  __shared__ __align__(16) char buf[L::BYTES];
 
-  const int split = blockIdx.x;
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
+  // Workgroups reach the XCDs round-robin in launch order, so blockIdx.x
+  // alone would pick the XCD (the grid's x extent is a multiple of 8 in
+  // practice), and split 0 of every sequence, always live, would land on
+  // one XCD while the late splits, live only for long contexts, share
+  // another. Rotating the split by the (sequence, kv head) index spreads
+  // each pair's live splits over consecutive XCDs from a rotating start.
+  const int split = (int)(((unsigned)blockIdx.x + (unsigned)(kvh + a.Hkv * b)) % (unsigned)a.nsplit);
   const int lane = threadIdx.x;
   const int g = lane >> 4;
   const int c = lane & 15;
@@ -364,9 +370,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   // E4M3 caches: k_scale multiplies every score, v_scale every value
   const float cexp = KV8 ? a.c * a.k_scale : a.c;
 
-  // ---- q^T operand: head c, columns 32s + 8g .. +8 (step s, lane group g);
-  // loaded first: the memory counter is in order, so the first step then waits
-  // only for q and its own step
+  // ---- q^T operand: head c, columns 32s + 8g .. +8 (step s, lane group g)
   u32x4 qf[KS];
   const bool q_live = c < G && a.qmode != 2;
   {
@@ -390,34 +394,26 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       }
   }
 
-  // Step q's physical blocks: a block past the split's last one carries the
-  // step's first block, and a step past the split re-reads step 0 (cache
-  // hits), so that every step issues the same loads. q is a compile-time
-  // index wherever this is used (the step loop is unrolled); the selection is
-  // made between values (readfirstlane), not between array elements, which
-  // the compiler would turn into one dynamically indexed load and so keep
-  // phys[] in scratch memory.
+  // Step q's physical blocks (q < ns): a block past the split's last one
+  // carries the step's first block (a cache hit; its tokens are masked), so
+  // that every step issues the same loads. q is a compile-time index wherever
+  // this is used (the step loop is unrolled); the selection is made between
+  // values (readfirstlane), not between array elements, which the compiler
+  // would turn into one dynamically indexed load and so keep phys[] in
+  // scratch memory.
   auto step_blocks = [&](int q, int (&ph)[NB]) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       const int i = NB * q + j;
       const int own = __builtin_amdgcn_readfirstlane(phys[i]);
       const int first = __builtin_amdgcn_readfirstlane(phys[NB * q]);
-      const int zero = __builtin_amdgcn_readfirstlane(phys[0]);
-      ph[j] = i < nb ? own : (q < ns ? first : zero);
+      ph[j] = i < nb ? own : first;
     }
   };
-  // The scheduling barriers keep q's loads and the two steps' loads in this
-  // order (the memory counter is in order; the waits below rely on it).
   {
     int ph[NB];
     step_blocks(0, ph);
-    __builtin_amdgcn_sched_barrier(0);
-    load_step<D, KV8>(buf0, kbase, vbase, block_stride, ph, o);
-    __builtin_amdgcn_sched_barrier(0);
-    step_blocks(1, ph);
-    load_step<D, KV8>(buf1, kbase, vbase, block_stride, ph, o);
-    __builtin_amdgcn_sched_barrier(0);
+    load_step<D, KV8>(buf, kbase, vbase, block_stride, ph, o);
   }
 
   if (a.rope) {
@@ -446,21 +442,16 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
   for (int p = 0; p < NS; ++p) {
     if (p >= ns) break;  // wave-uniform
-    char* buf = (p & 1) ? buf1 : buf0;
-    // step p has landed once at most the next step's loads are outstanding
-    if (p + 1 < NS)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L::LOADS) : "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // step p (and q) have landed
     const int t0 = (blk0 + NB * p) * kDecodeBlock;
     if (t0 + 16 * NB > ctx)
       step_compute<T, D, KV8, true>(st, buf, qf, o, t0, ctx, cexp, lane);
     else
       step_compute<T, D, KV8, false>(st, buf, qf, o, t0, ctx, cexp, lane);
-    if (p + 2 < NS) {
-      // every read of this buffer has returned before new data is written to it
+    if (p + 1 < NS && p + 1 < ns) {
+      // every read of the buffer has returned before new data is written to it
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      const int q = p + 2 < NS ? p + 2 : 0;  // in range also where the branch is dead
+      const int q = p + 1 < NS ? p + 1 : 0;  // in range also where the branch is dead
       int ph[NB];
       step_blocks(q, ph);
       load_step<D, KV8>(buf, kbase, vbase, block_stride, ph, o);
