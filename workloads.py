@@ -352,3 +352,30 @@ def decode_bytes(ctx_lens, Hq, Hkv, D, elem=2, max_blocks=None, kv_elem=None):
     lse = B * Hq * 4
     table = int(((ctx + BLOCK - 1) // BLOCK).sum()) * 4
     return kv + qo + lse + table + 4 * B
+
+
+# Linear layers of a Llama3-8B / Granite-8B transformer block (hidden 4096, 32 query and 8 kv heads of
+# 128, MLP width 14336), as weight shapes (N = out_features, K = in_features): fused q/k/v projection,
+# output projection, fused gate/up projection, down projection. Decode runs them at M = batch tokens
+# (the pages' end-to-end runs: batch 2; their decode micro-benchmark: batch 1).
+LINEAR_SHAPES = {
+    "qkv_proj": (6144, 4096),
+    "o_proj": (4096, 4096),
+    "gate_up_proj": (28672, 4096),
+    "down_proj": (4096, 14336),
+}
+LINEAR_M = 2
+
+
+def gemm_inputs(M: int, N: int, K: int, dtype: str, seed: int):
+    """Activations x [M, K] ~ N(0, 1) and weights w [N, K] ~ N(0, 1/K), rounded to dtype (float32
+    arrays holding the 16-bit values), so that y = x w^T has entries of order 1."""
+    rng = np.random.default_rng(seed)
+    x = round_to(rng.standard_normal((M, K), dtype=np.float32), dtype)
+    w = round_to(rng.standard_normal((N, K), dtype=np.float32) / np.float32(math.sqrt(K)), dtype)
+    return dict(x=x, w=w)
+
+
+def gemm_bytes(M: int, N: int, K: int, elem: int = 2) -> int:
+    """Algorithmic HBM bytes of y = x w^T: the weight, the activations and the output, each once."""
+    return (N * K + M * K + M * N) * elem
