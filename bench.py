@@ -54,6 +54,7 @@ KERNEL_SOURCES = {
     "append_fp8": ["tiled_attention_02_amd/csrc/paged_cache.hip", "tiled_attention_02_amd/csrc/attn_device.h"],
     "chunked_prefill_fp8": ["tiled_attention_02_amd/csrc/prefill_fwd.hip",
                             "tiled_attention_02_amd/csrc/attn_device.h"],
+    "gemm": ["tiled_attention_02_amd/csrc/gemm_splitk.hip", "tiled_attention_02_amd/csrc/attn_device.h"],
 }
 APPEND_LAYERS = 8
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
@@ -86,7 +87,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-flush", action="store_true", help="skip the cache flush between calls")
-    p.add_argument("--only", choices=["prefill", "prefill_fp8", "decode", "decode_fp8", "chunked"], default=None,
+    p.add_argument("--only", choices=["prefill", "prefill_fp8", "decode", "decode_fp8", "chunked", "gemm"],
+                   default=None,
                    help="profile helper: run only one of the two calls (not a benchmark line)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="run a plain device copy of this many MiB (counter calibration) and exit")
@@ -142,6 +144,25 @@ def cpu_baseline_prefill_fp8(x, case, qs, ks, vs, budget_heads=8, row_stride=16)
             "sample": f"float64 oracle (dequantize, then the definition) on {len(heads)} of {case.Hq} heads x "
                       f"{len(rows)} query rows (every {row_stride}th) of the 16384-token causal prefill; "
                       f"{dt:.1f} s wall"}
+
+
+def cpu_baseline_gemm(gx, min_seconds=5.0):
+    """The float64 oracle over the four linear layers at M = 2, repeated for a stable figure."""
+    import workloads as W
+    from oracle import gemm as G
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        for d in gx.values():
+            G.linear(d["x"], d["w"])
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    nbytes = sum(W.gemm_bytes(d["x"].shape[0], d["w"].shape[0], d["w"].shape[1]) for d in gx.values()) * reps
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": _oracle_threads(), "kind": "oracle",
+            "sample": f"float64 oracle (numpy matmul) over the four linear layers at M = 2, the whole workload, "
+                      f"repeated {reps} times; {dt:.1f} s wall"}
 
 
 def cpu_baseline_decode(x, case, nseq=64, min_seconds=5.0):
@@ -374,6 +395,14 @@ def main():
     fp8_sets = [(ckn, cvn, ck8, cv8)] + [tuple(t.clone() for t in (ckn, cvn, ck8, cv8))
                                          for _ in range(APPEND_LAYERS - 1)]
 
+    # the linear layers of a Llama3-8B / Granite-8B block at decode batch 2 (split-K GEMM)
+    log("[bench] building inputs: Llama3-8B linear layers, M = 2")
+    gx = {name: W.gemm_inputs(W.LINEAR_M, N, K, "bf16", seed=80 + i)
+          for i, (name, (N, K)) in enumerate(W.LINEAR_SHAPES.items())}
+    gdev = {name: (torch.from_numpy(d["x"]).to(bf).to(dev), torch.from_numpy(d["w"]).to(bf).to(dev),
+                   torch.empty((W.LINEAR_M, d["w"].shape[0]), dtype=bf, device=dev)) for name, d in gx.items()}
+    gbytes = {name: W.gemm_bytes(W.LINEAR_M, *W.LINEAR_SHAPES[name]) for name in gx}
+
     pflops = W.prefill_flops(pc.B, pc.Hq, pc.T, pc.T, pc.D, True)
     dbytes = W.decode_bytes(xd["ctx_lens"], dc.Hq, dc.Hkv, dc.D)
     d8bytes = W.decode_bytes(xd8["ctx_lens"], dc.Hq, dc.Hkv, dc.D, kv_elem=1)
@@ -422,6 +451,10 @@ def main():
 
         parts.append(("append_fp8", appends8, APPEND_LAYERS))
         parts.append(("chunked_prefill_fp8", chunk_prefill8, 1))
+
+    if args.only in (None, "gemm"):
+        for name, (gxd, gwd, gyd) in gdev.items():
+            parts.append(("gemm_" + name, (lambda x_=gxd, w_=gwd, y_=gyd: ta.attn_gemm_splitk(x_, w_, out=y_)), 1))
 
     def evict():
         # read-only pass over 1 GiB: pushes the inputs out of every cache level
@@ -494,7 +527,7 @@ def main():
                                "chunked bf16 prefill "
                                "B=4 Hq=32 Hkv=8 D=128 prefix~U[2048,8192] chunk=1024 through the block table "
                                "(chunked; again with RoPE fused: chunked_rope; again over E4M3 caches: "
-                               "chunked_fp8)",
+                               "chunked_fp8) + split-K GEMM of the four Llama3-8B linear layers at M=2 (gemm)",
                    "prefill_gflop_per_call": round(pflops / 1e9, 3),
                    "decode_mb_per_call": round(dbytes / 1e6, 3),
                    "cache_eviction_before_each_call": "none" if args.no_flush else "1 GiB read pass",
@@ -564,6 +597,21 @@ def main():
                                     "frac": round(a8_gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic("append_fp8"),
                                     "kernel": "append_kernel (E4M3 codes)", "algorithmic_bytes_per_launch": a8bytes}}},
     }
+    g_us = {name: ms["gemm_" + name] * 1e3 for name in gx}
+    g_gbs = sum(gbytes.values()) / (sum(g_us.values()) * 1e-6) / 1e9
+    gu_gbs = gbytes["gate_up_proj"] / (g_us["gate_up_proj"] * 1e-6) / 1e9
+    out["gemm"] = {
+        "workload": "split-K GEMM y = x w^T, bf16, the four linear layers of a Llama3-8B / Granite-8B block "
+                    "(q/k/v 6144x4096, o 4096x4096, gate/up 28672x4096, down 4096x14336) at M = 2 tokens, "
+                    "each call after the eviction pass (weights cold, as in a decode step)",
+        "value": round(g_gbs, 1), "unit": "GB/s", "us_per_layer": round(sum(g_us.values()), 2),
+        "layers": {name: {"us_per_call": round(g_us[name], 2),
+                          "GB_per_s": round(gbytes[name] / (g_us[name] * 1e-6) / 1e9, 1),
+                          "config": "tuned table"} for name in gx},
+        "roofline": {"bound": "hbm", "achieved": round(gu_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gu_gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic("gemm"),
+                     "kernel": "gemm_splitk_kernel (gate/up projection, the largest launch)",
+                     "algorithmic_bytes_per_launch": gbytes["gate_up_proj"]}}
     out["context"] = context_measurements(ta, W, torch, np, dev, flush_rows, flush_dst, evict)
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline: float64 oracle on a sample of the prefill workload")
@@ -581,6 +629,8 @@ def main():
                                                                       KS8, VS8)
         log("[bench] cpu baseline: float64 oracle on a sample of the rotary chunked-prefill workload")
         out["chunked_rope"]["cpu_baseline"] = cpu_baseline_chunked(xc, cc, rope=W.rope_table(16384, cc.D))
+        log("[bench] cpu baseline: float64 oracle on the linear layers")
+        out["gemm"]["cpu_baseline"] = cpu_baseline_gemm(gx)
     print(json.dumps(out), flush=True)
 
 

@@ -283,6 +283,44 @@ attn_status attn_decode_paged_rope(const void* q, const void* k_cache, const voi
                                    float scale, attn_dtype dtype, void* workspace,
                                    size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Linear-layer matrix product with the reduction (K) dimension split across
+ * workers and the pieces summed: the SplitK GEMM that the comemg.com page
+ * ("天下苦英偉達久矣！PyTorch免CUDA加速推理，Triton時代要來？", section "Triton
+ * SplitK GEMM 內核") uses for the Llama3-8B and Granite-8B linear layers, tuned
+ * per weight shape as in its section "GEMM 內核調優":
+ *
+ *   y[m, n] = sum_k x[m, k] * w[n, k]        (y = x w^T, no bias)
+ *
+ *  x : device [M, K] elements of `dtype` (activations, one row per token),
+ *      16-byte aligned.
+ *  w : device [N, K] elements of `dtype` (the weight, out x in features),
+ *      16-byte aligned.
+ *  y : device [M, N] elements of `dtype`, 2-byte aligned; written.
+ *  M, N, K >= 0, K % 8 == 0, K < 2^24. M == 0 or N == 0: nothing is written
+ *  (the pointers are not used); K == 0: y = 0 (x and w may be null).
+ * Products and sums in fp32, each output rounded once to `dtype`; the
+ * summation order depends only on (K, configuration), so results are
+ * deterministic. Sized for decode (a few rows of x): each launch covers 32
+ * rows of x, so the weight is read ceil(M / 32) times. The K split is made
+ * inside a workgroup (its waves sum consecutive K ranges, reduced in on-chip
+ * memory): one launch, no workspace.
+ *
+ * attn_gemm_splitk uses the configuration tuned for (N, K) (the linear
+ * layers named above) or a default one; attn_gemm_splitk_cfg takes it:
+ *  rows   : weight rows per workgroup, 16 or 32
+ *  waves  : waves per workgroup, 1 .. 16, each summing one K range
+ *  unroll : k-steps of 32 per round of loads, 1, 2, 4 or 8
+ * Errors: ATTN_ERR_INVALID (null pointer with M, N > 0, misalignment, bad
+ * configuration), ATTN_ERR_UNSUPPORTED (dtype, K % 8, K too large).
+ */
+attn_status attn_gemm_splitk(const void* x, const void* w, void* y, int M, int N, int K,
+                             attn_dtype dtype, hipStream_t stream);
+
+attn_status attn_gemm_splitk_cfg(const void* x, const void* w, void* y, int M, int N, int K,
+                                 attn_dtype dtype, int rows, int waves, int unroll,
+                                 hipStream_t stream);
+
 /* Workspace bytes attn_decode_paged needs for these sizes (0 if they are invalid). */
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_blocks_per_seq, int block_size);
 

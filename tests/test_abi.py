@@ -151,6 +151,28 @@ def test_append_fp8_rejects_before_launch(L, kw, code):
     assert ta.attn_last_error().startswith("attn_cache_append_fp8:")
 
 
+def _gemm(L, x=FAKE, w=FAKE, y=FAKE, M=2, N=4096, K=4096, dtype=1, cfg=None):
+    if cfg is None:
+        return L.attn_gemm_splitk(x, w, y, M, N, K, dtype, None)
+    return L.attn_gemm_splitk_cfg(x, w, y, M, N, K, dtype, *cfg, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), 1), (dict(w=None), 1), (dict(y=None), 1), (dict(x=FAKE_MIS), 1), (dict(w=FAKE_MIS), 1),
+    (dict(y=ctypes.c_void_p(0x10001)), 1), (dict(M=-1), 1), (dict(N=-1), 1), (dict(K=-8), 1),
+    (dict(K=4100), 2), (dict(K=1 << 24), 2), (dict(dtype=7), 2),
+    (dict(cfg=(8, 8, 4)), 1), (dict(cfg=(16, 0, 4)), 1), (dict(cfg=(16, 17, 4)), 1), (dict(cfg=(16, 8, 3)), 1),
+])
+def test_gemm_rejects_before_launch(L, kw, code):
+    assert _gemm(L, **kw) == code
+
+
+def test_gemm_empty_sizes_are_a_no_op(L):
+    # nothing to write: accepted without touching the (fake) pointers
+    assert _gemm(L, M=0) == 0 and _gemm(L, N=0) == 0
+    assert _gemm(L, x=None, w=None, y=None, M=0) == 0
+
+
 def test_workspace_size(L):
     import tiled_attention_02_amd as ta
     # 256 blocks of 16 tokens -> 16 splits of 256 tokens, each partial holding D values + log-sum,

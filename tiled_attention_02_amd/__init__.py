@@ -15,13 +15,14 @@ import os
 __all__ = ["attn_fwd", "attn_decode_paged", "attn_fwd_paged", "attn_cache_append", "attn_cache_append_fp8",
            "attn_decode_paged_fp8", "attn_fwd_paged_fp8", "attn_fwd_fp8", "attn_cache_append_rope",
            "attn_fwd_paged_rope", "attn_decode_paged_rope", "attn_decode_workspace_bytes",
-           "attn_status_str", "attn_last_error", "AttnError", "lib", "LIB_PATH", "EXPORTS", "BLOCK_SIZE",
-           "decode_workspace"]
+           "attn_gemm_splitk", "attn_status_str", "attn_last_error", "AttnError", "lib", "LIB_PATH", "EXPORTS",
+           "BLOCK_SIZE", "decode_workspace"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
 EXPORTS = ("attn_fwd", "attn_decode_paged", "attn_fwd_paged", "attn_cache_append", "attn_cache_append_fp8",
            "attn_decode_paged_fp8", "attn_fwd_paged_fp8", "attn_fwd_fp8", "attn_cache_append_rope",
-           "attn_fwd_paged_rope", "attn_decode_paged_rope", "attn_decode_workspace_bytes", "attn_status_str", "attn_last_error")
+           "attn_fwd_paged_rope", "attn_decode_paged_rope", "attn_decode_workspace_bytes", "attn_gemm_splitk",
+           "attn_gemm_splitk_cfg", "attn_status_str", "attn_last_error")
 BLOCK_SIZE = 16
 
 ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
@@ -71,6 +72,10 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_paged_rope.restype = i
     L.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
     L.attn_decode_workspace_bytes.restype = sz
+    L.attn_gemm_splitk.argtypes = [vp, vp, vp, i, i, i, i, vp]
+    L.attn_gemm_splitk.restype = i
+    L.attn_gemm_splitk_cfg.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, vp]
+    L.attn_gemm_splitk_cfg.restype = i
     L.attn_status_str.argtypes = [i]
     L.attn_status_str.restype = ctypes.c_char_p
     L.attn_last_error.argtypes = []
@@ -376,3 +381,28 @@ def attn_cache_append_fp8(k_new, v_new, k_cache, v_cache, k_scale: float, v_scal
                                      ctypes.c_float(v_scale), _ptr(block_table), _ptr(start_pos), _ptr(new_lens), B,
                                      Hkv, Tnew, D, bs, block_table.shape[1], NB, dt, _stream(k_new.device))
     _raise(st)
+
+
+def attn_gemm_splitk(x, w, out=None, config=None):
+    """Linear-layer product y = x w^T (no bias): x [M, K], w [N, K] (bf16 or fp16, contiguous, on the GPU),
+    K % 8 == 0. config: None for the tuned/default configuration, or (rows, waves, unroll).
+    Returns y [M, N] like x."""
+    import torch
+    dt = _dtype_code(x)
+    _check(x.dim() == 2 and w.dim() == 2 and x.shape[1] == w.shape[1], "x [M, K] and w [N, K] required")
+    _check(w.dtype == x.dtype, "x and w must share a dtype")
+    for t, n in ((x, "x"), (w, "w")):
+        _check(t.is_cuda and t.is_contiguous(), f"{n} must be a contiguous GPU tensor")
+    M, K = x.shape
+    N = w.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    _check(out.shape == (M, N) and out.dtype == x.dtype and out.is_contiguous(), "out must be [M, N] like x")
+    if config is None:
+        st = lib().attn_gemm_splitk(_ptr(x), _ptr(w), _ptr(out), M, N, K, dt, _stream(x.device))
+    else:
+        rows, waves, unroll = config
+        st = lib().attn_gemm_splitk_cfg(_ptr(x), _ptr(w), _ptr(out), M, N, K, dt, rows, waves, unroll,
+                                        _stream(x.device))
+    _raise(st)
+    return out

@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libattn.so")
-SOURCES = ["libattn.cpp", "prefill_fwd.hip", "decode_paged.hip", "paged_cache.hip"]
+SOURCES = ["libattn.cpp", "prefill_fwd.hip", "decode_paged.hip", "paged_cache.hip", "gemm_splitk.hip"]
 ARCH = "gfx950"
 
 

@@ -77,6 +77,22 @@ struct DecodeArgs {
 constexpr int kDecodeBlock = 16;        // tokens per cache block
 constexpr int kSplitBlocks = 16;        // cache blocks per split (256 tokens)
 
+// Split-K linear-layer product y [M, N] = x [M, K] w [N, K]^T (16-bit).
+struct GemmArgs {
+  const void* x;
+  const void* w;
+  void* y;
+  int M, N, K;   // M <= 32 per launch (the C ABI splits larger M)
+  int kslice;    // K elements per wave: a multiple of 32, waves * kslice >= K
+  int vec_store; // N % 4 == 0 and y 8-byte aligned: 4 outputs per store
+};
+// rows: weight rows per workgroup (16 or 32); waves: waves per workgroup
+// (1 .. 16), each taking one K range; unroll: k-steps of 32 per round of loads
+// (1, 2, 4 or 8)
+struct GemmConfig {
+  int rows, waves, unroll;
+};
+
 hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int D, bool causal, hipStream_t stream);
 hipError_t launch_prefill_paged(const PrefillArgs& a, bool bf16, int D, bool causal, hipStream_t stream);
 hipError_t launch_prefill_paged_fp8(const PrefillArgs& a, bool bf16, int D, bool causal, hipStream_t stream);
@@ -86,6 +102,7 @@ hipError_t launch_append_fp8(const AppendArgs& a, bool bf16, hipStream_t stream)
 hipError_t launch_append_rope(const AppendArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_decode_fp8(const DecodeArgs& a, bool bf16, hipStream_t stream);
+hipError_t launch_gemm(const GemmArgs& a, const GemmConfig& cfg, bool bf16, hipStream_t stream);
 
 // Workspace: the per-split partials (Hkv is part of the signature so that a
 // layout that depends on it stays a library-internal change).

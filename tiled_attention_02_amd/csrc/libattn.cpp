@@ -237,6 +237,63 @@ attn_status fwd_paged_impl(const char* fn, bool fp8, const void* q, const void* 
   return ok();
 }
 
+// Linear-layer product: configurations tuned per weight shape. Each entry was
+// the fastest of every (rows, waves, unroll) configuration for its shape on
+// MI355X at M = 2 (the sweep of tiled_attention_02_amd/tune_gemm.py); other
+// shapes take kGemmDefault.
+struct GemmTuned {
+  int N, K;
+  attn::GemmConfig cfg;
+};
+constexpr GemmTuned kGemmTuned[] = {
+    {6144, 4096, {16, 4, 4}},    // fused q/k/v projection
+    {4096, 4096, {16, 8, 4}},    // output projection
+    {28672, 4096, {16, 8, 4}},   // fused gate/up projection
+    {4096, 14336, {16, 12, 2}},  // down projection
+};
+constexpr attn::GemmConfig kGemmDefault = {16, 8, 4};
+
+attn::GemmConfig gemm_config(int N, int K) {
+  for (const GemmTuned& t : kGemmTuned)
+    if (t.N == N && t.K == K) return t.cfg;
+  return kGemmDefault;
+}
+
+attn_status gemm_impl(const char* fn, const void* x, const void* w, void* y, int M, int N, int K,
+                      attn_dtype dtype, attn::GemmConfig cfg, hipStream_t stream) {
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, (int)dtype);
+  if (M < 0 || N < 0 || K < 0) return fail(ATTN_ERR_INVALID, "%s: negative size (M=%d N=%d K=%d)", fn, M, N, K);
+  if (K % 8 != 0) return fail(ATTN_ERR_UNSUPPORTED, "%s: K = %d is not a multiple of 8", fn, K);
+  if (K >= (1 << 24)) return fail(ATTN_ERR_UNSUPPORTED, "%s: K = %d too large", fn, K);
+  if (cfg.rows != 16 && cfg.rows != 32)
+    return fail(ATTN_ERR_INVALID, "%s: rows = %d (16 or 32)", fn, cfg.rows);
+  if (cfg.waves < 1 || cfg.waves > 16) return fail(ATTN_ERR_INVALID, "%s: waves = %d (1 .. 16)", fn, cfg.waves);
+  if (cfg.unroll != 1 && cfg.unroll != 2 && cfg.unroll != 4 && cfg.unroll != 8)
+    return fail(ATTN_ERR_INVALID, "%s: unroll = %d (1, 2, 4 or 8)", fn, cfg.unroll);
+  if (M == 0 || N == 0) return ok();
+  if (!y || (K > 0 && (!x || !w)))
+    return fail(ATTN_ERR_INVALID, "%s: y, and x and w unless K == 0, must be non-null", fn);
+  if (!aligned16(x) || !aligned16(w)) return fail(ATTN_ERR_INVALID, "%s: x and w must be 16-byte aligned", fn);
+  if (reinterpret_cast<uintptr_t>(y) & 1u) return fail(ATTN_ERR_INVALID, "%s: y must be 2-byte aligned", fn);
+  attn::GemmArgs a;
+  a.w = w;
+  a.N = N;
+  a.K = K;
+  // each wave's K range: a multiple of 32, the waves together covering K
+  const int per = (K + cfg.waves - 1) / cfg.waves;
+  a.kslice = per < 32 ? 32 : (per + 31) / 32 * 32;
+  a.vec_store = (N % 4 == 0 && (reinterpret_cast<uintptr_t>(y) & 7u) == 0) ? 1 : 0;
+  // one launch per 32 activation rows
+  for (int m0 = 0; m0 < M; m0 += 32) {
+    a.x = static_cast<const uint16_t*>(x) + (size_t)m0 * K;
+    a.y = static_cast<uint16_t*>(y) + (size_t)m0 * N;
+    a.M = M - m0 < 32 ? M - m0 : 32;
+    const hipError_t e = attn::launch_gemm(a, cfg, dtype == ATTN_BF16, stream);
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  }
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -345,6 +402,16 @@ attn_status attn_fwd_fp8(const void* q, const void* k, const void* v, float q_sc
   hipError_t e = attn::launch_prefill_fp8(a, dtype == ATTN_BF16, D, causal != 0, stream);
   if (e != hipSuccess) return fail(ATTN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
+}
+
+attn_status attn_gemm_splitk(const void* x, const void* w, void* y, int M, int N, int K, attn_dtype dtype,
+                             hipStream_t stream) {
+  return gemm_impl("attn_gemm_splitk", x, w, y, M, N, K, dtype, gemm_config(N, K), stream);
+}
+
+attn_status attn_gemm_splitk_cfg(const void* x, const void* w, void* y, int M, int N, int K, attn_dtype dtype,
+                                 int rows, int waves, int unroll, hipStream_t stream) {
+  return gemm_impl("attn_gemm_splitk_cfg", x, w, y, M, N, K, dtype, attn::GemmConfig{rows, waves, unroll}, stream);
 }
 
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_blocks_per_seq, int block_size) {
