@@ -90,6 +90,23 @@ def test_chunk_edges(ta, starts, lens):
     _chunk_check(ta, case, starts=starts, lens=lens, what=f"chunk edges start={starts} n={lens}")
 
 
+def test_chunk_widely_varied_prefixes(ta):
+    """Prefixes from 0 to 3000 tokens and chunks from 0 to 400 rows in one batch: the workgroups take the
+    (sequence, query tile) groups in decreasing work, so the order differs from launch order; every row
+    still matches the oracle."""
+    case = W.ChunkCase("varied", B=8, Hq=4, Hkv=2, D=128, dtype="bf16", ctx_lo=0, ctx_hi=3000, chunk_lo=0,
+                       chunk_hi=400, seed=66)
+    _chunk_check(ta, case, starts=[0, 3000, 17, 1500, 2999, 640, 0, 2222], lens=[400, 1, 0, 129, 256, 77, 5, 400],
+                 what="chunk varied prefixes")
+
+
+def test_chunk_batch_beyond_the_ordered_grid(ta):
+    """70 sequences (more than the 64 whose groups are ordered by work): the launch-order path."""
+    case = W.ChunkCase("many", B=70, Hq=4, Hkv=1, D=64, dtype="fp16", ctx_lo=0, ctx_hi=300, chunk_lo=1,
+                       chunk_hi=40, seed=67)
+    _chunk_check(ta, case, what="chunk B=70")
+
+
 def test_chunk_all_rows_are_queries(ta):
     """q_lens NULL: every one of the Tq rows is a query (all chunks of equal length)."""
     case = W.ChunkCase("full", B=2, Hq=4, Hkv=1, D=64, dtype="fp16", ctx_lo=10, ctx_hi=400, chunk_lo=200,

@@ -22,6 +22,7 @@ struct PrefillArgs {
   float c;    // |scale| * log2(e), or 1 when scale == 0
   int qmode;
   int xcd_remap;  // set by the launcher: group kv-head siblings on one XCD
+  int lpt;        // set by the launcher (paged form): query-tile groups in decreasing work
   // paged form (chunked prefill): k / v are the caches [num_blocks][Hkv][16][D]
   const int* table;     // [B][max_blocks]
   const int* ctx_lens;  // [B] keys per sequence
