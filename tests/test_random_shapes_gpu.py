@@ -1,0 +1,111 @@
+"""GPU parity on seeded random configurations (through the C ABI, against the float64 oracle).
+
+Each case draws its configuration from its own seed (numpy default_rng), so a failure names a
+reproducible case: prefill (batch, heads with GQA groups 1-8, Tq / Tk from 1 to 300 including
+Tq != Tk, D 64 / 128, bf16 / fp16, causal or not, ragged or not, scale drawn from a wide range),
+paged decode (context lengths 1 to 2000 mixed within a batch, head layouts, scale), chunked prefill
+(prefixes 0 to 1500, chunks 0 to 200) and the split-K GEMM (M 1 to 40, N 1 to 700, K a multiple of 8
+up to 3000, a random configuration). Tolerances are those of the hand-picked parity tests.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import gemm as G
+from oracle import oracle as O
+from test_chunked_gpu import _chunk_check
+from test_parity_gpu import _compare, _decode_check, _note, _run_prefill
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ta(gpu):
+    import torch  # noqa: F401
+    import tiled_attention_02_amd as ta
+    ta.lib()
+    return ta
+
+
+def _heads(rng):
+    hkv = int(rng.integers(1, 5))
+    g = int(rng.choice([1, 2, 3, 4, 6, 8]))
+    return hkv * g, hkv
+
+
+@pytest.mark.parametrize("seed", range(1000, 1016))
+def test_random_prefill(ta, seed):
+    rng = np.random.default_rng(seed)
+    hq, hkv = _heads(rng)
+    D = int(rng.choice([64, 128]))
+    dtype = str(rng.choice(["bf16", "fp16"]))
+    causal = bool(rng.integers(0, 2))
+    ragged = bool(rng.integers(0, 4) == 0)
+    T = int(rng.integers(1, 301))
+    Tq, Tk = T, T
+    if not ragged and rng.integers(0, 2):
+        Tq, Tk = int(rng.integers(1, 301)), int(rng.integers(1, 301))
+    scale = float(rng.choice([1.0 / np.sqrt(D), 0.0, -0.2, 0.01, 1.0]))
+    B = int(rng.integers(1, 4))
+    # the scale is passed explicitly below (0.0 is valid: uniform weights)
+    case = W.PrefillCase(f"random prefill {seed}", B=B, Hq=hq, Hkv=hkv, T=T, D=D, dtype=dtype, causal=causal,
+                         ragged=ragged and T >= 2, seed=seed)
+    x = W.prefill_inputs(case, nan_padding=True, Tq=Tq, Tk=Tk)
+    _note(f"[case] random prefill seed={seed} B={B} Hq={hq} Hkv={hkv} Tq={Tq} Tk={Tk} D={D} {dtype} "
+          f"causal={causal} ragged={x['seq_lens'] is not None} scale={scale}")
+    o, lse = _run_prefill(ta, x, case, causal, scale)
+    o_ref, lse_ref = O.prefill(x["q"], x["k"], x["v"], scale, causal, x["seq_lens"])
+    _compare(o, lse, o_ref, lse_ref, dtype, what=f"random prefill {seed}")
+
+
+@pytest.mark.parametrize("seed", range(2000, 2012))
+def test_random_decode(ta, seed):
+    rng = np.random.default_rng(seed)
+    hq, hkv = _heads(rng)
+    D = int(rng.choice([64, 128]))
+    dtype = str(rng.choice(["bf16", "fp16"]))
+    B = int(rng.integers(1, 9))
+    ctx = rng.integers(1, 2001, B)
+    ctx[rng.integers(0, B)] = int(rng.choice([1, 16, 256, 257, 2000]))
+    scale = float(rng.choice([1.0 / np.sqrt(D), -0.1, 0.3]))
+    case = W.DecodeCase(f"random decode {seed}", B=B, Hq=hq, Hkv=hkv, D=D, dtype=dtype, ctx_lo=1,
+                        ctx_hi=int(ctx.max()), seed=seed, scale=scale)
+    _decode_check(ta, case, ctx_lens=ctx, scale=scale, what=f"random decode {seed} Hq={hq} Hkv={hkv} D={D} {dtype}")
+
+
+@pytest.mark.parametrize("seed", range(3000, 3008))
+def test_random_chunked_prefill(ta, seed):
+    rng = np.random.default_rng(seed)
+    hq, hkv = _heads(rng)
+    D = int(rng.choice([64, 128]))
+    dtype = str(rng.choice(["bf16", "fp16"]))
+    B = int(rng.integers(1, 6))
+    starts = [int(v) for v in rng.integers(0, 1501, B)]
+    lens = [int(v) for v in rng.integers(0, 201, B)]
+    lens[0] = max(lens[0], 1)
+    causal = bool(rng.integers(0, 4) != 0)
+    case = W.ChunkCase(f"random chunk {seed}", B=B, Hq=hq, Hkv=hkv, D=D, dtype=dtype, ctx_lo=0, ctx_hi=1500,
+                       chunk_lo=0, chunk_hi=max(lens), seed=seed)
+    _chunk_check(ta, case, causal=causal, starts=starts, lens=lens,
+                 what=f"random chunk {seed} Hq={hq} Hkv={hkv} D={D} {dtype} causal={causal}")
+
+
+@pytest.mark.parametrize("seed", range(4000, 4010))
+def test_random_gemm(ta, seed):
+    import torch
+    rng = np.random.default_rng(seed)
+    M = int(rng.integers(1, 41))
+    N = int(rng.integers(1, 701))
+    K = 8 * int(rng.integers(1, 376))
+    dtype = str(rng.choice(["bf16", "fp16"]))
+    config = (int(rng.choice([16, 32])), int(rng.integers(1, 17)), int(rng.choice([1, 2, 4, 8])))
+    d = W.gemm_inputs(M, N, K, dtype, seed)
+    _note(f"[case] random gemm seed={seed} M={M} N={N} K={K} {dtype} config={config}")
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    y = ta.attn_gemm_splitk(torch.from_numpy(d["x"]).to(tdt).cuda(), torch.from_numpy(d["w"]).to(tdt).cuda(),
+                            config=config)
+    torch.cuda.synchronize()
+    err = np.abs(y.float().cpu().numpy() - G.linear(d["x"], d["w"]))
+    ratio = float((err / G.error_bound(d["x"], d["w"], dtype)).max())
+    _note(f"[parity] random gemm {seed}: max err/bound={ratio:.3f}")
+    assert ratio <= 1.0
