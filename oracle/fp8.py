@@ -54,13 +54,15 @@ def float_to_e4m3(x) -> np.ndarray:
     numbers, k >= -6) and 2^-9 below 2^-6 (subnormals): |x| is rounded to a
     multiple of that step (np.rint: ties to even, which is the even code since
     the code's last bit is the multiple's last bit), then clamped to 448.
-    NaN maps to a NaN code with x's sign.
+    Infinities saturate like every other magnitude above 448. NaN maps to a NaN code with x's sign.
     """
     x = np.asarray(x, dtype=np.float32).astype(np.float64)
     neg = np.signbit(x)
     a = np.abs(x)
     nan = np.isnan(a)
-    a = np.where(nan, 0.0, a)
+    # saturation first: every magnitude above 448, infinity included, becomes 448 (the rounding below
+    # would also take (448, 464] to 448, but has no step for infinity)
+    a = np.where(nan, 0.0, np.minimum(a, E4M3_MAX))
     k = np.floor(np.log2(np.where(a > 0, a, 1.0)))
     step = np.exp2(np.maximum(k, -6.0) - 3.0)
     r = np.minimum(np.rint(a / step) * step, E4M3_MAX)

@@ -61,8 +61,8 @@ def pin_nearest(enc, dec):
 
 
 def pin_saturation(enc):
-    x = np.array([448.0, 449.0, 464.0, 465.0, 1e6, 3e38, -449.0, -1e6], dtype=np.float32)
-    assert enc(x).tolist() == [0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE]
+    x = np.array([448.0, 449.0, 464.0, 465.0, 1e6, 3e38, -449.0, -1e6, np.inf, -np.inf], dtype=np.float32)
+    assert enc(x).tolist() == [0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE, 0x7E, 0xFE]
 
 
 def _all_pins(enc, dec):
@@ -126,6 +126,13 @@ def test_codec_pins_catch_planted_mistakes(enc, dec, name):
 
 
 # ---------------------------------------------------------------- quantisation with a scale
+def test_quantize_saturates_quotients_that_overflow():
+    # x / scale beyond float32's range is infinite before the conversion: it saturates like any magnitude
+    # above 448
+    x = np.array([3e38, -3e38, 65504.0, 1.0], dtype=np.float32)
+    assert F8.quantize(x, 1e-35).tolist() == [0x7E, 0xFE, 0x7E, 0x7E]
+
+
 def test_quantize_error_within_half_step():
     rng = np.random.default_rng(3)
     for s in (1.0, 0.25, 0.0078125, 3.0, 0.1):
