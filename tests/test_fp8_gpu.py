@@ -147,6 +147,53 @@ def test_fp8_append_codes_bit_exact(ta, D, dtype, ks, vs):
     assert np.array_equal(vc.cpu().numpy(), vref), "V codes differ"
 
 
+def _every_16bit_value(dtype):
+    """Every finite 16-bit value of dtype and both infinities, as float32."""
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    if dtype == "bf16":
+        v = (bits << 16).view(np.float32)
+    else:
+        v = bits.astype(np.uint16).view(np.float16).astype(np.float32)
+    return v[~np.isnan(v)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("ks", [0.1, 1.0 / 3.0, 0.37, 0.0123, 1.0, 2.0 ** -100, 2.0 ** -101, 2.0 ** 100, 1e-35, 3e35])
+def test_fp8_append_every_16bit_value(ta, dtype, ks):
+    """Every finite 16-bit value (and +-inf) through the quantizing append, codes bit for bit against the
+    oracle's float32 division and rounding: covers the multiply-and-correct division (scales in
+    [2^-100, 2^100]) and the plain division (scales outside), saturation and the subnormal codes."""
+    import torch
+    vals = _every_16bit_value(dtype)
+    D = 128
+    n = -(-len(vals) // (16 * D)) * 16 * D  # whole cache blocks
+    flat = np.zeros(n, dtype=np.float32)
+    flat[:len(vals)] = vals
+    T = n // D
+    kn = flat.reshape(1, 1, T, D)
+    vn = kn[:, :, ::-1].copy()
+    nblk = T // 16
+    table = np.arange(nblk, dtype=np.int32).reshape(1, nblk)
+    k8 = np.full((nblk, 1, 16, D), W.E4M3_NAN, dtype=np.uint8)
+    v8 = k8.copy()
+    vs = 0.37 if ks != 0.37 else 0.1
+    _note(f"[case] fp8 append every {dtype} value ks={ks} vs={vs} rows={T}")
+    kc, vc = _u8(k8), _u8(v8)
+    start = np.zeros(1, dtype=np.int32)
+    ta.attn_cache_append_fp8(_dev(kn, dtype), _dev(vn, dtype), kc, vc, ks, vs, _i32(table), _i32(start), None)
+    torch.cuda.synchronize()
+    kref, vref = F8.cache_append_fp8(kn, vn, k8, v8, table, start, ks, vs)
+    kg, vg = kc.cpu().numpy(), vc.cpu().numpy()
+    for name, got, ref, src in (("K", kg, kref, kn), ("V", vg, vref, vn)):
+        bad = np.nonzero(got.reshape(-1) != ref.reshape(-1))[0]
+        if bad.size:
+            xs = src.reshape(-1)[bad[:8]]
+            _note(f"[mismatch] {name}: x={xs.tolist()} bits={[hex(int(b)) for b in xs.view(np.uint32)]} "
+                  f"gpu={got.reshape(-1)[bad[:8]].tolist()} oracle={ref.reshape(-1)[bad[:8]].tolist()}")
+    assert np.array_equal(kg, kref), f"K codes differ at {int((kg != kref).sum())} values"
+    assert np.array_equal(vg, vref), f"V codes differ at {int((vg != vref).sum())} values"
+
+
 def test_fp8_append_then_decode(ta):
     """A decode step as a server runs it: the new token's K/V quantized into the cache, then the decode."""
     import torch
