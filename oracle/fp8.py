@@ -79,7 +79,8 @@ def float_to_e4m3(x) -> np.ndarray:
 def quantize(x, scale) -> np.ndarray:
     """Codes of x / scale (float32 division), as stored in an FP8 cache."""
     s = np.float32(scale)
-    return float_to_e4m3(np.asarray(x, dtype=np.float32) / s)
+    with np.errstate(over="ignore"):  # a quotient beyond float32's range is infinite, then saturates
+        return float_to_e4m3(np.asarray(x, dtype=np.float32) / s)
 
 
 def dequantize(codes, scale) -> np.ndarray:
