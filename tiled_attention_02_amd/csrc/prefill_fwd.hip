@@ -75,6 +75,9 @@
 namespace attn {
 
 constexpr float kLazyRescale = 8.0f;
+// 16-bit products: bound on a lane's tile sum of p under the running max as it
+// stands, past which the tile is redone after moving the max
+constexpr float kOptimisticSum = 32768.0f;
 // FP8 form: lazy margin of the running max and the matching scale 2^(8 - margin) of p
 constexpr float kF8Margin = 1.0f;
 constexpr float kF8PScaleLog2 = 8.0f - kF8Margin;
@@ -517,12 +520,10 @@ __device__ __forceinline__ void tile_pv(Acc<D>& st, const u32x4 (&pf)[BK / 16], 
 // Mask and online-softmax statistics for one tile of scores: the tile max,
 // and the (lazy) rescale of the running sums and of O. Returns the max to
 // subtract in the exponentials.
-template <class T, int D, int BK, bool CAUSAL, bool F8 = false>
-__device__ __forceinline__ float softmax_stats(f32x16 (&sacc)[BK / 32], Acc<D>& st, const Geo& g, int k0, int qrow,
-                                               int w_lo, int h, float cexp) {
-  // FP8 form: the max moves once it grows by more than 1 (log2 units), so
-  // p <= 2 and the scaled p * 2^7 stay <= 2^8, inside E4M3's range
-  constexpr float kMargin = F8 ? kF8Margin : kLazyRescale;
+// Mask (diagonal and tail tiles only): keys past the row's last visible key
+// become -inf.
+template <int D, int BK, bool CAUSAL>
+__device__ __forceinline__ void softmax_mask(f32x16 (&sacc)[BK / 32], const Geo& g, int k0, int qrow, int w_lo, int h) {
   using S = Shape<D, BK>;
   const bool need_mask = (k0 + BK > g.Lk) || (CAUSAL && k0 + BK - 1 > w_lo + g.off);
   if (need_mask) {
@@ -535,6 +536,16 @@ __device__ __forceinline__ float softmax_stats(f32x16 (&sacc)[BK / 32], Acc<D>& 
         sacc[kb][r] = key > lim ? -__builtin_inff() : sacc[kb][r];
       }
   }
+}
+
+// Tile max and lazy rescale: the running max moves when the tile's max
+// exceeds it by more than the margin; returns the max to subtract.
+template <class T, int D, int BK, bool F8 = false>
+__device__ __forceinline__ float softmax_max(const f32x16 (&sacc)[BK / 32], Acc<D>& st, float cexp) {
+  // FP8 form: the max moves once it grows by more than 1 (log2 units), so
+  // p <= 2 and the scaled p * 2^7 stay <= 2^8, inside E4M3's range
+  constexpr float kMargin = F8 ? kF8Margin : kLazyRescale;
+  using S = Shape<D, BK>;
   // tile max (raw scores; cexp > 0)
   float mx = sacc[0][0];
 #pragma unroll
@@ -542,7 +553,6 @@ __device__ __forceinline__ float softmax_stats(f32x16 (&sacc)[BK / 32], Acc<D>& 
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
   mx = half_swap_max(mx) * cexp;  // -inf stays -inf (cexp > 0)
-  // lazy rescale: move m only when the max grows by more than the margin
   const bool grow = mx > st.m + kMargin;
   if (__builtin_amdgcn_ballot_w64(grow)) {
     const float m_new = grow ? mx : st.m;
@@ -558,8 +568,8 @@ __device__ __forceinline__ float softmax_stats(f32x16 (&sacc)[BK / 32], Acc<D>& 
 
 // p = 2^(s*c - m), the two running sums, and the P^T operand (no branches).
 template <class T, int D, int BK, bool F8 = false>
-__device__ __forceinline__ void softmax_exp(const f32x16 (&sacc)[BK / 32], u32x4 (&pf)[BK / 16], Acc<D>& st,
-                                            float msub, float cexp) {
+__device__ __forceinline__ float softmax_exp(const f32x16 (&sacc)[BK / 32], u32x4 (&pf)[BK / 16], Acc<D>& st,
+                                             float msub, float cexp) {
   using S = Shape<D, BK>;
   if constexpr (F8) {
     // p * 2^7 (<= 2^8), rounded to E4M3: byte 16 kb + r of the lane's P^T
@@ -579,7 +589,7 @@ __device__ __forceinline__ void softmax_exp(const f32x16 (&sacc)[BK / 32], u32x4
       }
     st.l += ls;
     st.lr = st.l;
-    return;
+    return ls;
   }
   // one partial sum per 8 probabilities keeps the dependency chains short, so
   // the work interleaves with the matrix instructions of the next tile
@@ -606,6 +616,7 @@ __device__ __forceinline__ void softmax_exp(const f32x16 (&sacc)[BK / 32], u32x4
   }
   st.l += ls;
   st.lr += lrs;
+  return ls;
 }
 
 // O = O^T / l, lse = (m + log2 l) ln 2; padding rows -> 0, -inf.
@@ -785,14 +796,19 @@ __device__ __forceinline__ void pipe_step(int kt, const char* kcur, const char* 
   const bool work_next = kt + 1 < g.nkt && wave_live && (!CAUSAL || (kt + 1) * BK <= w_last);
   if (work) {
     u32x4 pf[S::PS];
-    const float msub = softmax_stats<T, D, BK, CAUSAL, F8>(s_cur, st, g, kt * BK, qrow, w_lo, h, cexp);
+    softmax_mask<D, BK, CAUSAL>(s_cur, g, kt * BK, qrow, w_lo, h);
+    // 16-bit products: the exponentials use the running max as it stands
+    // (no tile max on the way); the FP8 form needs the max first
+    const float l0 = st.l, lr0 = st.lr;
+    const float msub = F8 ? softmax_max<T, D, BK, true>(s_cur, st, cexp) : st.m;
+    float ls;
     if (work_next && KV8) {
       // E4M3 tiles: the compiler schedules the reads and the exponentials
       tile_qk_plain<T, D, BK, KV8, F8>(s_nxt, kcur, o, st);
-      softmax_exp<T, D, BK, F8>(s_cur, pf, st, msub, cexp);
+      ls = softmax_exp<T, D, BK, F8>(s_cur, pf, st, msub, cexp);
     } else if (work_next) {
       tile_qk_plain<T, D, BK>(s_nxt, kcur, o, st);
-      softmax_exp<T, D, BK>(s_cur, pf, st, msub, cexp);
+      ls = softmax_exp<T, D, BK>(s_cur, pf, st, msub, cexp);
       // interleave: each MFMA of the next tile's S is followed by a share of
       // the current tile's vector work; K fragments stay kQkDepth steps ahead
       constexpr int NMF = S::KS * S::KB;
@@ -809,7 +825,20 @@ __device__ __forceinline__ void pipe_step(int kt, const char* kcur, const char* 
         }
       }
     } else {
-      softmax_exp<T, D, BK, F8>(s_cur, pf, st, msub, cexp);
+      ls = softmax_exp<T, D, BK, F8>(s_cur, pf, st, msub, cexp);
+    }
+    if constexpr (!F8) {
+      // A lane whose 32 probabilities sum past 2^15 (or to inf / NaN: the
+      // first visible tile, where the running max is -inf) needs the running
+      // max moved first: the tile is redone with the lazy rescale. Otherwise
+      // every p <= 2^15 stays inside fp16's range and the P operand's
+      // relative precision is that of any other p.
+      if (__builtin_amdgcn_ballot_w64(!(ls <= kOptimisticSum))) {
+        st.l = l0;
+        st.lr = lr0;
+        const float m2 = softmax_max<T, D, BK>(s_cur, st, cexp);
+        softmax_exp<T, D, BK>(s_cur, pf, st, m2, cexp);
+      }
     }
     __builtin_amdgcn_s_setprio(2);
     tile_pv<T, D, BK, KV8, F8>(st, pf, vcur, o);
