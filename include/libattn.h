@@ -301,8 +301,8 @@ attn_status attn_decode_paged_rope(const void* q, const void* k_cache, const voi
  *  (the pointers are not used); K == 0: y = 0 (x and w may be null).
  * Products and sums in fp32, each output rounded once to `dtype`; the
  * summation order depends only on (K, configuration), so results are
- * deterministic. Sized for decode (a few rows of x): each launch covers 32
- * rows of x, so the weight is read ceil(M / 32) times. The K split is made
+ * deterministic. Sized for decode (a few rows of x): each launch covers 64
+ * rows of x, so the weight is read ceil(M / 64) times. The K split is made
  * inside a workgroup (its waves sum consecutive K ranges, reduced in on-chip
  * memory): one launch, no workspace.
  *

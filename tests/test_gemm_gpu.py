@@ -4,7 +4,7 @@ Reference: y = x w^T in float64 (oracle/gemm.py). Tolerance per element: oracle/
 unit in the last place of the output type at |y| plus gamma_K * sum_k |x_mk w_nk| (float32 products and
 sums, u = 2^-24), which any float32 summation order meets. The largest error / bound ratio is printed.
 Cases: the Llama3-8B / Granite-8B linear layers at decode batch 1 and 2 (every element), ragged M, N and
-K around the tile sizes (16 weight rows, 16 activation rows, k-steps of 32, one launch per 32 rows of
+K around the tile sizes (16 weight rows, 16 activation rows, k-steps of 32, one launch per 64 rows of
 x), every configuration on one ragged shape, K = 0, and determinism.
 """
 import numpy as np
@@ -64,7 +64,7 @@ def test_llama_linear_layers_fp16(ta, layer):
     _check(ta, 2, N, K, "fp16", seed=63, what=layer)
 
 
-@pytest.mark.parametrize("M", [1, 3, 16, 17, 32, 33, 44])
+@pytest.mark.parametrize("M", [1, 3, 16, 17, 32, 33, 44, 63, 64, 65, 130])
 @pytest.mark.parametrize("N,K", [(1, 8), (15, 24), (17, 40), (100, 328), (257, 1000)])
 def test_ragged_shapes(ta, M, N, K):
     _check(ta, M, N, K, "bf16" if (M + N) % 2 else "fp16", seed=M * 1000 + N, what="ragged")
@@ -76,6 +76,12 @@ CONFIGS = [(r, wv, u) for r in (16, 32) for wv in (1, 2, 3, 5, 8, 16) for u in (
 @pytest.mark.parametrize("config", CONFIGS, ids=lambda c: f"r{c[0]}w{c[1]}u{c[2]}")
 def test_every_configuration(ta, config):
     _check(ta, 19, 83, 2056, "bf16", seed=70, config=config, what="config")
+
+
+@pytest.mark.parametrize("config", [(32, 16, 8), (32, 16, 1), (16, 16, 4)])
+def test_largest_reduction_tiles(ta, config):
+    """64 activation rows with 32 weight rows and 16 waves: 128 KiB of partial tiles in LDS."""
+    _check(ta, 64, 200, 4096, "bf16", seed=73, config=config, what="64 rows")
 
 
 def test_zero_k_gives_zero(ta):

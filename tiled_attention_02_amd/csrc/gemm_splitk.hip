@@ -142,25 +142,45 @@ __global__ __launch_bounds__(1024) void gemm_splitk_kernel(GemmArgs a) {
   }
 }
 
+// The partial tiles of every wave sit in LDS for the reduction: up to
+// 16 waves x 2 x 4 tiles x 1 KiB = 128 KiB, above the 64 KiB a launch gets
+// without asking (gfx950 has 160 KiB per CU).
+template <class K>
+static hipError_t launch_k(K kernel, const GemmArgs& a, dim3 grid, dim3 block, size_t lds, hipStream_t stream) {
+  if (lds > 65536) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kernel, grid, block, lds, stream, a);
+  return hipGetLastError();
+}
+
 template <class T, int R, int MT>
 static hipError_t launch_u(const GemmArgs& a, int waves, int unroll, hipStream_t stream) {
   const dim3 grid((unsigned)((a.N + R - 1) / R)), block((unsigned)(64 * waves));
   const size_t lds = (size_t)waves * (R / 16) * MT * 64 * sizeof(f32x4);
   switch (unroll) {
-    case 1: hipLaunchKernelGGL((gemm_splitk_kernel<T, R, MT, 1>), grid, block, lds, stream, a); break;
-    case 2: hipLaunchKernelGGL((gemm_splitk_kernel<T, R, MT, 2>), grid, block, lds, stream, a); break;
-    case 4: hipLaunchKernelGGL((gemm_splitk_kernel<T, R, MT, 4>), grid, block, lds, stream, a); break;
-    default: hipLaunchKernelGGL((gemm_splitk_kernel<T, R, MT, 8>), grid, block, lds, stream, a); break;
+    case 1: return launch_k(gemm_splitk_kernel<T, R, MT, 1>, a, grid, block, lds, stream);
+    case 2: return launch_k(gemm_splitk_kernel<T, R, MT, 2>, a, grid, block, lds, stream);
+    case 4: return launch_k(gemm_splitk_kernel<T, R, MT, 4>, a, grid, block, lds, stream);
+    default: return launch_k(gemm_splitk_kernel<T, R, MT, 8>, a, grid, block, lds, stream);
   }
-  return hipGetLastError();
+}
+
+template <class T, int R>
+static hipError_t launch_r(const GemmArgs& a, const GemmConfig& cfg, hipStream_t stream) {
+  switch ((a.M + 15) / 16) {  // tiles of 16 activation rows
+    case 1: return launch_u<T, R, 1>(a, cfg.waves, cfg.unroll, stream);
+    case 2: return launch_u<T, R, 2>(a, cfg.waves, cfg.unroll, stream);
+    case 3: return launch_u<T, R, 3>(a, cfg.waves, cfg.unroll, stream);
+    default: return launch_u<T, R, 4>(a, cfg.waves, cfg.unroll, stream);
+  }
 }
 
 template <class T>
 static hipError_t launch_t(const GemmArgs& a, const GemmConfig& cfg, hipStream_t stream) {
-  const bool two = a.M > 16;
-  if (cfg.rows == 32)
-    return two ? launch_u<T, 32, 2>(a, cfg.waves, cfg.unroll, stream) : launch_u<T, 32, 1>(a, cfg.waves, cfg.unroll, stream);
-  return two ? launch_u<T, 16, 2>(a, cfg.waves, cfg.unroll, stream) : launch_u<T, 16, 1>(a, cfg.waves, cfg.unroll, stream);
+  return cfg.rows == 32 ? launch_r<T, 32>(a, cfg, stream) : launch_r<T, 16>(a, cfg, stream);
 }
 
 hipError_t launch_gemm(const GemmArgs& a, const GemmConfig& cfg, bool bf16, hipStream_t stream) {

@@ -83,7 +83,7 @@ struct GemmArgs {
   const void* x;
   const void* w;
   void* y;
-  int M, N, K;   // M <= 32 per launch (the C ABI splits larger M)
+  int M, N, K;   // M <= kGemmRowsPerLaunch per launch (the C ABI splits larger M)
   int kslice;    // K elements per wave: a multiple of 32, waves * kslice >= K
   int vec_store; // N % 4 == 0 and y 8-byte aligned: 4 outputs per store
 };
@@ -93,6 +93,7 @@ struct GemmArgs {
 struct GemmConfig {
   int rows, waves, unroll;
 };
+constexpr int kGemmRowsPerLaunch = 64;  // activation rows per launch: up to 4 tiles of 16
 
 hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int D, bool causal, hipStream_t stream);
 hipError_t launch_prefill_paged(const PrefillArgs& a, bool bf16, int D, bool causal, hipStream_t stream);

@@ -283,11 +283,11 @@ attn_status gemm_impl(const char* fn, const void* x, const void* w, void* y, int
   const int per = (K + cfg.waves - 1) / cfg.waves;
   a.kslice = per < 32 ? 32 : (per + 31) / 32 * 32;
   a.vec_store = (N % 4 == 0 && (reinterpret_cast<uintptr_t>(y) & 7u) == 0) ? 1 : 0;
-  // one launch per 32 activation rows
-  for (int m0 = 0; m0 < M; m0 += 32) {
+  // one launch per kGemmRowsPerLaunch activation rows
+  for (int m0 = 0; m0 < M; m0 += attn::kGemmRowsPerLaunch) {
     a.x = static_cast<const uint16_t*>(x) + (size_t)m0 * K;
     a.y = static_cast<uint16_t*>(y) + (size_t)m0 * N;
-    a.M = M - m0 < 32 ? M - m0 : 32;
+    a.M = M - m0 < attn::kGemmRowsPerLaunch ? M - m0 : attn::kGemmRowsPerLaunch;
     const hipError_t e = attn::launch_gemm(a, cfg, dtype == ATTN_BF16, stream);
     if (e != hipSuccess) return fail(ATTN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   }
