@@ -33,7 +33,7 @@ def _heads(rng):
     return hkv * g, hkv
 
 
-@pytest.mark.parametrize("seed", range(1000, 1016))
+@pytest.mark.parametrize("seed", range(1000, 1048))
 def test_random_prefill(ta, seed):
     rng = np.random.default_rng(seed)
     hq, hkv = _heads(rng)
@@ -58,7 +58,7 @@ def test_random_prefill(ta, seed):
     _compare(o, lse, o_ref, lse_ref, dtype, what=f"random prefill {seed}")
 
 
-@pytest.mark.parametrize("seed", range(2000, 2012))
+@pytest.mark.parametrize("seed", range(2000, 2036))
 def test_random_decode(ta, seed):
     rng = np.random.default_rng(seed)
     hq, hkv = _heads(rng)
@@ -73,7 +73,7 @@ def test_random_decode(ta, seed):
     _decode_check(ta, case, ctx_lens=ctx, scale=scale, what=f"random decode {seed} Hq={hq} Hkv={hkv} D={D} {dtype}")
 
 
-@pytest.mark.parametrize("seed", range(3000, 3008))
+@pytest.mark.parametrize("seed", range(3000, 3024))
 def test_random_chunked_prefill(ta, seed):
     rng = np.random.default_rng(seed)
     hq, hkv = _heads(rng)
@@ -90,7 +90,7 @@ def test_random_chunked_prefill(ta, seed):
                  what=f"random chunk {seed} Hq={hq} Hkv={hkv} D={D} {dtype} causal={causal}")
 
 
-@pytest.mark.parametrize("seed", range(4000, 4010))
+@pytest.mark.parametrize("seed", range(4000, 4024))
 def test_random_gemm(ta, seed):
     import torch
     rng = np.random.default_rng(seed)
