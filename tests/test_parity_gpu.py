@@ -306,6 +306,14 @@ def test_decode_explicit_workspace_reused_across_shapes(ta):
         _compare(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, c.dtype, what=c.name)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_decode_long_contexts(ta, dtype):
+    """Contexts up to 33000 tokens (130 ranges of 256 in one sequence): the merge reads its split slots in
+    rounds of 16; lengths on and off the range and block edges."""
+    case = W.DecodeCase("long-ctx", B=4, Hq=8, Hkv=1, D=128, dtype=dtype, ctx_lo=1, ctx_hi=33000, seed=49)
+    _decode_check(ta, case, ctx_lens=[33000, 20481, 4097, 12800], what=f"decode long contexts {dtype}")
+
+
 # ---------------------------------------------------------------- large batch, graph replays
 def test_decode_large_batch(ta):
     """8200 sequences (16400 (sequence, kv head) pairs, grid z = 8200): most contexts are short (one
