@@ -497,7 +497,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 // of a sequence's splits. One workgroup of D threads per (query head,
 // sequence); thread d produces output column d. Every split slot holds a
 // partial (splits past the sequence's end hold log2-sum-exp = -inf, and their
-// values are never used), so all slots are read in one round, 16 at a time.
+// values are never used), so the slots are read 16 at a time with no
+// dependent load (one round for up to 16 splits).
 template <class T, int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
   const int hq = blockIdx.x;
