@@ -238,6 +238,139 @@ def cpu_baseline_chunked_fp8(x, case, k8, v8, ks, vs, nseq=1):
                       f"{case.B} sequences, all {case.Hq} heads and rows; {dt:.1f} s wall"}
 
 
+def _parity(o_gpu, o_ref, lse_gpu=None, lse_ref=None, tol=1e-2, bound=None, what=""):
+    """Element-wise check of GPU outputs against the oracle's: |dO| <= max(tol, one bf16 unit at |O|)
+    (or <= bound where a derived bound is given), |dlse| <= 1e-4 * max(1, |lse|)."""
+    import numpy as np
+    o_gpu = np.asarray(o_gpu, dtype=np.float64)
+    o_ref = np.asarray(o_ref, dtype=np.float64)
+    err = np.abs(o_gpu - o_ref)
+    if bound is None:
+        ax = np.maximum(np.abs(o_ref), 2.0 ** -14)
+        allow = np.maximum(tol, 2.0 ** (np.floor(np.log2(ax)) - 7))
+    else:
+        allow = bound
+    res = {"what": what, "elements": int(err.size), "max_abs_err": float(err.max()),
+           "max_err_over_allowed": float((err / allow).max())}
+    ok = bool(np.isfinite(o_gpu).all()) and res["max_err_over_allowed"] <= 1.0
+    if lse_gpu is not None:
+        lse_gpu = np.asarray(lse_gpu, dtype=np.float64)
+        lse_ref = np.asarray(lse_ref, dtype=np.float64)
+        rel = np.abs(lse_gpu - lse_ref) / np.maximum(1.0, np.abs(lse_ref))
+        res["max_rel_lse_err"] = float(rel.max())
+        ok = ok and res["max_rel_lse_err"] <= 1e-4
+    res["ok"] = ok
+    return res
+
+
+def parity_on_timed_buffers(ta, torch, np, W, pc, xp, o, lse, xp8, scales8, o8, lse8, dc, xd, do, dlse, xd8, ks8,
+                            vs8, do8, dlse8, cc, xc, rope_tab, calls, co, clse, ck8, cv8, gx, gdev):
+    """The outputs of the timed calls (the same buffers, after the timed steps) against the float64 oracle on a
+    sample: prefill and FP8 prefill on 4 heads x 8 rows of the 16k config, both decodes on the whole batch,
+    each chunked leg (re-run once on its own caches: the legs share the output buffer) on its first sequence,
+    every linear layer whole. Part of the CPU-baseline leg (it runs the oracle)."""
+    from oracle import fp8 as F8
+    from oracle import gemm as G
+    from oracle import oracle as O
+    from oracle import rope as R
+    res = {}
+    torch.cuda.synchronize()
+    heads, rows = [0, 7, 13, 31], [0, 1, 127, 128, 4095, 8191, 12000, 16383]
+    picks = np.array([(0, h, i) for h in heads for i in rows])
+    og, lg = o.float().cpu().numpy(), lse.cpu().numpy()
+    orf, lrf = O.prefill_rows(xp["q"], xp["k"], xp["v"], pc.scale, True, None, picks)
+    res["prefill"] = _parity(og[0, picks[:, 1], picks[:, 2]], orf, lg[0, picks[:, 1], picks[:, 2]], lrf,
+                             what="4 heads x 8 rows")
+    qs, kps, vps = scales8
+    og8, lg8 = o8.float().cpu().numpy(), lse8.cpu().numpy()
+    qd, kd, vd = F8.dequantize(xp8["q"], qs), F8.dequantize(xp8["k"], kps), F8.dequantize(xp8["v"], vps)
+    orf8, lrf8 = O.prefill_rows(qd, kd, vd, pc.scale, True, None, picks)
+    bnd = F8.prefill_fp8_bound(xp8["v"], vps, pc.T)  # [B, Hkv]: all keys (conservative for earlier rows)
+    allow8 = bnd[0, picks[:, 1] // (pc.Hq // pc.Hkv)][:, None] + 2.0 ** (np.floor(np.log2(np.maximum(
+        np.abs(orf8), 2.0 ** -14))) - 7)
+    res["prefill_fp8"] = _parity(og8[0, picks[:, 1], picks[:, 2]], orf8, lg8[0, picks[:, 1], picks[:, 2]], lrf8,
+                                 bound=allow8, what="4 heads x 8 rows; derived E4M3 bound")
+    dref, dlref = O.decode_paged(xd["q"], xd["k_cache"], xd["v_cache"], xd["block_table"], xd["ctx_lens"], dc.scale)
+    res["decode"] = _parity(do.float().cpu().numpy(), dref, dlse.cpu().numpy(), dlref, what="whole batch")
+    d8ref, dl8ref = F8.decode_paged_fp8(xd8["q"], xd8["k_cache"], xd8["v_cache"], ks8, vs8, xd8["block_table"],
+                                        xd8["ctx_lens"], dc.scale)
+    res["decode_fp8"] = _parity(do8.float().cpu().numpy(), d8ref, dlse8.cpu().numpy(), dl8ref, what="whole batch")
+    sl = slice(0, 1)
+    kref, vref = O.cache_append(xc["k_new"], xc["v_new"], xc["k_cache"], xc["v_cache"], xc["block_table"],
+                                xc["start_pos"], xc["new_lens"])
+    for name, call in calls:
+        call()
+        torch.cuda.synchronize()
+        og_c, lg_c = co[0:1].float().cpu().numpy(), clse[0:1].cpu().numpy()
+        if name == "chunked":
+            r, lr_ = O.prefill_paged(xc["q"][sl], kref, vref, xc["block_table"][sl], xc["ctx_lens"][sl],
+                                     xc["new_lens"][sl], cc.scale, True)
+        elif name == "chunked_rope":
+            tab = rope_tab.cpu().numpy()
+            kr, vr = R.cache_append_rope(xc["k_new"], xc["v_new"], xc["k_cache"], xc["v_cache"], xc["block_table"],
+                                         xc["start_pos"], tab, cc.dtype, xc["new_lens"])
+            r, lr_ = R.prefill_paged_rope(xc["q"][sl], kr, vr, xc["block_table"][sl], xc["ctx_lens"][sl],
+                                          xc["new_lens"][sl], tab, cc.scale, cc.dtype, True)
+        else:
+            k8r, v8r = F8.cache_append_fp8(xc["k_new"], xc["v_new"], ck8, cv8, xc["block_table"], xc["start_pos"],
+                                           ks8, vs8, xc["new_lens"])
+            r, lr_ = F8.prefill_paged_fp8(xc["q"][sl], k8r, v8r, ks8, vs8, xc["block_table"][sl], xc["ctx_lens"][sl],
+                                          xc["new_lens"][sl], cc.scale, True)
+        n = int(xc["new_lens"][0])
+        res[name] = _parity(og_c[:, :, :n], r[:, :, :n], lg_c[:, :, :n], lr_[:, :, :n],
+                            what="first sequence, all heads and rows")
+    worst = 0.0
+    for name, d in gx.items():
+        yg = gdev[name][2].float().cpu().numpy()
+        ratio = float((np.abs(yg - G.linear(d["x"], d["w"])) / G.error_bound(d["x"], d["w"], "bf16")).max())
+        worst = max(worst, ratio)
+    res["gemm"] = {"what": "four layers, every element", "max_err_over_bound": worst, "ok": worst <= 1.0}
+    res["all_ok"] = all(v.get("ok", False) for v in res.values() if isinstance(v, dict))
+    return res
+
+
+def clock_derived_peak(torch):
+    """Dense bf16 MFMA peak from the chip's CU count and maximum shader clock read on the box:
+    nCU x 4096 flop/clk (a 32x32x16 bf16 MFMA is 32768 flop in 32 clocks on each of 4 SIMDs) x sclk.
+    The clock comes from the HIP runtime already loaded in this process (no second load)."""
+    import ctypes
+    try:
+        hip = ctypes.CDLL("libamdhip64.so.7", mode=os.RTLD_NOLOAD)
+    except OSError:
+        return None
+    khz = ctypes.c_int(0)
+    dev = torch.cuda.current_device()
+    HIP_DEVICE_ATTRIBUTE_CLOCK_RATE = 5  # hipDeviceAttributeClockRate (kHz) in hip_runtime_api.h
+    if hip.hipDeviceGetAttribute(ctypes.byref(khz), HIP_DEVICE_ATTRIBUTE_CLOCK_RATE, dev) != 0 or khz.value <= 0:
+        return None
+    ncu = torch.cuda.get_device_properties(dev).multi_processor_count
+    return {"cus": int(ncu), "max_sclk_mhz": khz.value / 1e3,
+            "bf16_dense_tflops": round(ncu * 4096 * khz.value * 1e3 / 1e12, 1)}
+
+
+def decode_rotation_crosscheck(ta, torch, np, dq, kc, vc, bt, cl, scale, ws, copies=4, reps=24):
+    """Decode timed without the eviction pass, rotating through `copies` independent copies of the caches
+    (each 150 MB, together past the 256 MB Infinity Cache), so each call still finds its cache cold."""
+    kcs = [kc] + [kc.clone() for _ in range(copies - 1)]
+    vcs = [vc] + [vc.clone() for _ in range(copies - 1)]
+    out = torch.empty_like(dq)
+    lse = torch.empty(dq.shape[:2], dtype=torch.float32, device=dq.device)
+    for i in range(copies):
+        ta.attn_decode_paged(dq, kcs[i], vcs[i], bt, cl, scale=scale, out=out, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    ts = []
+    for r in range(reps):
+        i = r % copies
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        ta.attn_decode_paged(dq, kcs[i], vcs[i], bt, cl, scale=scale, out=out, lse=lse, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del kcs, vcs
+    return float(np.median(ts)) * 1e3, float(np.min(ts)) * 1e3
+
+
 def context_measurements(ta, W, torch, np, dev, flush_rows, flush_dst, evict):
     """Figures reported beside the headline numbers (not part of `value`).
 
@@ -486,6 +619,8 @@ def main():
           for i, (name, _, n) in enumerate(parts)}
     ms_min = {name: float(np.min([e[2 * i].elapsed_time(e[2 * i + 1]) / n for e in evs]))
               for i, (name, _, n) in enumerate(parts)}
+    ms_med = {name: float(np.median([e[2 * i].elapsed_time(e[2 * i + 1]) / n for e in evs]))
+              for i, (name, _, n) in enumerate(parts)}
     log("[bench] " + "; ".join(f"{k} {v * 1e3:.1f} us (min {ms_min[k] * 1e3:.1f})" for k, v in ms.items()) +
         f"; wall/step {wall / args.steps * 1e3:.2f} ms")
     if args.only:
@@ -535,6 +670,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(p_tfs, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(p_tfs / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic("prefill"),
                      "kernel": "prefill_kernel", "ms_per_launch": round(p_avg, 4),
+                     "ms_per_launch_median": round(ms_med["prefill"], 4), "ms_per_launch_min": round(ms_min["prefill"], 4),
                      "algorithmic_flops_per_launch": pflops},
         "prefill_fp8": {"value": round(p8_tfs, 2), "unit": "TFLOP/s", "ms_per_call": round(p8_avg, 4),
                         "workload": pc.name + ", E4M3 q/k/v (scales 0.25, 0.25, 0.5), bf16 output",
@@ -544,6 +680,7 @@ def main():
                                      "kernel": "prefill_kernel (FP8 form: fp8 x fp8 products)",
                                      "algorithmic_flops_per_launch": pflops}},
         "decode": {"value": round(d_gbs, 1), "unit": "GB/s", "us_per_call": round(d_avg * 1e3, 2),
+                   "us_per_call_median": round(ms_med["decode"] * 1e3, 2), "us_per_call_min": round(ms_min["decode"] * 1e3, 2),
                    "roofline": {"bound": "hbm", "achieved": round(d_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                 "frac": round(d_gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic("decode"),
                                 "kernels": "decode_split_kernel + decode_combine_kernel",
@@ -613,6 +750,12 @@ def main():
                      "kernel": "gemm_splitk_kernel (gate/up projection, the largest launch)",
                      "algorithmic_bytes_per_launch": gbytes["gate_up_proj"]}}
     out["context"] = context_measurements(ta, W, torch, np, dev, flush_rows, flush_dst, evict)
+    out["context"]["clock_derived_peak"] = clock_derived_peak(torch)
+    rot_med, rot_min = decode_rotation_crosscheck(ta, torch, np, dq, kc, vc, bt, cl, dc.scale, ws)
+    out["context"]["decode_rotating_4_cache_copies"] = {
+        "us_per_call_median": round(rot_med, 2), "us_per_call_min": round(rot_min, 2),
+        "GB_per_s_median": round(dbytes / (rot_med * 1e-6) / 1e9, 1),
+        "what": "attn_decode_paged without the eviction pass, rotating 4 independent copies of the caches"}
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline: float64 oracle on a sample of the prefill workload")
         out["cpu_baseline"] = cpu_baseline_prefill(xp, pc)
@@ -631,6 +774,14 @@ def main():
         out["chunked_rope"]["cpu_baseline"] = cpu_baseline_chunked(xc, cc, rope=W.rope_table(16384, cc.D))
         log("[bench] cpu baseline: float64 oracle on the linear layers")
         out["gemm"]["cpu_baseline"] = cpu_baseline_gemm(gx)
+        log("[bench] parity of the timed calls' outputs against the oracle (sampled)")
+        pcalls = {name: call for name, call, _ in parts}
+        chunk_calls = [("chunked", pcalls["chunked_prefill"]), ("chunked_rope", pcalls["chunked_prefill_rope"]),
+                       ("chunked_fp8", pcalls["chunked_prefill_fp8"])]
+        out["parity_on_timed_buffers"] = parity_on_timed_buffers(
+            ta, torch, np, W, pc, xp, o, lse, xp8, (QS8, KSP8, VSP8), o8, lse8, dc, xd, do, dlse, xd8, KS8, VS8,
+            do8, dlse8, cc, xc, rope_tab, chunk_calls, co, clse, ck8.cpu().numpy(), cv8.cpu().numpy(), gx, gdev)
+        log(f"[bench] parity on timed buffers: all ok = {out['parity_on_timed_buffers']['all_ok']}")
     print(json.dumps(out), flush=True)
 
 
