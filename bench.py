@@ -11,14 +11,22 @@ One step = one pass of the whole hot path on seeded synthetic inputs:
     sequences with cached prefixes ~ U[2048, 8192], Llama3-8B heads
     (attn_cache_append of the chunk's K/V into each of 8 layers' caches,
     then attn_fwd_paged on one of them), once plain and once with the rotary
-    embedding fused in (rotating append, rotated queries).
-Each call is timed with HIP events on the stream it runs on. Before each call
-(outside its events) a read pass over a 1 GiB buffer evicts the inputs from
-the 256 MB Infinity Cache and the L2s, so the timed call reads its inputs from
-HBM; a read pass leaves clean lines behind, whereas a write pass would leave a
-gigabyte of dirty lines whose write-back would land inside the timed region.
-"context" holds figures reported beside the headline ones: the Llama3-8B-shaped
-512-token prefill (launch-dominated) and the rate of a plain streaming read.
+    embedding fused in (rotating append, rotated queries), and once over E4M3
+    caches (quantizing append), and
+  * the long causal prefill's shape on E4M3 q, k, v (attn_fwd_fp8), and
+  * the four Llama3-8B linear layers at 2 activation rows (attn_gemm_splitk).
+Each call is timed with HIP events on the stream it runs on (mean, median and
+minimum over the timed steps). Before each call (outside its events) a read
+pass over a 1 GiB buffer evicts the inputs from the 256 MB Infinity Cache and
+the L2s, so the timed call reads its inputs from HBM; a read pass leaves clean
+lines behind, whereas a write pass would leave a gigabyte of dirty lines whose
+write-back would land inside the timed region. "context" holds figures
+reported beside the headline ones: the Llama3-8B-shaped 512-token prefill
+(launch-dominated, per call and back to back), the rate of a plain streaming
+read, the MFMA peak derived from the device's CU count and clock, the decode
+timed over 4 rotating cache copies instead of the eviction pass, and the host
+processor. After timing, the outputs of the timed calls are compared with the
+float64 oracle ("parity_on_timed_buffers").
 
 Prints ONE JSON line. value = prefill TFLOP/s (algorithmic flops: 4*D per
 unmasked query/key pair); the decode figure (algorithmic HBM bytes: K and V of
@@ -83,8 +91,8 @@ def measured_traffic(kind):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-flush", action="store_true", help="skip the cache flush between calls")
     p.add_argument("--only", choices=["prefill", "prefill_fp8", "decode", "decode_fp8", "chunked", "gemm"],
@@ -106,6 +114,20 @@ def _oracle_threads():
         return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
     except Exception:
         return len(os.sched_getaffinity(0))
+
+
+def host_cpu():
+    """The host processor the oracle runs on: model name and usable cores."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "usable_cores": len(os.sched_getaffinity(0)), "oracle_threads": _oracle_threads()}
 
 
 def cpu_baseline_prefill(x, case, budget_heads=32, row_stride=8):
@@ -751,6 +773,7 @@ def main():
                      "algorithmic_bytes_per_launch": gbytes["gate_up_proj"]}}
     out["context"] = context_measurements(ta, W, torch, np, dev, flush_rows, flush_dst, evict)
     out["context"]["clock_derived_peak"] = clock_derived_peak(torch)
+    out["context"]["host_cpu"] = host_cpu()
     rot_med, rot_min = decode_rotation_crosscheck(ta, torch, np, dq, kc, vc, bt, cl, dc.scale, ws)
     out["context"]["decode_rotating_4_cache_copies"] = {
         "us_per_call_median": round(rot_med, 2), "us_per_call_min": round(rot_min, 2),
