@@ -5,8 +5,9 @@ past 2^32. Here each cache holds 600,000 blocks of 16 tokens x 2 kv heads x 128 
 1,100,000 blocks, 4.5 GB, for the E4M3 form), and every block a sequence uses lies past byte 2^32 of
 its cache (the last block of the cache included). The oracle works on compact caches that hold only
 those blocks, with the block table renumbered; the GPU copies them to their high physical ids. Covered:
-decode (16-bit and E4M3), append into the high blocks (16-bit, rotary, E4M3) and the chunked prefill
-over them. The rest of each large cache is never written nor read.
+decode (16-bit and E4M3), append into the high blocks (16-bit and E4M3) and the chunked prefill over
+them. The rest of each large cache is never written nor read. A last case runs the contiguous prefill
+on K and V tensors of 2.3 GB each (rows past byte 2^31).
 """
 import numpy as np
 import pytest
@@ -152,3 +153,35 @@ def test_append_and_chunked_prefill_past_4_gib(ta):
              what="chunked prefill over E4M3 caches past 4 GiB")
     del kc8, vc8
     _free()
+
+
+def test_prefill_kv_past_2_gib(ta):
+    """Contiguous K and V of 1.15e9 elements each (2.3 GB in bf16), so key rows sit past byte 2^31 of the
+    tensor: 32 queries per head against 4.5M keys, non-causal. K/V repeat a random block of 1,000,003 rows
+    (a prime period, so an offset that wrapped would read other rows) and the last 1000 keys of each head
+    are drawn apart with three times the spread, so they dominate the softmax. Sampled rows against the
+    oracle."""
+    import torch
+    Hq, Hkv, D, Tk, Tq, P = 4, 2, 128, 4_500_000, 32, 1_000_003
+    assert Hkv * Tk * D < 2 ** 31 and Hkv * Tk * D * 2 > 2 ** 31
+    rng = np.random.default_rng(99)
+    q = W.round_to(rng.standard_normal((1, Hq, Tq, D), dtype=np.float32), "bf16")
+    kv = []
+    for _ in range(2):
+        base = W.round_to(rng.standard_normal((Hkv, P, D), dtype=np.float32), "bf16")
+        t = np.tile(base, (1, -(-Tk // P), 1))[:, :Tk]
+        t[:, -1000:] = W.round_to(3.0 * rng.standard_normal((Hkv, 1000, D), dtype=np.float32), "bf16")
+        kv.append(np.ascontiguousarray(t[None]))
+        del base, t
+    k, v = kv
+    _note(f"[case] prefill with K/V of {k.size} elements each (Tk={Tk})")
+    scale = 1.0 / np.sqrt(D)
+    o, lse = ta.attn_fwd(_dev(q, "bf16"), _dev(k, "bf16"), _dev(v, "bf16"), scale=scale, causal=False)
+    torch.cuda.synchronize()
+    o, lse = o.float().cpu().numpy(), lse.cpu().numpy()
+    _free()
+    picks = np.array([(0, h, i) for h in (0, 3) for i in (0, 17, 31)])
+    o_ref, lse_ref = O.prefill_rows(q, k, v, scale, False, None, picks)
+    og = o[picks[:, 0], picks[:, 1], picks[:, 2]]
+    lg = lse[picks[:, 0], picks[:, 1], picks[:, 2]]
+    _compare(og, lg, o_ref, lse_ref, "bf16", what="prefill with K/V past 2 GiB")
