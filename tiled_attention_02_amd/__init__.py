@@ -8,6 +8,7 @@ no fallback path. If the shared library is missing, loading fails loudly.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 import os
@@ -115,6 +116,19 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+@contextlib.contextmanager
+def _on(first, *others):
+    """Makes the device of `first` current for a library call (the C library launches on the current HIP
+    device) after checking that every other tensor argument lives on that device."""
+    import torch
+    dev = first.device
+    for t in others:
+        if t is not None:
+            _check(t.device == dev, f"every tensor must be on {dev} (found one on {t.device})")
+    with torch.cuda.device(dev):
+        yield
+
+
 def _raise(status):
     if status != ATTN_OK:
         raise AttnError(status, attn_last_error())
@@ -148,8 +162,9 @@ def attn_fwd(q, k, v, scale: float | None = None, causal: bool = False, seq_lens
     if seq_lens is not None:
         _check(seq_lens.is_cuda and seq_lens.dtype == torch.int32 and seq_lens.numel() == B
                and seq_lens.is_contiguous(), "seq_lens must be a contiguous int32 GPU tensor [B]")
-    st = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Tq, Tk, D,
-                        ctypes.c_float(scale), int(bool(causal)), _ptr(seq_lens), dt, _stream(q.device))
+    with _on(q, k, v, out, lse, seq_lens):
+        st = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Tq, Tk, D,
+                            ctypes.c_float(scale), int(bool(causal)), _ptr(seq_lens), dt, _stream(q.device))
     _raise(st)
     return out, lse
 
@@ -178,9 +193,10 @@ def attn_fwd_fp8(q, k, v, q_scale: float, k_scale: float, v_scale: float, scale:
     if seq_lens is not None:
         _check(seq_lens.is_cuda and seq_lens.dtype == torch.int32 and seq_lens.numel() == B
                and seq_lens.is_contiguous(), "seq_lens must be a contiguous int32 GPU tensor [B]")
-    st = lib().attn_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), ctypes.c_float(q_scale), ctypes.c_float(k_scale),
-                            ctypes.c_float(v_scale), _ptr(out), _ptr(lse), B, Hq, Hkv, Tq, Tk, D, ctypes.c_float(scale),
-                            int(bool(causal)), _ptr(seq_lens), dt, _stream(q.device))
+    with _on(q, k, v, out, lse, seq_lens):
+        st = lib().attn_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), ctypes.c_float(q_scale), ctypes.c_float(k_scale),
+                                ctypes.c_float(v_scale), _ptr(out), _ptr(lse), B, Hq, Hkv, Tq, Tk, D, ctypes.c_float(scale),
+                                int(bool(causal)), _ptr(seq_lens), dt, _stream(q.device))
     _raise(st)
     return out, lse
 
@@ -255,14 +271,15 @@ def _decode(q, k_cache, v_cache, scales, block_table, ctx_lens, scale, out, lse,
         workspace = decode_workspace(q.device, need)
     tail = (_ptr(out), _ptr(lse), B, Hq, Hkv, D, bs, maxb, NB, ctypes.c_float(scale), dt, _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream(q.device))
-    if rope is not None:
-        st = lib().attn_decode_paged_rope(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(rope), _check_rope(rope, D),
-                                          _ptr(block_table), _ptr(ctx_lens), *tail)
-    elif scales is None:
-        st = lib().attn_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(ctx_lens), *tail)
-    else:
-        st = lib().attn_decode_paged_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.c_float(scales[0]),
-                                         ctypes.c_float(scales[1]), _ptr(block_table), _ptr(ctx_lens), *tail)
+    with _on(q, k_cache, v_cache, block_table, ctx_lens, out, lse, workspace, rope):
+        if rope is not None:
+            st = lib().attn_decode_paged_rope(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(rope), _check_rope(rope, D),
+                                              _ptr(block_table), _ptr(ctx_lens), *tail)
+        elif scales is None:
+            st = lib().attn_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(ctx_lens), *tail)
+        else:
+            st = lib().attn_decode_paged_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.c_float(scales[0]),
+                                             ctypes.c_float(scales[1]), _ptr(block_table), _ptr(ctx_lens), *tail)
     _raise(st)
     return out, lse
 
@@ -325,14 +342,15 @@ def _fwd_paged(q, k_cache, v_cache, scales, block_table, ctx_lens, q_lens, scale
         _check(lse.shape == (B, Hq, Tq) and lse.dtype == torch.float32 and lse.is_contiguous(), "bad lse")
     tail = (_ptr(block_table), _ptr(ctx_lens), _ptr(q_lens), _ptr(out), _ptr(lse), B, Hq, Hkv, Tq, D, bs,
             block_table.shape[1], NB, ctypes.c_float(scale), int(bool(causal)), dt, _stream(q.device))
-    if scales is not None:
-        max_pos = _check_rope(rope, D) if rope is not None else 0
-        st = lib().attn_fwd_paged_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.c_float(scales[0]),
-                                      ctypes.c_float(scales[1]), _ptr(rope), max_pos, *tail)
-    elif rope is not None:
-        st = lib().attn_fwd_paged_rope(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(rope), _check_rope(rope, D), *tail)
-    else:
-        st = lib().attn_fwd_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), *tail)
+    with _on(q, k_cache, v_cache, block_table, ctx_lens, q_lens, out, lse, rope):
+        if scales is not None:
+            max_pos = _check_rope(rope, D) if rope is not None else 0
+            st = lib().attn_fwd_paged_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.c_float(scales[0]),
+                                          ctypes.c_float(scales[1]), _ptr(rope), max_pos, *tail)
+        elif rope is not None:
+            st = lib().attn_fwd_paged_rope(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(rope), _check_rope(rope, D), *tail)
+        else:
+            st = lib().attn_fwd_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), *tail)
     _raise(st)
     return out, lse
 
@@ -353,11 +371,12 @@ def attn_cache_append(k_new, v_new, k_cache, v_cache, block_table, start_pos, ne
     _check_i32(new_lens, B, "new_lens", optional=True)
     tail = (_ptr(block_table), _ptr(start_pos), _ptr(new_lens), B, Hkv, Tnew, D, bs, block_table.shape[1], NB, dt,
             _stream(k_new.device))
-    if rope is not None:
-        st = lib().attn_cache_append_rope(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(rope),
-                                          _check_rope(rope, D), *tail)
-    else:
-        st = lib().attn_cache_append(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), *tail)
+    with _on(k_new, v_new, k_cache, v_cache, block_table, start_pos, new_lens, rope):
+        if rope is not None:
+            st = lib().attn_cache_append_rope(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(rope),
+                                              _check_rope(rope, D), *tail)
+        else:
+            st = lib().attn_cache_append(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), *tail)
     _raise(st)
 
 
@@ -377,9 +396,10 @@ def attn_cache_append_fp8(k_new, v_new, k_cache, v_cache, k_scale: float, v_scal
     _check_i32(block_table, block_table.numel(), "block_table")
     _check_i32(start_pos, B, "start_pos")
     _check_i32(new_lens, B, "new_lens", optional=True)
-    st = lib().attn_cache_append_fp8(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), ctypes.c_float(k_scale),
-                                     ctypes.c_float(v_scale), _ptr(block_table), _ptr(start_pos), _ptr(new_lens), B,
-                                     Hkv, Tnew, D, bs, block_table.shape[1], NB, dt, _stream(k_new.device))
+    with _on(k_new, v_new, k_cache, v_cache, block_table, start_pos, new_lens):
+        st = lib().attn_cache_append_fp8(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), ctypes.c_float(k_scale),
+                                         ctypes.c_float(v_scale), _ptr(block_table), _ptr(start_pos), _ptr(new_lens), B,
+                                         Hkv, Tnew, D, bs, block_table.shape[1], NB, dt, _stream(k_new.device))
     _raise(st)
 
 
@@ -398,11 +418,12 @@ def attn_gemm_splitk(x, w, out=None, config=None):
     if out is None:
         out = torch.empty((M, N), dtype=x.dtype, device=x.device)
     _check(out.shape == (M, N) and out.dtype == x.dtype and out.is_contiguous(), "out must be [M, N] like x")
-    if config is None:
-        st = lib().attn_gemm_splitk(_ptr(x), _ptr(w), _ptr(out), M, N, K, dt, _stream(x.device))
-    else:
-        rows, waves, unroll = config
-        st = lib().attn_gemm_splitk_cfg(_ptr(x), _ptr(w), _ptr(out), M, N, K, dt, rows, waves, unroll,
-                                        _stream(x.device))
+    with _on(x, w, out):
+        if config is None:
+            st = lib().attn_gemm_splitk(_ptr(x), _ptr(w), _ptr(out), M, N, K, dt, _stream(x.device))
+        else:
+            rows, waves, unroll = config
+            st = lib().attn_gemm_splitk_cfg(_ptr(x), _ptr(w), _ptr(out), M, N, K, dt, rows, waves, unroll,
+                                            _stream(x.device))
     _raise(st)
     return out
