@@ -389,8 +389,19 @@ def decode_rotation_crosscheck(ta, torch, np, dq, kc, vc, bt, cl, scale, ws, cop
         e1.record()
         torch.cuda.synchronize()
         ts.append(e0.elapsed_time(e1))
+    # the same calls back to back, as a model's layers would make them (one call per layer's cache, no
+    # events between): one event pair around each pass over the copies
+    bursts = []
+    for r in range(max(1, reps // copies)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(copies):
+            ta.attn_decode_paged(dq, kcs[i], vcs[i], bt, cl, scale=scale, out=out, lse=lse, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        bursts.append(e0.elapsed_time(e1) / copies)
     del kcs, vcs
-    return float(np.median(ts)) * 1e3, float(np.min(ts)) * 1e3
+    return float(np.median(ts)) * 1e3, float(np.min(ts)) * 1e3, float(np.median(bursts)) * 1e3
 
 
 def context_measurements(ta, W, torch, np, dev, flush_rows, flush_dst, evict):
@@ -774,11 +785,15 @@ def main():
     out["context"] = context_measurements(ta, W, torch, np, dev, flush_rows, flush_dst, evict)
     out["context"]["clock_derived_peak"] = clock_derived_peak(torch)
     out["context"]["host_cpu"] = host_cpu()
-    rot_med, rot_min = decode_rotation_crosscheck(ta, torch, np, dq, kc, vc, bt, cl, dc.scale, ws)
+    rot_med, rot_min, burst = decode_rotation_crosscheck(ta, torch, np, dq, kc, vc, bt, cl, dc.scale, ws)
     out["context"]["decode_rotating_4_cache_copies"] = {
         "us_per_call_median": round(rot_med, 2), "us_per_call_min": round(rot_min, 2),
         "GB_per_s_median": round(dbytes / (rot_med * 1e-6) / 1e9, 1),
-        "what": "attn_decode_paged without the eviction pass, rotating 4 independent copies of the caches"}
+        "us_per_call_back_to_back": round(burst, 2),
+        "GB_per_s_back_to_back": round(dbytes / (burst * 1e-6) / 1e9, 1),
+        "what": "attn_decode_paged without the eviction pass, rotating 4 independent copies of the caches: "
+                "events around each call, and around passes of 4 back-to-back calls (one per copy, as a "
+                "model's layers make them) divided by 4"}
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline: float64 oracle on a sample of the prefill workload")
         out["cpu_baseline"] = cpu_baseline_prefill(xp, pc)
