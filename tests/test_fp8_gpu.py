@@ -103,10 +103,13 @@ def test_fp8_decode_extreme_codes(ta):
     del torch
 
 
-def test_fp8_decode_equals_16bit_decode_of_dequantized_cache(ta):
+def test_fp8_decode_matches_16bit_decode_of_dequantized_cache(ta):
     """Power-of-two scales: the FP8 decode and the 16-bit decode over the dequantized values (exact in bf16)
-    agree bit for bit: both kernels take the same online-softmax steps, and the scales fold out of the
-    products exactly."""
+    compute the same scores (the scales fold out exactly); the E4M3 kernel takes 64-token steps and the
+    16-bit one 32-token steps, so their running maxima, and with them the bf16 roundings of the
+    probabilities, can differ: each O is within 2^-8 max|v| of the exact weighted mean from that rounding,
+    so the two agree within 2^-7 max|v| plus one unit in the last place; lse (fp32 sums of the unrounded
+    probabilities) within 1e-6 relative."""
     import torch
     case = W.DecodeCase("fp8 vs bf16", B=16, Hq=12, Hkv=2, D=128, dtype="bf16", ctx_lo=1, ctx_hi=3000, seed=86)
     x = W.decode_inputs_fp8(case, nan_fill=False)
@@ -118,7 +121,14 @@ def test_fp8_decode_equals_16bit_decode_of_dequantized_cache(ta):
     o16, l16 = ta.attn_decode_paged(_dev(x["q"], "bf16"), _dev(kd, "bf16"), _dev(vd, "bf16"),
                                     _i32(x["block_table"]), _i32(x["ctx_lens"]), scale=case.scale)
     torch.cuda.synchronize()
-    assert np.array_equal(o8, o16.float().cpu().numpy()) and np.array_equal(l8, l16.cpu().numpy())
+    o16 = o16.float().cpu().numpy()
+    l16 = l16.cpu().numpy()
+    ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(o16), 2.0 ** -126))) - 7)
+    same = float((o8 == o16).mean())
+    _note(f"[parity] fp8 vs 16-bit decode: max |dO| = {float(np.abs(o8 - o16).max()):.2e}, "
+          f"{100 * same:.2f} % identical, max rel dlse = {float((np.abs(l8 - l16) / np.abs(l16)).max()):.2e}")
+    assert (np.abs(o8 - o16) <= 2.0 ** -7 * float(np.abs(vd).max()) + ulp).all()
+    assert (np.abs(l8 - l16) <= 1e-6 * np.maximum(1.0, np.abs(l16))).all()
 
 
 # ---------------------------------------------------------------- quantizing append vs the oracle
