@@ -77,8 +77,8 @@ def test_fp8_decode_head_layouts(ta, Hq, Hkv, D, dtype, ks, vs):
     _decode_fp8_check(ta, case, ks, vs, what=f"Hq={Hq} Hkv={Hkv} D={D} {dtype}")
 
 
-@pytest.mark.parametrize("ctx", [[1, 2, 15, 16, 17, 31, 32, 33], [255, 256, 257, 511, 512, 513, 1000, 4096],
-                                 [33000, 20481, 4097, 12800]])
+@pytest.mark.parametrize("ctx", [[1, 2, 15, 16, 17, 31, 32, 33], [48, 63, 64, 65, 127, 128, 129, 192],
+                                 [255, 256, 257, 511, 512, 513, 1000, 4096], [33000, 20481, 4097, 12800]])
 def test_fp8_decode_context_edges(ta, ctx):
     case = W.DecodeCase("fp8 edges", B=len(ctx), Hq=12, Hkv=2, D=128, dtype="bf16", ctx_lo=1, ctx_hi=4096, seed=83)
     _decode_fp8_check(ta, case, 0.3, 0.7, ctx_lens=ctx, what=f"ctx={ctx}")

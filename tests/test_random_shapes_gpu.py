@@ -4,7 +4,8 @@ Each case draws its configuration from its own seed (numpy default_rng), so a fa
 reproducible case: prefill (batch, heads with GQA groups 1-8, Tq / Tk from 1 to 300 including
 Tq != Tk, D 64 / 128, bf16 / fp16, causal or not, ragged or not, scale drawn from a wide range),
 paged decode (context lengths 1 to 2000 mixed within a batch, head layouts, scale), chunked prefill
-(prefixes 0 to 1500, chunks 0 to 200) and the split-K GEMM (M 1 to 40, N 1 to 700, K a multiple of 8
+(prefixes 0 to 1500, chunks 0 to 200), decode over E4M3 caches (contexts 1 to 2000, scales drawn
+over four decades) and the split-K GEMM (M 1 to 40, N 1 to 700, K a multiple of 8
 up to 3000, a random configuration). Tolerances are those of the hand-picked parity tests.
 """
 import numpy as np
@@ -14,6 +15,7 @@ import workloads as W
 from oracle import gemm as G
 from oracle import oracle as O
 from test_chunked_gpu import _chunk_check
+from test_fp8_gpu import _decode_fp8_check
 from test_parity_gpu import _compare, _decode_check, _note, _run_prefill
 
 pytestmark = pytest.mark.gpu
@@ -71,6 +73,22 @@ def test_random_decode(ta, seed):
     case = W.DecodeCase(f"random decode {seed}", B=B, Hq=hq, Hkv=hkv, D=D, dtype=dtype, ctx_lo=1,
                         ctx_hi=int(ctx.max()), seed=seed, scale=scale)
     _decode_check(ta, case, ctx_lens=ctx, scale=scale, what=f"random decode {seed} Hq={hq} Hkv={hkv} D={D} {dtype}")
+
+
+@pytest.mark.parametrize("seed", range(5000, 5024))
+def test_random_fp8_decode(ta, seed):
+    rng = np.random.default_rng(seed)
+    hq, hkv = _heads(rng)
+    D = int(rng.choice([64, 128]))
+    dtype = str(rng.choice(["bf16", "fp16"]))
+    B = int(rng.integers(1, 9))
+    ctx = rng.integers(1, 2001, B)
+    ctx[rng.integers(0, B)] = int(rng.choice([1, 63, 64, 65, 256, 2000]))
+    ks, vs = (float(10.0 ** rng.uniform(-3, 1)) for _ in range(2))
+    case = W.DecodeCase(f"random fp8 decode {seed}", B=B, Hq=hq, Hkv=hkv, D=D, dtype=dtype, ctx_lo=1,
+                        ctx_hi=int(ctx.max()), seed=seed)
+    _decode_fp8_check(ta, case, ks, vs, ctx_lens=ctx,
+                      what=f"random fp8 decode {seed} Hq={hq} Hkv={hkv} D={D} {dtype} ks={ks:.3g} vs={vs:.3g}")
 
 
 @pytest.mark.parametrize("seed", range(3000, 3024))
