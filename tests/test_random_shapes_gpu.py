@@ -5,18 +5,22 @@ reproducible case: prefill (batch, heads with GQA groups 1-8, Tq / Tk from 1 to 
 Tq != Tk, D 64 / 128, bf16 / fp16, causal or not, ragged or not, scale drawn from a wide range),
 paged decode (context lengths 1 to 2000 mixed within a batch, head layouts, scale), chunked prefill
 (prefixes 0 to 1500, chunks 0 to 200), decode over E4M3 caches (contexts 1 to 2000, scales drawn
-over four decades) and the split-K GEMM (M 1 to 40, N 1 to 700, K a multiple of 8
+over four decades), chunked prefill with the rotary embedding fused and over E4M3 caches, and the
+split-K GEMM (M 1 to 40, N 1 to 700, K a multiple of 8
 up to 3000, a random configuration). Tolerances are those of the hand-picked parity tests.
 """
 import numpy as np
 import pytest
 
 import workloads as W
+from oracle import fp8 as F8
 from oracle import gemm as G
 from oracle import oracle as O
+from oracle import rope as R
 from test_chunked_gpu import _chunk_check
-from test_fp8_gpu import _decode_fp8_check
-from test_parity_gpu import _compare, _decode_check, _note, _run_prefill
+from test_fp8_gpu import _decode_fp8_check, _fp8_chunk_inputs
+from test_parity_gpu import _compare, _decode_check, _dev, _note, _run_prefill
+from test_rope_gpu import _append as _rope_append, _check_append, _table
 
 pytestmark = pytest.mark.gpu
 
@@ -127,3 +131,64 @@ def test_random_gemm(ta, seed):
     ratio = float((err / G.error_bound(d["x"], d["w"], dtype)).max())
     _note(f"[parity] random gemm {seed}: max err/bound={ratio:.3f}")
     assert ratio <= 1.0
+
+
+def _chunk_case(rng, seed, name):
+    hq, hkv = _heads(rng)
+    D = int(rng.choice([64, 128]))
+    dtype = str(rng.choice(["bf16", "fp16"]))
+    B = int(rng.integers(1, 5))
+    starts = [int(v) for v in rng.integers(0, 1501, B)]
+    lens = [int(v) for v in rng.integers(1, 201, B)]
+    causal = bool(rng.integers(0, 4) != 0)
+    case = W.ChunkCase(f"{name} {seed}", B=B, Hq=hq, Hkv=hkv, D=D, dtype=dtype, ctx_lo=0, ctx_hi=1500,
+                       chunk_lo=1, chunk_hi=max(lens), seed=seed)
+    return case, starts, lens, causal
+
+
+@pytest.mark.parametrize("seed", range(6000, 6012))
+def test_random_rope_chunked_prefill(ta, seed):
+    import torch
+    rng = np.random.default_rng(seed)
+    case, starts, lens, causal = _chunk_case(rng, seed, "random rope chunk")
+    x = W.chunk_inputs(case, nan_fill=True, starts=starts, lens=lens)
+    tab, tab_d = _table(case.D)
+    what = f"random rope chunk {seed} Hq={case.Hq} Hkv={case.Hkv} D={case.D} {case.dtype} causal={causal}"
+    _note(f"[case] {what} start={starts} n={lens}")
+    kc, vc = _rope_append(ta, x, case.dtype, tab_d)
+    kref, vref = R.cache_append_rope(x["k_new"], x["v_new"], x["k_cache"], x["v_cache"], x["block_table"],
+                                     x["start_pos"], tab, case.dtype, x["new_lens"])
+    _check_append(kc, vc, kref, vref, case.dtype, what)
+    o, lse = ta.attn_fwd_paged(_dev(x["q"], case.dtype), kc, vc, _i32(x["block_table"]), _i32(x["ctx_lens"]),
+                               _i32(x["new_lens"]), scale=case.scale, causal=causal, rope=tab_d)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = R.prefill_paged_rope(x["q"], kref, vref, x["block_table"], x["ctx_lens"], x["new_lens"], tab,
+                                          case.scale, case.dtype, causal)
+    _compare(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, case.dtype, what=what)
+
+
+@pytest.mark.parametrize("seed", range(7000, 7012))
+def test_random_fp8_chunked_prefill(ta, seed):
+    import torch
+    rng = np.random.default_rng(seed)
+    case, starts, lens, causal = _chunk_case(rng, seed, "random fp8 chunk")
+    case = W.ChunkCase(case.name, B=case.B, Hq=case.Hq, Hkv=case.Hkv, D=case.D, dtype=case.dtype, ctx_lo=0,
+                       ctx_hi=1500, chunk_lo=1, chunk_hi=200, seed=seed)
+    x, k8, v8 = _fp8_chunk_inputs(case, seed + 1)
+    # v_scale at most 10^-0.5: the values stay within a few units (codes up to 7.5), the regime the absolute
+    # O tolerances are stated for (a larger v_scale scales the rounding error of P with it)
+    ks, vs = float(10.0 ** rng.uniform(-3, 1)), float(10.0 ** rng.uniform(-3, -0.5))
+    what = f"random fp8 chunk {seed} Hq={case.Hq} Hkv={case.Hkv} D={case.D} {case.dtype} causal={causal}"
+    _note(f"[case] {what} ctx={x['ctx_lens'].tolist()} n={x['new_lens'].tolist()} ks={ks:.3g} vs={vs:.3g}")
+    u8 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    o, lse = ta.attn_fwd_paged_fp8(_dev(x["q"], case.dtype), u8(k8), u8(v8), ks, vs, _i32(x["block_table"]),
+                                   _i32(x["ctx_lens"]), _i32(x["new_lens"]), scale=case.scale, causal=causal)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = F8.prefill_paged_fp8(x["q"], k8, v8, ks, vs, x["block_table"], x["ctx_lens"], x["new_lens"],
+                                          case.scale, causal)
+    _compare(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, case.dtype, what=what)
+
+
+def _i32(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
