@@ -26,9 +26,16 @@
  *    fallback (the same page notes that hard-coding a backend must fail when
  *    no backend supports the inputs). A failed launch returns ATTN_ERR_HIP.
  *    attn_last_error() returns a per-thread message for the last non-OK status.
- *  - Device-resident values (seq_lens, ctx_lens, block ids) are trusted:
- *    checking them would need a synchronisation. Out-of-range values there are
- *    undefined behaviour.
+ *  - Device-resident lengths (seq_lens, ctx_lens, q_lens, start_pos,
+ *    new_lens) are trusted: checking them would need a synchronisation; values
+ *    outside the ranges stated below are undefined behaviour.
+ *  - Block ids: one rule for every call that takes a block table. An entry
+ *    used for a block inside a sequence's context should lie in
+ *    [0, num_blocks). Any other value marks an unmapped block: the appends
+ *    write nothing to it, and the attention calls read its keys and values as
+ *    zeros. No call ever reads or writes memory outside the caches because of
+ *    a block id. Entries for blocks past a sequence's context may be loaded
+ *    but are never used.
  *  - Alignment: q, k, v, o, k_cache, v_cache must be 16-byte aligned.
  *  - Numerics: products accumulate in fp32; the probabilities are rounded to
  *    the input dtype for the P.V product; O is rounded to the input dtype
@@ -91,13 +98,15 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
  *  k_cache,
  *  v_cache     : [num_blocks, Hkv, block_size, D] elements of `dtype`, so every
  *                (block, kv head) holds block_size*D contiguous elements.
- *  block_table : device int32 [B, max_blocks_per_seq]; entries at or beyond
- *                ceil(ctx_lens[b] / block_size) are never read.
+ *  block_table : device int32 [B, max_blocks_per_seq], 4-byte aligned; block
+ *                ids follow the rule above (entries at or beyond
+ *                ceil(ctx_lens[b] / block_size) are never used).
  *  ctx_lens    : device int32 [B]; 1 <= ctx_lens[b] <= max_blocks_per_seq *
  *                block_size. It counts every cached token including the new
  *                one, whose key/value are already in the cache: the query sees
  *                positions 0 .. ctx_lens[b]-1. Slots beyond it are never used.
- *  lse         : [B, Hq] fp32 natural-log log-sum-exp; may be NULL.
+ *  lse         : [B, Hq] fp32 natural-log log-sum-exp; may be NULL; 4-byte
+ *                aligned (ctx_lens too).
  *  block_size == 16, D in {64, 128}, Hq % Hkv == 0, Hq / Hkv <= 16.
  *  workspace   : device scratch of at least attn_decode_workspace_bytes(...)
  *                bytes, 256-byte aligned, owned by the caller; contents on
@@ -129,9 +138,9 @@ attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_
  *  v_cache     : [num_blocks, Hkv, block_size, D] as for attn_decode_paged;
  *                the keys/values of positions 0 .. ctx_lens[b]-1 must be in
  *                the cache (the chunk's own included).
- *  block_table : device int32 [B, max_blocks_per_seq]; entries at or beyond
- *                ceil(ctx_lens[b] / block_size) are never read; entries read
- *                must lie in [0, num_blocks) (others are clamped into it).
+ *  block_table : device int32 [B, max_blocks_per_seq], 4-byte aligned; block
+ *                ids follow the rule above (entries at or beyond
+ *                ceil(ctx_lens[b] / block_size) are never used).
  *  ctx_lens    : device int32 [B]; q_lens[b] <= ctx_lens[b] <=
  *                max_blocks_per_seq * block_size.
  *  q_lens      : device int32 [B] with 0 <= q_lens[b] <= Tq, or NULL (every
@@ -160,9 +169,10 @@ attn_status attn_fwd_paged(const void* q, const void* k_cache, const void* v_cac
  *  k_new, v_new: [B, Hkv, Tnew, D] elements of `dtype`.
  *  k_cache,
  *  v_cache     : [num_blocks, Hkv, block_size, D], updated in place.
- *  block_table : device int32 [B, max_blocks_per_seq]; the blocks written must
- *                be mapped (entries in [0, num_blocks)); a token whose position
- *                falls outside the table or on an unmapped entry is not written.
+ *  block_table : device int32 [B, max_blocks_per_seq], 4-byte aligned; the
+ *                blocks written must be mapped (entries in [0, num_blocks));
+ *                a token whose position falls outside the table or on an
+ *                unmapped entry is not written (the block-id rule above).
  *  start_pos   : device int32 [B], first position written (>= 0).
  *  new_lens    : device int32 [B] with 0 <= new_lens[b] <= Tnew, or NULL (all
  *                Tnew tokens).
@@ -217,11 +227,16 @@ attn_status attn_decode_paged_fp8(const void* q, const void* k_cache, const void
  * > 0); o is `dtype` (bf16 or fp16), lse fp32. Both products run on the fp8
  * matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4), twice the bf16 rate; the
  * scores are exact up to fp32 accumulation. The probabilities enter the P.V
- * product as E4M3 values (p * 2^8 rounded to nearest; p <= 1 since the running
- * max is kept exact), and O is divided by the fp32 sum of the unrounded p: per
- * output element the error against attention over the dequantized inputs is
- * at most (2^-4 + L * 2^-18) * max |v| for L visible keys, plus the output
- * rounding. Same masking, ragged and GQA rules as attn_fwd.
+ * product as E4M3 values: the running max moves only once a score exceeds it
+ * by more than 1 (log2 units), so p = 2^(x - m) <= 2, and p * 2^7 (<= 2^8) is
+ * rounded to nearest; O is divided by the fp32 sum of the unrounded p. Per
+ * output element (row i, column d) the error against attention over the
+ * dequantized inputs is then at most
+ *   2^-4 * sum_j P_ij |v_jd| + 2^-17 * max_j P_ij * sum_j |v_jd|
+ * over the row's visible keys j (P the exact softmax: each weight is off by
+ * 2^-4 relative in E4M3's normal range, 2^-17 absolute below it), plus the
+ * fp32 accumulation and the output rounding. Same masking, ragged and GQA
+ * rules as attn_fwd.
  */
 attn_status attn_fwd_fp8(const void* q, const void* k, const void* v, float q_scale, float k_scale,
                          float v_scale, void* o, float* lse, int B, int Hq, int Hkv, int Tq, int Tk,

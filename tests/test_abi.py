@@ -197,3 +197,46 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(ta, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(ImportError):
         ta.lib()
+
+
+_NO_DEVICE_SCRIPT = r"""
+import ctypes, sys
+sys.path.insert(0, sys.argv[1])
+import tiled_attention_02_amd as ta
+L = ta.lib()
+F = ctypes.c_void_p(0x10000)
+f = ctypes.c_float
+calls = {
+    "attn_fwd": lambda: L.attn_fwd(F, F, F, F, None, 1, 4, 2, 8, 8, 128, f(0.1), 1, None, 1, None),
+    "attn_fwd_fp8": lambda: L.attn_fwd_fp8(F, F, F, f(1), f(1), f(1), F, None, 1, 4, 2, 8, 8, 128, f(0.1), 1, None,
+                                           1, None),
+    "attn_decode_paged": lambda: L.attn_decode_paged(F, F, F, F, F, F, None, 2, 12, 2, 128, 16, 64, 100, f(0.1), 1,
+                                                     F, 1 << 30, None),
+    "attn_decode_paged_fp8": lambda: L.attn_decode_paged_fp8(F, F, F, f(1), f(1), F, F, F, None, 2, 12, 2, 128, 16,
+                                                             64, 100, f(0.1), 1, F, 1 << 30, None),
+    "attn_fwd_paged": lambda: L.attn_fwd_paged(F, F, F, F, F, None, F, None, 2, 8, 2, 64, 128, 16, 64, 100,
+                                               f(0.1), 1, 1, None),
+    "attn_cache_append": lambda: L.attn_cache_append(F, F, F, F, F, F, None, 2, 2, 64, 128, 16, 64, 100, 1, None),
+    "attn_gemm_splitk": lambda: L.attn_gemm_splitk(F, F, F, 2, 4096, 4096, 1, None),
+}
+for name, call in calls.items():
+    st = call()
+    print(name, st, ta.attn_last_error())
+    assert st == 3, (name, st)
+    assert ta.attn_last_error().startswith(name + ": launch failed"), ta.attn_last_error()
+print("ALL_HIP_ERRORS")
+"""
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU device node is present: the call would launch")
+def test_valid_call_without_a_device_returns_hip_error(L):
+    """A well-formed call (every host check passes) on a machine with no GPU: the launch itself fails and
+    the call returns ATTN_ERR_HIP with the runtime's message, instead of crashing or reporting success.
+    Runs only where no GPU device node exists, in a child process (the pointers are never dereferenced:
+    without a device nothing launches)."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, "-c", _NO_DEVICE_SCRIPT, ROOT], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "ALL_HIP_ERRORS" in r.stdout

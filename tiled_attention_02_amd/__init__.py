@@ -20,6 +20,7 @@ __all__ = ["attn_fwd", "attn_decode_paged", "attn_fwd_paged", "attn_cache_append
            "BLOCK_SIZE", "decode_workspace"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+LIB_SINGLE_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn_single.so")
 EXPORTS = ("attn_fwd", "attn_decode_paged", "attn_fwd_paged", "attn_cache_append", "attn_cache_append_fp8",
            "attn_decode_paged_fp8", "attn_fwd_paged_fp8", "attn_fwd_fp8", "attn_cache_append_rope",
            "attn_fwd_paged_rope", "attn_decode_paged_rope", "attn_decode_workspace_bytes", "attn_gemm_splitk",
@@ -41,12 +42,35 @@ class AttnError(RuntimeError):
 def lib() -> ctypes.CDLL:
     """Load libattn.so (built in-tree by tiled_attention_02_amd.build)."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m tiled_attention_02_amd.build` "
+    if _lib is None:
+        _lib = _load(LIB_PATH)
+    return _lib
+
+
+@contextlib.contextmanager
+def single_buffer_library():
+    """Routes the calls made inside the block to libattn_single.so: the same library built with the
+    prefill's debug key loop (one K and one V buffer, nothing overlapped), whose results must equal the
+    pipelined kernel's bit for bit. Test use only."""
+    global _lib
+    prev = lib()
+    _lib = _load(LIB_SINGLE_PATH)
+    try:
+        yield _lib
+    finally:
+        _lib = prev
+
+
+_loaded = {}
+
+
+def _load(path) -> ctypes.CDLL:
+    if path in _loaded:
+        return _loaded[path]
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m tiled_attention_02_amd.build` "
                           "(the HIP library is required; there is no fallback)")
-    L = ctypes.CDLL(LIB_PATH)
+    L = ctypes.CDLL(path)
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, i, vp]
     L.attn_fwd.restype = i
@@ -81,7 +105,7 @@ def lib() -> ctypes.CDLL:
     L.attn_status_str.restype = ctypes.c_char_p
     L.attn_last_error.argtypes = []
     L.attn_last_error.restype = ctypes.c_char_p
-    _lib = L
+    _loaded[path] = L
     return L
 
 

@@ -160,22 +160,26 @@ __device__ __forceinline__ void make_dec_offs(DecOffs<D, KV8>& o, int lane) {
 // buffer: buffer loads that write LDS directly, each instruction 1 KiB of
 // consecutive bytes of one block (whole rows). ph[j] is block j's physical
 // block; a block past the sequence's last one carries the step's first block
-// instead (a cache hit: every token there is masked or zeroed anyway).
+// instead (a cache hit: every token there is masked or zeroed anyway). An id
+// outside [0, num_blocks) is an unmapped block: its descriptor covers no bytes,
+// so the hardware writes zeros to LDS and nothing outside the caches is read.
 template <int D, bool KV8>
 __device__ __forceinline__ void load_step(char* buf, const char* kbase, const char* vbase, size_t block_stride,
-                                          const int (&ph)[StepLds<D, KV8>::NB], const DecOffs<D, KV8>& o) {
+                                          const int (&ph)[StepLds<D, KV8>::NB], int num_blocks,
+                                          const DecOffs<D, KV8>& o) {
   using L = StepLds<D, KV8>;
 #pragma unroll
   for (int j = 0; j < L::NB; ++j) {
-    const size_t off = (size_t)ph[j] * block_stride;
+    const bool mapped = (unsigned)ph[j] < (unsigned)num_blocks;
+    const size_t off = (size_t)(mapped ? ph[j] : 0) * block_stride;
 #pragma unroll
     for (int kv = 0; kv < 2; ++kv) {
       const uint64_t p = reinterpret_cast<uint64_t>((kv ? vbase : kbase) + off);
       // uniform by construction; readfirstlane keeps the descriptor scalar
       const uint64_t pu = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(p >> 32)) << 32) |
                           (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
-      const __amdgpu_buffer_rsrc_t rsrc =
-          __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(pu), (short)0, L::BLK, kDecodeDword3);
+      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          reinterpret_cast<void*>(pu), (short)0, mapped ? L::BLK : 0, kDecodeDword3);
       char* dst = buf + (L::NB * kv + j) * L::BLK;
       // the host compilation pass of this file does not know this builtin (it
       // would drop the kernels' host stubs); the function only runs on the device
@@ -338,7 +342,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 
   // The split's block-table entries are read together with the context
   // length (scalar loads, one round trip); entries at or beyond the sequence's
-  // end are read only if they exist in the table and never used.
+  // end may be read (if they exist in the table) but are never used.
   int phys[kSplitBlocks];
 #pragma unroll
   for (int i = 0; i < kSplitBlocks; ++i) phys[i] = trow[min(blk0 + i, a.max_blocks - 1)];
@@ -414,7 +418,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   {
     int ph[NB];
     step_blocks(0, ph);
-    load_step<D, KV8>(buf, kbase, vbase, block_stride, ph, o);
+    load_step<D, KV8>(buf, kbase, vbase, block_stride, ph, a.num_blocks, o);
   }
 
   if (a.rope) {
@@ -455,7 +459,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       const int q = p + 1 < NS ? p + 1 : 0;  // in range also where the branch is dead
       int ph[NB];
       step_blocks(q, ph);
-      load_step<D, KV8>(buf, kbase, vbase, block_stride, ph, o);
+      load_step<D, KV8>(buf, kbase, vbase, block_stride, ph, a.num_blocks, o);
     }
   }
 

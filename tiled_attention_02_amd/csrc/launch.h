@@ -65,6 +65,7 @@ struct DecodeArgs {
   float* ws;   // per-split partials: [B][Hq][nsplit][D + 4] fp32 (O, then log2-sum-exp, pad)
   int B, Hq, Hkv, G, D;
   int max_blocks;
+  int num_blocks;  // physical blocks in the caches: ids outside [0, num_blocks) read as zeros
   int nsplit;  // maximum number of splits per sequence
   float c;
   int qmode;

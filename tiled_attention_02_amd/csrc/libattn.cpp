@@ -82,6 +82,9 @@ attn_status decode_impl(const char* fn, bool fp8, const void* q, const void* k_c
     return fail(ATTN_ERR_UNSUPPORTED, "%s: sizes too large", fn);
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
     return fail(ATTN_ERR_INVALID, "%s: q, caches and o must be 16-byte aligned", fn);
+  if ((lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) || (reinterpret_cast<uintptr_t>(block_table) & 3u) ||
+      (reinterpret_cast<uintptr_t>(ctx_lens) & 3u))
+    return fail(ATTN_ERR_INVALID, "%s: lse, block_table and ctx_lens must be 4-byte aligned", fn);
   if (attn_status st = check_rope(fn, rope, max_pos, D); st != ATTN_OK) return st;
   const size_t need = attn::decode_workspace_bytes(B, Hq, Hkv, D, max_blocks_per_seq);
   const int nsplit = (max_blocks_per_seq + attn::kSplitBlocks - 1) / attn::kSplitBlocks;
@@ -110,6 +113,7 @@ attn_status decode_impl(const char* fn, bool fp8, const void* q, const void* k_c
   a.G = Hq / Hkv;
   a.D = D;
   a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
   a.nsplit = nsplit;
   a.k_scale = fp8 ? k_scale : 1.f;
   a.v_scale = fp8 ? v_scale : 1.f;
@@ -239,8 +243,8 @@ attn_status fwd_paged_impl(const char* fn, bool fp8, const void* q, const void* 
 
 // Linear-layer product: configurations tuned per weight shape. Each entry was
 // the fastest of every (rows, waves, unroll) configuration for its shape on
-// MI355X at M = 2 (the sweep of tiled_attention_02_amd/tune_gemm.py); other
-// shapes take kGemmDefault.
+// MI355X at M = 2 (an exhaustive sweep through attn_gemm_splitk_cfg, median of
+// 7 calls each after a cache eviction); other shapes take kGemmDefault.
 struct GemmTuned {
   int N, K;
   attn::GemmConfig cfg;

@@ -719,8 +719,8 @@ struct Stager {
       (void)e;
     } else {
       // one descriptor per cache block: its physical block, and only its rows
-      // below Lk (a block past the sequence gets none: nothing is read and the
-      // LDS rows receive zeros)
+      // below Lk (a block past the sequence, or an unmapped one (id -1 in the
+      // LDS table), gets none: nothing is read and the LDS rows receive zeros)
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
         int phys = e[i * JW];
@@ -728,7 +728,7 @@ struct Stager {
         for (int j = 1; j < JW; ++j)
           if (wblk == j) phys = e[i * JW + j];
         const int lb = k0 / 16 + i * JW + wblk;
-        const int rows = __builtin_amdgcn_readfirstlane(min(max(Lk - 16 * lb, 0), 16));
+        const int rows = __builtin_amdgcn_readfirstlane(phys < 0 ? 0 : min(max(Lk - 16 * lb, 0), 16));
         const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(base + (size_t)(rows > 0 ? phys : 0) * bstride), (short)0, rows * S::RB, kBufferDword3);
         load_lds(rsrc, tile + loff[i], voff[i]);
@@ -759,6 +759,30 @@ struct Stager {
 __device__ __forceinline__ void staged_barrier() {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+}
+
+// The end of a tile's arithmetic, shared by the pipelined and the debug key
+// loops: with 16-bit products, a lane whose 32 probabilities sum past 2^15
+// (or to inf / NaN: the first visible tile, where the running max is -inf)
+// needs the running max moved first, so the tile's exponentials are redone
+// after the lazy rescale (below that sum every p <= 2^15 stays inside fp16's
+// range and the P operand keeps the relative precision of any other p); then
+// O^T += V^T P^T.
+template <class T, int D, int BK, bool KV8, bool F8>
+__device__ __forceinline__ void finish_tile(const f32x16 (&s_cur)[BK / 32], u32x4 (&pf)[BK / 16], Acc<D>& st,
+                                            const Offs<D, BK>& o, const char* vcur, float ls, float l0, float lr0,
+                                            float cexp) {
+  if constexpr (!F8) {
+    if (__builtin_amdgcn_ballot_w64(!(ls <= kOptimisticSum))) {
+      st.l = l0;
+      st.lr = lr0;
+      const float m2 = softmax_max<T, D, BK>(s_cur, st, cexp);
+      softmax_exp<T, D, BK>(s_cur, pf, st, m2, cexp);
+    }
+  }
+  __builtin_amdgcn_s_setprio(2);
+  tile_pv<T, D, BK, KV8, F8>(st, pf, vcur, o);
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // One pipelined key step kt. On entry the scores of tile kt (s_cur) are in
@@ -827,24 +851,40 @@ __device__ __forceinline__ void pipe_step(int kt, const char* kcur, const char* 
     } else {
       ls = softmax_exp<T, D, BK, F8>(s_cur, pf, st, msub, cexp);
     }
-    if constexpr (!F8) {
-      // A lane whose 32 probabilities sum past 2^15 (or to inf / NaN: the
-      // first visible tile, where the running max is -inf) needs the running
-      // max moved first: the tile is redone with the lazy rescale. Otherwise
-      // every p <= 2^15 stays inside fp16's range and the P operand's
-      // relative precision is that of any other p.
-      if (__builtin_amdgcn_ballot_w64(!(ls <= kOptimisticSum))) {
-        st.l = l0;
-        st.lr = lr0;
-        const float m2 = softmax_max<T, D, BK>(s_cur, st, cexp);
-        softmax_exp<T, D, BK>(s_cur, pf, st, m2, cexp);
-      }
-    }
-    __builtin_amdgcn_s_setprio(2);
-    tile_pv<T, D, BK, KV8, F8>(st, pf, vcur, o);
-    __builtin_amdgcn_s_setprio(0);
+    finish_tile<T, D, BK, KV8, F8>(s_cur, pf, st, o, vcur, ls, l0, lr0, cexp);
   }
   staged_barrier();
+}
+
+// Debug form of the key loop (built with ATTN_SINGLE_BUFFER): one K and one V
+// buffer, and for each tile the loads, a barrier, the tile's whole arithmetic
+// (the same functions in the same order as the pipelined steps) and a second
+// barrier before the buffers are reused. Nothing overlaps, so a result that
+// differs from the pipelined kernel's, bit for bit, points at a staging race.
+template <class T, int D, int BK, bool CAUSAL, bool KV8, bool F8, class KStg, class VStg>
+__device__ __forceinline__ void single_buffer_loop(char* kbuf, char* vbuf, const KStg& ks, const VStg& vs,
+                                                   Acc<D>& st, const Offs<D, BK>& o, const Geo& g, bool wave_live,
+                                                   int w_last, int w_lo, int qrow, int h, float cexp) {
+  using S = Shape<D, BK>;
+  for (int kt = 0; kt < g.nkt; ++kt) {
+    int e[KStg::EPT];
+    ks.entries(kt, e);
+    ks.load(kt, g.Lk, kbuf, e);
+    vs.load(kt, g.Lk, vbuf, e);
+    staged_barrier();
+    if (wave_live && (!CAUSAL || kt * BK <= w_last)) {
+      f32x16 s[S::KB];
+      u32x4 pf[S::PS];
+      tile_qk_plain<T, D, BK, KV8, F8>(s, kbuf, o, st);
+      softmax_mask<D, BK, CAUSAL>(s, g, kt * BK, qrow, w_lo, h);
+      const float l0 = st.l, lr0 = st.lr;
+      const float msub = F8 ? softmax_max<T, D, BK, true>(s, st, cexp) : st.m;
+      const float ls = softmax_exp<T, D, BK, F8>(s, pf, st, msub, cexp);
+      finish_tile<T, D, BK, KV8, F8>(s, pf, st, o, vbuf, ls, l0, lr0, cexp);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -887,7 +927,11 @@ __global__ __launch_bounds__(BQ * 2, 2) void prefill_kernel(PrefillArgs a) {
     vs.init(static_cast<const char*>(a.v) + head, tid, bstride, tbl);
     const int nb = min((g.Lk + 15) / 16, kMaxPagedPrefillBlocks);
     const int* trow = a.table + (size_t)g.b * a.max_blocks;
-    for (int i = tid; i < nb; i += THREADS) tbl[i] = min(max(trow[i], 0), a.num_blocks - 1);
+    // an id outside [0, num_blocks) is an unmapped block: kept as -1, read as zeros
+    for (int i = tid; i < nb; i += THREADS) {
+      const int id = trow[i];
+      tbl[i] = (unsigned)id < (unsigned)a.num_blocks ? id : -1;
+    }
     __syncthreads();
   } else if constexpr (F8) {
     const size_t head = (size_t)(g.b * a.Hkv + g.kvh) * a.Tk * D;  // bytes: 1 per element
@@ -898,6 +942,13 @@ __global__ __launch_bounds__(BQ * 2, 2) void prefill_kernel(PrefillArgs a) {
     vs.init(reinterpret_cast<const char*>(g.Vg), tid);
   }
 
+  const bool wave_live = w_lo < g.Lq;
+  const int w_last = min(w_lo + 31, g.Lq - 1) + g.off;  // last key any row of this wavefront sees
+#if defined(ATTN_SINGLE_BUFFER)
+  (void)kb1;
+  (void)vb1;
+  single_buffer_loop<T, D, BK, CAUSAL, KV8, F8>(kb0, vb0, ks, vs, st, o, g, wave_live, w_last, w_lo, qrow, h, cexp);
+#else
   int ecar[KStg::EPT] = {};  // physical blocks of the tile after the current one
   if (g.nkt > 0) {
     int e0[KStg::EPT];
@@ -910,10 +961,17 @@ __global__ __launch_bounds__(BQ * 2, 2) void prefill_kernel(PrefillArgs a) {
     }
   }
   staged_barrier();
-  const bool wave_live = w_lo < g.Lq;
-  const int w_last = min(w_lo + 31, g.Lq - 1) + g.off;  // last key any row of this wavefront sees
   f32x16 s0[S::KB], s1[S::KB];
   if (g.nkt > 0 && wave_live && (!CAUSAL || 0 <= w_last)) tile_qk<T, D, BK, KV8, F8>(s0, kb0, o, st);
+  // The first step loads K_2 into kb0, which every wavefront has just read as
+  // K_0 (each wavefront stages only its own rows of a tile but reads all of
+  // them): no wavefront may start those loads before all have finished
+  // reading. Later steps reuse a buffer only after the barrier ending the step
+  // that read it.
+  if (g.nkt > 2) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
   for (int kt = 0; kt < g.nkt; kt += 2) {
     pipe_step<T, D, BK, CAUSAL, KV8, F8>(kt, kb1, vb0, kb0, vb1, s0, s1, ks, vs, ecar, st, o, g, wave_live, w_last,
                                          w_lo, qrow, h, cexp);
@@ -921,6 +979,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void prefill_kernel(PrefillArgs a) {
       pipe_step<T, D, BK, CAUSAL, KV8, F8>(kt + 1, kb0, vb1, kb1, vb0, s1, s0, ks, vs, ecar, st, o, g, wave_live,
                                            w_last, w_lo, qrow, h, cexp);
   }
+#endif
   epilogue<T, D>(st, g, a.Tq, qrow, h, KV8 ? a.v_scale : 1.f, F8 ? kF8PScaleLog2 : 0.f);
 }
 
