@@ -31,7 +31,7 @@ import numpy as np
 from . import oracle as O
 
 __all__ = ["E4M3_MAX", "e4m3_to_float", "float_to_e4m3", "quantize", "dequantize", "cache_append_fp8",
-           "decode_paged_fp8", "prefill_paged_fp8", "prefill_fp8", "prefill_fp8_bound"]
+           "decode_paged_fp8", "prefill_paged_fp8", "prefill_fp8"]
 
 E4M3_MAX = 448.0
 
@@ -115,14 +115,3 @@ def prefill_fp8(q8, k8, v8, q_scale, k_scale, v_scale, scale, causal=False, seq_
     """Prefill attention on E4M3 inputs: the prefill definition on the dequantized q, k, v."""
     return O.prefill(dequantize(q8, q_scale), dequantize(k8, k_scale), dequantize(v8, v_scale), scale, causal,
                      seq_lens)
-
-
-def prefill_fp8_bound(v8, v_scale, Lk):
-    """Bound on |O_fp8 - O| per (b, hq) for a computation that rounds the probabilities to E4M3 after
-    scaling them by 2^7, with a running max that lags the true one by at most 1 (log2 units, so every
-    p <= 2 and the largest >= 1), and divides by the exact sum: each weight p_j is off by at most
-    2^-4 p_j (normal range) or 2^-17 (subnormal range, p_j < 2^-13), and sum p_j >= 1, so
-    |dO| <= (2^-4 + L * 2^-17) * max_j |v_j| with L keys. Returns [B, Hkv] (max over each kv head's V)."""
-    vd = np.abs(dequantize(v8, v_scale))
-    vmax = np.nanmax(vd.reshape(vd.shape[0], vd.shape[1], -1), axis=2)
-    return (2.0 ** -4 + Lk * 2.0 ** -17) * vmax

@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 
 import workloads as W
+from oracle import bounds as BD
 from oracle import oracle as O
 from test_parity_gpu import TOL, LSE_REL, _compare, _dev, _note
 
@@ -66,7 +67,9 @@ def _chunk_check(ta, case, causal=True, starts=None, lens=None, what=None, use_l
     torch.cuda.synchronize()
     o_ref, lse_ref = O.prefill_paged(x["q"], kref, vref, x["block_table"], x["ctx_lens"], q_lens, case.scale,
                                      causal)
-    _compare(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, case.dtype, what=what)
+    bound = BD.prefill_paged(x["q"], kref, vref, x["block_table"], x["ctx_lens"], q_lens, case.scale, causal,
+                             case.dtype)
+    _compare(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, case.dtype, what=what, bound=bound)
     return x, kc, vc, o, lse
 
 

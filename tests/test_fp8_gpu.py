@@ -19,6 +19,7 @@ import numpy as np
 import pytest
 
 import workloads as W
+from oracle import bounds as BD
 from oracle import fp8 as F8
 from test_parity_gpu import _compare, _dev, _note
 
@@ -59,7 +60,9 @@ def _decode_fp8_check(ta, case, ks, vs, ctx_lens=None, what=None):
     o, lse = _run_decode_fp8(ta, x, case, ks, vs)
     o_ref, lse_ref = F8.decode_paged_fp8(x["q"], x["k_cache"], x["v_cache"], ks, vs, x["block_table"],
                                          x["ctx_lens"], case.scale)
-    _compare(o, lse, o_ref, lse_ref, case.dtype, what=f"fp8 decode {what}")
+    bound = BD.decode_paged(x["q"], F8.dequantize(x["k_cache"], ks), F8.dequantize(x["v_cache"], vs),
+                            x["block_table"], x["ctx_lens"], case.scale, case.dtype)
+    _compare(o, lse, o_ref, lse_ref, case.dtype, what=f"fp8 decode {what}", bound=bound)
     return x, o, lse
 
 
@@ -99,7 +102,9 @@ def test_fp8_decode_extreme_codes(ta):
     o, lse = _run_decode_fp8(ta, x, case, ks, vs)
     o_ref, lse_ref = F8.decode_paged_fp8(x["q"], x["k_cache"], x["v_cache"], ks, vs, x["block_table"],
                                          x["ctx_lens"], case.scale)
-    _compare(o, lse, o_ref, lse_ref, "bf16", what="fp8 decode wide codes")
+    bound = BD.decode_paged(x["q"], F8.dequantize(x["k_cache"], ks), F8.dequantize(x["v_cache"], vs),
+                            x["block_table"], x["ctx_lens"], case.scale, "bf16")
+    _compare(o, lse, o_ref, lse_ref, "bf16", what="fp8 decode wide codes", bound=bound)
     del torch
 
 
@@ -271,7 +276,9 @@ def test_fp8_chunked_prefill(ta, D, dtype, causal):
     torch.cuda.synchronize()
     o_ref, lse_ref = F8.prefill_paged_fp8(x["q"], k8, v8, ks, vs, x["block_table"], x["ctx_lens"], x["new_lens"],
                                           case.scale, causal)
-    _compare(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, dtype, what=what)
+    bound = BD.prefill_paged(x["q"], F8.dequantize(k8, ks), F8.dequantize(v8, vs), x["block_table"], x["ctx_lens"],
+                             x["new_lens"], case.scale, causal, dtype)
+    _compare(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, dtype, what=what, bound=bound)
 
 
 def test_fp8_append_then_chunked_prefill_with_rope(ta):
@@ -321,5 +328,6 @@ def test_fp8_chunked_prefill_long_prefix_sampled(ta):
     rows = np.array([0, 1, 63, 64, 127, 128, 255, 256, 300, 511])
     picks = np.array([(0, hq, i) for hq in range(case.Hq) for i in rows])
     o_ref, lse_ref = O.prefill_rows(x["q"], K, V, case.scale, True, None, picks)
+    bound = BD.prefill_rows(x["q"], K, V, case.scale, True, None, picks, "bf16")
     _compare(o[0][picks[:, 1], picks[:, 2]], lse[0][picks[:, 1], picks[:, 2]], o_ref, lse_ref, "bf16",
-             what="fp8 long prefix sampled")
+             what="fp8 long prefix sampled", bound=bound)

@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 
 import workloads as W
+from oracle import bounds as BD
 from oracle import fp8 as F8
 from oracle import gemm as G
 from oracle import oracle as O
@@ -127,13 +128,18 @@ def test_graph_replays_every_entry_point(ta):
     o, lse = got["chunk"]
     o_ref, lse_ref = O.prefill_paged(new["q"], kref, vref, x["block_table"], x["ctx_lens"], x["new_lens"],
                                      1.0 / np.sqrt(D), True)
-    _compare(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, dt, what="graph: chunked prefill")
+    bound = BD.prefill_paged(new["q"], kref, vref, x["block_table"], x["ctx_lens"], x["new_lens"], 1.0 / np.sqrt(D),
+                             True, dt)
+    _compare(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, dt, what="graph: chunked prefill",
+             bound=bound)
     o, lse = got["decode"]
     o_ref, lse_ref = O.decode_paged(new["qd"], kref, vref, x["block_table"], x["ctx_lens"], 1.0 / np.sqrt(D))
-    _compare(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, dt, what="graph: decode")
+    bound = BD.decode_paged(new["qd"], kref, vref, x["block_table"], x["ctx_lens"], 1.0 / np.sqrt(D), dt)
+    _compare(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, dt, what="graph: decode", bound=bound)
     o, lse = got["prefill"]
     o_ref, lse_ref = O.prefill(new["pq"], p["k"], p["v"], 1.0 / np.sqrt(D), True, p["seq_lens"])
-    _compare(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, dt, what="graph: prefill")
+    bound = BD.prefill(new["pq"], p["k"], p["v"], 1.0 / np.sqrt(D), True, p["seq_lens"], dt)
+    _compare(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, dt, what="graph: prefill", bound=bound)
     y = got["gemm"][0].float().cpu().numpy()
     assert (np.abs(y - G.linear(new["gx"], g_in["w"])) <= G.error_bound(new["gx"], g_in["w"], dt)).all()
     # E4M3 caches: the appended codes are the oracle's

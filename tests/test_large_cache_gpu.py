@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 
 import workloads as W
+from oracle import bounds as BD
 from oracle import fp8 as F8
 from oracle import oracle as O
 from test_parity_gpu import _compare, _dev, _note
@@ -77,7 +78,9 @@ def test_decode_over_caches_past_4_gib(ta):
                                   _i32(x["ctx_lens"]), scale=case.scale)
     torch.cuda.synchronize()
     o_ref, lse_ref = O.decode_paged(x["q"], x["k_cache"], x["v_cache"], x["block_table"], x["ctx_lens"], case.scale)
-    _compare(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, "bf16", what="decode past 4 GiB")
+    bound = BD.decode_paged(x["q"], x["k_cache"], x["v_cache"], x["block_table"], x["ctx_lens"], case.scale, "bf16")
+    _compare(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, "bf16", what="decode past 4 GiB",
+             bound=bound)
     del kc, vc
     _free()
 
@@ -97,7 +100,10 @@ def test_fp8_decode_over_caches_past_4_gib(ta):
     torch.cuda.synchronize()
     o_ref, lse_ref = F8.decode_paged_fp8(x["q"], x["k_cache"], x["v_cache"], ks, vs, x["block_table"],
                                          x["ctx_lens"], case.scale)
-    _compare(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, "bf16", what="E4M3 decode past 4 GiB")
+    bound = BD.decode_paged(x["q"], F8.dequantize(x["k_cache"], ks), F8.dequantize(x["v_cache"], vs),
+                            x["block_table"], x["ctx_lens"], case.scale, "bf16")
+    _compare(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, "bf16", what="E4M3 decode past 4 GiB",
+             bound=bound)
     del kc, vc
     _free()
 
@@ -125,7 +131,10 @@ def test_append_and_chunked_prefill_past_4_gib(ta):
         assert np.array_equal(g[~np.isnan(g)], ref[~np.isnan(ref)]), f"{n}: appended values differ"
     o_ref, lse_ref = O.prefill_paged(x["q"], kref, vref, x["block_table"], x["ctx_lens"], x["new_lens"],
                                      case.scale, True)
-    _compare(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, "bf16", what="chunked prefill past 4 GiB")
+    bound = BD.prefill_paged(x["q"], kref, vref, x["block_table"], x["ctx_lens"], x["new_lens"], case.scale, True,
+                             "bf16")
+    _compare(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, "bf16", what="chunked prefill past 4 GiB",
+             bound=bound)
     # the E4M3 form of the append into blocks past byte 2^32 of a 4.5 GB cache
     del kc, vc
     _free()
@@ -149,8 +158,10 @@ def test_append_and_chunked_prefill_past_4_gib(ta):
     assert np.array_equal(vc8.index_select(0, t8).cpu().numpy(), v8_ref)
     o_ref, lse_ref = F8.prefill_paged_fp8(x["q"], k8_ref, v8_ref, 0.05, 0.04, x["block_table"], x["ctx_lens"],
                                           x["new_lens"], case.scale, True)
+    bound = BD.prefill_paged(x["q"], F8.dequantize(k8_ref, 0.05), F8.dequantize(v8_ref, 0.04), x["block_table"],
+                             x["ctx_lens"], x["new_lens"], case.scale, True, "bf16")
     _compare(o8.float().cpu().numpy(), lse8.cpu().numpy(), o_ref, lse_ref, "bf16",
-             what="chunked prefill over E4M3 caches past 4 GiB")
+             what="chunked prefill over E4M3 caches past 4 GiB", bound=bound)
     del kc8, vc8
     _free()
 

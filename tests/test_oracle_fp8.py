@@ -220,13 +220,12 @@ def test_append_fp8_writes_codes_and_nothing_else():
     assert np.array_equal(kc[~touched], k8[~touched]) and np.array_equal(vc[~touched], v8[~touched])
 
 
-def test_prefill_fp8_scale_identity_and_bound_shape():
-    """O(qs, ks, vs, scale) = vs * O(1, 1, 1, scale * qs * ks); lse likewise (scale-only dependence)."""
+def test_prefill_fp8_scale_identity():
+    """O(qs, ks, vs, scale) = vs * O(1, 1, 1, scale * qs * ks); lse likewise (scale-only dependence). The
+    error budget of the FP8 arithmetic is pinned in test_oracle_bounds.py."""
     case = W.PrefillCase("fp8p", B=2, Hq=4, Hkv=2, T=40, D=16, dtype="bf16", causal=True, ragged=True, seed=73)
     x = W.prefill_inputs_fp8(case)
     o1, l1 = F8.prefill_fp8(x["q"], x["k"], x["v"], 0.5, 0.25, 4.0, 0.5, True, x["seq_lens"])
     o2, l2 = F8.prefill_fp8(x["q"], x["k"], x["v"], 1.0, 1.0, 1.0, 0.0625, True, x["seq_lens"])
     np.testing.assert_allclose(o1, 4.0 * o2, rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(l1, l2, rtol=1e-12, atol=1e-12)
-    b = F8.prefill_fp8_bound(x["v"], 4.0, 40)
-    assert b.shape == (2, 2) and (b > 0).all()

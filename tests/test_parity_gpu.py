@@ -1,10 +1,16 @@
 """GPU parity: libattn (HIP, through the C ABI) against the float64 CPU oracle.
 
 Tolerances (the accuracy target of this library): |O_gpu - O_ref| <= 1e-2 for
-bf16 and <= 2e-3 for fp16 over valid rows, widened element by element to one
-unit in the last place of the output format where that format cannot resolve
-the bound (|O| >= 2 in bf16, >= 4 in fp16); |lse_gpu - lse_ref| <= 1e-4 *
+bf16 and <= 2e-3 for fp16 over valid rows; |lse_gpu - lse_ref| <= 1e-4 *
 max(1, |lse_ref|); padded rows exactly O = 0 and lse = -inf.
+  * The five measured workloads are held to those absolute bounds as stated.
+  * Other cases allow, per element, max(bound, budget): the budget derived
+    from the library's stated arithmetic (oracle/bounds.py: P rounded to the
+    16-bit type, fp32 sums, the output rounding; pinned by CPU simulations).
+    Where no budget is computed, the allowance is max(bound, half a unit in
+    the last place of the output type at |O_ref| + bound): the output format
+    itself cannot resolve the bound from |O| >= 4 (bf16) or >= 8 (fp16).
+Every element above the stated bound is counted in the printed line.
 Inputs come from workloads.py (seeded); padding and unused cache slots hold
 NaN so that any read of them into a result shows up.
 """
@@ -15,6 +21,7 @@ import numpy as np
 import pytest
 
 import workloads as W
+from oracle import bounds as BD
 from oracle import oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -48,16 +55,16 @@ def _note(msg):
 
 def _ulp(x, dtype):
     """Spacing of the output format at |x| (bf16: 8 significant bits, fp16: 11)."""
-    mant = 8 if dtype == "bf16" else 11
-    ax = np.maximum(np.abs(x), 2.0 ** -14)
-    return 2.0 ** (np.floor(np.log2(ax)) - (mant - 1))
+    from oracle.gemm import ulp16
+    return ulp16(x, dtype)
 
 
-def _compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype, valid=None, what=""):
-    """Element-wise bound: max(tol, one unit in the last place of the output dtype at O_ref).
+def _compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype, valid=None, what="", bound=None, strict=False):
+    """Element-wise check of O and lse (see the module notes).
 
-    The unit-in-the-last-place term only exceeds tol where the output format
-    itself cannot resolve tol (|O| >= 2 for bf16, >= 4 for fp16).
+    strict: |dO| <= the stated bound everywhere. bound: per-element budget (oracle/bounds.py, same shape
+    as o_ref), allowance max(tol, budget). Neither: max(tol, half an ulp of the output type at |O_ref| +
+    tol), the limit of the format itself.
     """
     o_gpu = np.asarray(o_gpu, dtype=np.float64)
     lse_gpu = np.asarray(lse_gpu, dtype=np.float64)
@@ -66,16 +73,25 @@ def _compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype, valid=None, what=""):
     ov = valid[..., None] if o_ref.ndim == valid.ndim + 1 else valid
     ov = np.broadcast_to(ov, o_ref.shape)
     err = np.abs(o_gpu - o_ref)[ov]
-    allow = np.maximum(TOL[dtype], _ulp(o_ref[ov], dtype))
-    nrel = int((err > TOL[dtype]).sum())
+    tol = TOL[dtype]
+    if strict:
+        allow = np.full(err.shape, tol)
+        rule = "stated bound"
+    elif bound is not None:
+        allow = np.maximum(tol, np.asarray(bound, dtype=np.float64)[ov])
+        rule = "max(bound, derived budget)"
+    else:
+        allow = np.maximum(tol, 0.5 * _ulp(np.abs(o_ref[ov]) + tol, dtype))
+        rule = "max(bound, half ulp)"
+    nabove = int((err > tol).sum())
     emax = float(err.max()) if err.size else 0.0
     ratio = float((err / allow).max()) if err.size else 0.0
     lerr = float((np.abs(lse_gpu[valid] - lse_ref[valid]) / np.maximum(1.0, np.abs(lse_ref[valid]))).max()) \
         if valid.any() else 0.0
-    _note(f"[parity] {what}: max|dO|={emax:.3e} (tol {TOL[dtype]}; {nrel} elements above tol within 1 ulp) "
+    _note(f"[parity] {what}: max|dO|={emax:.3e} (bound {tol}; {nabove} elements above it) rule: {rule} "
           f"max err/allowed={ratio:.3f} max rel dlse={lerr:.3e}")
     assert np.isfinite(o_gpu[ov]).all(), f"{what}: non-finite output"
-    assert ratio <= 1.0, f"{what}: max |dO| = {emax} exceeds max(tol, 1 ulp)"
+    assert ratio <= 1.0, f"{what}: max |dO| = {emax} exceeds the allowance ({rule})"
     assert lerr <= LSE_REL, f"{what}: lse rel err = {lerr}"
     inv = ~valid
     if inv.any():
@@ -95,28 +111,29 @@ def _run_prefill(ta, x, case, causal=None, scale=None):
     return o.float().cpu().numpy(), lse.cpu().numpy()
 
 
-def _full_check(ta, case, nan_padding=True, causal=None, scale=None, Tq=None, Tk=None, what=None):
+def _full_check(ta, case, nan_padding=True, causal=None, scale=None, Tq=None, Tk=None, what=None, strict=False):
     x = W.prefill_inputs(case, nan_padding=nan_padding, Tq=Tq, Tk=Tk)
     causal = case.causal if causal is None else causal
     scale = case.scale if scale is None else scale
     _note(f"[case] {what or case.name} causal={causal} scale={scale} Tq={x['q'].shape[2]} Tk={x['k'].shape[2]}")
     o, lse = _run_prefill(ta, x, case, causal, scale)
     o_ref, lse_ref = O.prefill(x["q"], x["k"], x["v"], scale, causal, x["seq_lens"])
-    _compare(o, lse, o_ref, lse_ref, case.dtype, what=what or case.name)
+    bound = None if strict else BD.prefill(x["q"], x["k"], x["v"], scale, causal, x["seq_lens"], case.dtype)
+    _compare(o, lse, o_ref, lse_ref, case.dtype, what=what or case.name, bound=bound, strict=strict)
     return o, lse
 
 
 # ---------------------------------------------------------------- the five workloads
 def test_tiny_fp16(ta):
-    _full_check(ta, W.TINY)
+    _full_check(ta, W.TINY, strict=True)
 
 
 def test_bert_ragged_fp16_nan_padding(ta):
-    _full_check(ta, W.BERT)
+    _full_check(ta, W.BERT, strict=True)
 
 
 def test_llama_causal_gqa_bf16(ta):
-    _full_check(ta, W.LLAMA)
+    _full_check(ta, W.LLAMA, strict=True)
 
 
 def test_long_causal_bf16_sampled(ta):
@@ -133,7 +150,7 @@ def test_long_causal_bf16_sampled(ta):
     picks = np.array([(0, h, i) for h in range(case.Hq) for i in rows])
     o_ref, lse_ref = O.prefill_rows(x["q"], x["k"], x["v"], case.scale, True, None, picks)
     _compare(o[0][picks[:, 1], picks[:, 2]], lse[0][picks[:, 1], picks[:, 2]], o_ref, lse_ref, "bf16",
-             what="long sampled")
+             what="long sampled", strict=True)
     del torch
 
 
@@ -150,18 +167,20 @@ def _run_decode(ta, x, case, scale=None):
     return o.float().cpu().numpy(), lse.cpu().numpy()
 
 
-def _decode_check(ta, case, ctx_lens=None, scale=None, what=None):
+def _decode_check(ta, case, ctx_lens=None, scale=None, what=None, strict=False):
     x = W.decode_inputs(case, nan_fill=True, ctx_lens=ctx_lens)
     scale = case.scale if scale is None else scale
     _note(f"[case] {what or case.name} ctx[min,max]=({x['ctx_lens'].min()},{x['ctx_lens'].max()}) scale={scale}")
     o, lse = _run_decode(ta, x, case, scale)
     o_ref, lse_ref = O.decode_paged(x["q"], x["k_cache"], x["v_cache"], x["block_table"], x["ctx_lens"], scale)
-    _compare(o, lse, o_ref, lse_ref, case.dtype, what=what or case.name)
+    bound = None if strict else BD.decode_paged(x["q"], x["k_cache"], x["v_cache"], x["block_table"],
+                                                x["ctx_lens"], scale, case.dtype)
+    _compare(o, lse, o_ref, lse_ref, case.dtype, what=what or case.name, bound=bound, strict=strict)
     return x, o, lse
 
 
 def test_qwen_paged_decode_bf16(ta):
-    _decode_check(ta, W.QWEN)
+    _decode_check(ta, W.QWEN, strict=True)
 
 
 # ---------------------------------------------------------------- prefill edge cases
@@ -199,7 +218,8 @@ def test_prefill_peaked_scores(ta):
     _note("[case] peaked scores")
     o, lse = _run_prefill(ta, x, case)
     o_ref, lse_ref = O.prefill(x["q"], x["k"], x["v"], case.scale, True, None)
-    _compare(o, lse, o_ref, lse_ref, "bf16", what="peaked")
+    bound = BD.prefill(x["q"], x["k"], x["v"], case.scale, True, None, "bf16")
+    _compare(o, lse, o_ref, lse_ref, "bf16", what="peaked", bound=bound)
     del torch
 
 
@@ -303,7 +323,8 @@ def test_decode_explicit_workspace_reused_across_shapes(ta):
         o, lse = ta.attn_decode_paged(q, kc, vc, bt, cl, scale=c.scale, workspace=ws)
         torch.cuda.synchronize()
         o_ref, lse_ref = O.decode_paged(x["q"], x["k_cache"], x["v_cache"], x["block_table"], x["ctx_lens"], c.scale)
-        _compare(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, c.dtype, what=c.name)
+        bound = BD.decode_paged(x["q"], x["k_cache"], x["v_cache"], x["block_table"], x["ctx_lens"], c.scale, c.dtype)
+        _compare(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, c.dtype, what=c.name, bound=bound)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])

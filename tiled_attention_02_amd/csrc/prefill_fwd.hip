@@ -57,8 +57,9 @@
 // A operand V^T is 4 ds_read_b64_tr_b8 in the same key order). The running
 // max moves once it grows by more than 1 (log2), so p <= 2 and the scaled p
 // stay <= 2^8; O is divided by the fp32 sum of the unrounded scaled p. Error
-// of the rounding of P: at most (2^-4 + L * 2^-17) * max |v| per output
-// element for L keys.
+// of the rounding of P per output element (row i, column d): at most
+// 2^-4 sum_j P_ij |v_jd| + 2^-17 max_j P_ij sum_j |v_jd| over the row's keys
+// (2^-4 relative in E4M3's normal range, 2^-17 absolute below it).
 //
 // E4M3 form (chunked prefill over an FP8 cache, paged only): K/V tiles hold
 // one byte per element; operand fragments are converted to the 16-bit type
