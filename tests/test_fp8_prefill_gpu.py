@@ -9,9 +9,10 @@ Two references, both on the dequantized inputs:
   * the same FP8 arithmetic carried out in float64 (oracle/bounds.prefill_fp8_model_rows: 64-key tiles,
     the running max moved when a tile exceeds it by more than 1, p 2^7 rounded to E4M3), within the much
     tighter budget of what fp32 evaluation can change (keys at a rounding boundary, fp32 sums, the
-    output rounding). That check exposes a dropped or doubled key tile on every row length, the last row
-    of the 16384-token configuration included; rows whose tile schedule itself is ambiguous under fp32
-    fall back to the first check only (none so far).
+    output rounding, and the fp8 instruction's dot-product accuracy, 2^-13 of the sum of magnitudes,
+    re-measured by the last test here). Through O it exposes a dropped or doubled key tile on rows of up
+    to a few thousand keys; lse exposes it at every length. Rows whose tile schedule itself is ambiguous
+    under that accuracy fall back to the first check only.
 lse (from the unrounded probabilities and the fp32 scores) within 1e-4 * max(1, |lse|); padded rows
 exactly 0 / -inf.
 """
@@ -150,3 +151,32 @@ def test_fp8_prefill_long_causal_sampled(ta):
     model = BD.prefill_fp8_model_rows(qd, kd, vd, case.scale, True, None, picks, "bf16")
     _check(o[0][picks[:, 1], picks[:, 2]], lse[0][picks[:, 1], picks[:, 2]], o_ref, lse_ref, bound,
            "fp8 long sampled", model=model)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_matrix_instruction_dot_accuracy(ta, D):
+    """The accuracy the budgets assume for the scores' dot products, measured through the library: with one
+    key, lse = m ln 2 and m = (q . k) c, so lse gives the kernel's dot product. The fp8 instruction must stay
+    within F8_DOT (2^-13) of sum |q_e k_e| (oracle/bounds.py), the bf16 one within fp32's gamma_D."""
+    import torch
+    rng = np.random.default_rng(5 + D)
+    Tq = 4096
+    scale = 1.0 / np.sqrt(D)
+    c = float(np.float32(np.float32(scale) * np.float32(np.log2(np.e))))
+    q8 = W.e4m3_codes(rng, (1, 1, Tq, D))
+    k8 = W.e4m3_codes(rng, (1, 1, 1, D))
+    v8 = W.e4m3_codes(rng, (1, 1, 1, D))
+    _, lse = ta.attn_fwd_fp8(_u8(q8), _u8(k8), _u8(v8), 1.0, 1.0, 1.0, scale=scale, causal=False)
+    q16 = W.round_to(rng.standard_normal((1, 1, Tq, D), dtype=np.float32) * 2, "bf16")
+    k16 = W.round_to(rng.standard_normal((1, 1, 1, D), dtype=np.float32) * 2, "bf16")
+    dv = lambda a: torch.from_numpy(a).to(torch.bfloat16).cuda()  # noqa: E731
+    _, lse16 = ta.attn_fwd(dv(q16), dv(k16), dv(k16), scale=scale, causal=False)
+    torch.cuda.synchronize()
+    for name, lg, qv, kv, allow in (
+            ("fp8", lse, F8.e4m3_to_float(q8)[0, 0], F8.e4m3_to_float(k8)[0, 0, 0], BD.F8_DOT),
+            ("bf16", lse16, q16[0, 0].astype(np.float64), k16[0, 0, 0].astype(np.float64), D * 2.0 ** -24)):
+        s_gpu = lg.cpu().numpy()[0, 0].astype(np.float64) / (np.log(2.0) * c)
+        rel = np.abs(s_gpu - qv @ kv) / (np.abs(qv) @ np.abs(kv))
+        _note(f"[accuracy] {name} D={D}: max |dot error| / sum |products| = {rel.max():.3e} "
+              f"(2^{np.log2(rel.max()):.1f}; allowed {allow:.2e} plus the fp32 roundings of the scale and lse)")
+        assert rel.max() <= allow + 8 * 2.0 ** -24
