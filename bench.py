@@ -15,15 +15,18 @@ One step = one pass of the whole hot path on seeded synthetic inputs:
     caches (quantizing append), and
   * the long causal prefill's shape on E4M3 q, k, v (attn_fwd_fp8), and
   * the four Llama3-8B linear layers at 2 activation rows (attn_gemm_splitk).
+After the timed steps, two launch-sized prefill workloads get legs of their own
+("bert_prefill": the BERT-base-shaped ragged fp16 batch, B=8, H=12, D=64,
+lengths ~ U[64, 512]; "llama_prefill": the Llama3-8B-shaped causal bf16
+prefill, B=2, Hq=32, Hkv=8, T=512, D=128), each timed per call after the
+eviction pass and back to back over rotating copies of its inputs.
 Each call is timed with HIP events on the stream it runs on (mean, median and
 minimum over the timed steps). Before each call (outside its events) a read
 pass over a 1 GiB buffer evicts the inputs from the 256 MB Infinity Cache and
 the L2s, so the timed call reads its inputs from HBM; a read pass leaves clean
 lines behind, whereas a write pass would leave a gigabyte of dirty lines whose
 write-back would land inside the timed region. "context" holds figures
-reported beside the headline ones: the Llama3-8B-shaped 512-token prefill
-(launch-dominated, per call and back to back), the rate of a plain streaming
-read, the MFMA peak derived from the device's CU count and clock, the decode
+reported beside the headline ones: the rate of a plain streaming read, the MFMA peak derived from the device's CU count and clock, the decode
 timed over 4 rotating cache copies instead of the eviction pass, and the host
 processor. After timing, the outputs of the timed calls are compared with the
 float64 oracle ("parity_on_timed_buffers").
@@ -415,45 +418,92 @@ def decode_rotation_crosscheck(ta, torch, np, dq, kc, vc, bt, cl, scale, ws, cop
     return float(np.median(ts)) * 1e3, float(np.min(ts)) * 1e3, float(np.median(bursts)) * 1e3
 
 
-def context_measurements(ta, W, torch, np, dev, flush_rows, flush_dst, evict):
-    """Figures reported beside the headline numbers (not part of `value`).
+def small_prefill_leg(ta, torch, np, W, dev, case, evict, steps, copies):
+    """A launch-sized prefill workload (the BERT-shaped ragged batch, the Llama3-8B-shaped 512-token causal
+    prefill): timed per call after the eviction pass (events around each call), and back to back over
+    `copies` independent copies of the inputs (more bytes in total than the 256 MB Infinity Cache holds, so
+    each call reads its inputs from HBM, as a model's layers would), events around each pass of `copies`
+    calls. Returns (result dict, inputs, the first copy's o and lse)."""
+    x = W.prefill_inputs(case, nan_padding=case.ragged)
+    tdt = torch.float16 if case.dtype == "fp16" else torch.bfloat16
+    base = [torch.from_numpy(x[n]).to(tdt).to(dev) for n in ("q", "k", "v")]
+    sets = []
+    for c in range(copies):
+        q, k, v = base if c == 0 else [t.clone() for t in base]
+        sets.append((q, k, v, torch.empty_like(q), torch.empty(q.shape[:3], dtype=torch.float32, device=dev)))
+    sl = None if x["seq_lens"] is None else torch.from_numpy(x["seq_lens"]).to(dev)
 
-    * Llama3-8B-shaped prefill (B=2, Hq=32, Hkv=8, T=512, D=128, causal bf16):
-      4.3 GFLOP, about 2 us of the whole GPU, so its time is set by launch and
-      tail effects; timed per call (after the cache eviction) and as the mean
-      of 50 back-to-back calls.
-    * a plain streaming read: the 1 GiB eviction pass itself (torch.sum over
-      rows of 4096 float32), i.e. the HBM read rate a simple kernel attains here.
-    """
-    lc = W.LLAMA
-    xl = W.prefill_inputs(lc)
-    bf = torch.bfloat16
-    q = torch.from_numpy(xl["q"]).to(bf).to(dev)
-    k = torch.from_numpy(xl["k"]).to(bf).to(dev)
-    v = torch.from_numpy(xl["v"]).to(bf).to(dev)
-    o = torch.empty_like(q)
-    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
-    flops = W.prefill_flops(lc.B, lc.Hq, lc.T, lc.T, lc.D, True)
-    call = lambda: ta.attn_fwd(q, k, v, scale=lc.scale, causal=True, out=o, lse=lse)  # noqa: E731
-    for _ in range(3):
-        call()
+    def call(i):
+        q, k, v, o, lse = sets[i]
+        ta.attn_fwd(q, k, v, scale=case.scale, causal=case.causal, seq_lens=sl, out=o, lse=lse)
+
+    for i in range(copies):
+        call(i)
+    torch.cuda.synchronize()
     per = []
-    for _ in range(20):
+    for _ in range(steps):
         evict()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        call()
+        call(0)
         e1.record()
         torch.cuda.synchronize()
         per.append(e0.elapsed_time(e1))
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(50):
-        call()
-    e1.record()
-    torch.cuda.synchronize()
-    b2b = e0.elapsed_time(e1) / 50
-    med = float(np.median(per))
+    b2b = []
+    for _ in range(max(5, steps // 2)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(copies):
+            call(i)
+        e1.record()
+        torch.cuda.synchronize()
+        b2b.append(e0.elapsed_time(e1) / copies)
+    flops = W.prefill_flops(case.B, case.Hq, case.T, case.T, case.D, case.causal, x["seq_lens"])
+    nbytes = W.prefill_bytes(case.B, case.Hq, case.Hkv, case.T, case.T, case.D, x["seq_lens"])
+    t_b2b, t_per = float(np.mean(b2b)) * 1e-3, float(np.mean(per)) * 1e-3
+    tfs = flops / t_b2b / 1e12
+    res = {
+        "workload": case.name + (f", lengths {[int(v) for v in x['seq_lens']]}" if x["seq_lens"] is not None else ""),
+        "value": round(tfs, 2), "unit": "TFLOP/s",
+        "timing": f"back to back over {copies} input copies (events around each pass, per-call mean); "
+                  "us_per_call: one call after the eviction pass, events around it",
+        "us_per_call_back_to_back": round(t_b2b * 1e6, 2),
+        "us_per_call_back_to_back_min": round(float(np.min(b2b)) * 1e3, 2),
+        "us_per_call": round(t_per * 1e6, 2), "us_per_call_median": round(float(np.median(per)) * 1e3, 2),
+        "tflops_per_call": round(flops / t_per / 1e12, 2),
+        "gflop_per_call": round(flops / 1e9, 4), "mb_per_call": round(nbytes / 1e6, 3),
+        "roofline": {"bound": "mfma", "achieved": round(tfs, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tfs / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "prefill_kernel", "algorithmic_flops_per_launch": flops,
+                     "hbm_frac": round(nbytes / t_b2b / 1e9 / PEAK_HBM_GBS, 4),
+                     "note": "arithmetic intensity below the ridge (about 312 flop/byte): the launch is short enough "
+                             "that its fixed costs set the time; hbm_frac is the algorithmic bytes' rate against "
+                             "8 TB/s"}}
+    return res, x, sets[0][3], sets[0][4]
+
+
+def cpu_baseline_small_prefill(x, case, min_seconds=5.0):
+    """The float64 oracle on the whole workload, repeated for a stable figure."""
+    import workloads as W
+    from oracle import oracle as O
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        O.prefill(x["q"], x["k"], x["v"], case.scale, case.causal, x["seq_lens"])
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    flops = W.prefill_flops(case.B, case.Hq, case.T, case.T, case.D, case.causal, x["seq_lens"]) * reps
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _oracle_threads(), "kind": "oracle",
+            "sample": f"float64 oracle on the whole workload (every head and row), repeated {reps} times; "
+                      f"{dt:.1f} s wall"}
+
+
+def context_measurements(ta, W, torch, np, dev, flush_rows, flush_dst, evict):
+    """Figures reported beside the headline numbers (not part of `value`): the rate of a plain streaming
+    read, i.e. the 1 GiB eviction pass itself (torch.sum over rows of 4096 float32), the HBM read rate a
+    simple kernel attains here."""
     rd = []
     for _ in range(5):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -464,12 +514,6 @@ def context_measurements(ta, W, torch, np, dev, flush_rows, flush_dst, evict):
         rd.append(e0.elapsed_time(e1))
     nbytes = flush_rows.numel() * 4
     return {
-        "llama3_8b_shaped_prefill": {
-            "workload": "causal bf16 B=2 Hq=32 Hkv=8 T=512 D=128", "gflop_per_call": round(flops / 1e9, 3),
-            "us_per_call_median": round(med * 1e3, 2),
-            "tflops_per_call": round(flops / (med * 1e-3) / 1e12, 1),
-            "us_per_call_back_to_back": round(b2b * 1e3, 2),
-            "tflops_back_to_back": round(flops / (b2b * 1e-3) / 1e12, 1)},
         "streaming_read_gbs": {"value": round(nbytes / (float(np.median(rd)) * 1e-3) / 1e9, 1),
                                "what": "torch.sum over a 1 GiB float32 buffer in rows of 4096 (the eviction pass), median of 5"},
     }
@@ -706,7 +750,9 @@ def main():
                                "chunked bf16 prefill "
                                "B=4 Hq=32 Hkv=8 D=128 prefix~U[2048,8192] chunk=1024 through the block table "
                                "(chunked; again with RoPE fused: chunked_rope; again over E4M3 caches: "
-                               "chunked_fp8) + split-K GEMM of the four Llama3-8B linear layers at M=2 (gemm)",
+                               "chunked_fp8) + split-K GEMM of the four Llama3-8B linear layers at M=2 (gemm) + "
+                               "ragged fp16 encoder prefill B=8 H=12 D=64 lengths~U[64,512] (bert_prefill) + causal "
+                               "bf16 prefill B=2 Hq=32 Hkv=8 T=512 D=128 (llama_prefill)",
                    "prefill_gflop_per_call": round(pflops / 1e9, 3),
                    "decode_mb_per_call": round(dbytes / 1e6, 3),
                    "cache_eviction_before_each_call": "none" if args.no_flush else "1 GiB read pass",
@@ -793,6 +839,11 @@ def main():
                      "frac": round(gu_gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic("gemm"),
                      "kernel": "gemm_splitk_kernel (gate/up projection, the largest launch)",
                      "algorithmic_bytes_per_launch": gbytes["gate_up_proj"]}}
+    small = {}
+    for key, case, copies in (("bert_prefill", W.BERT, 24), ("llama_prefill", W.LLAMA, 16)):
+        log(f"[bench] {case.name}: per call and back to back over {copies} input copies")
+        small[key] = small_prefill_leg(ta, torch, np, W, dev, case, evict, max(args.steps, 20), copies)
+        out[key] = small[key][0]
     out["context"] = context_measurements(ta, W, torch, np, dev, flush_rows, flush_dst, evict)
     out["context"]["clock_derived_peak"] = clock_derived_peak(torch)
     out["context"]["host_cpu"] = host_cpu()
@@ -823,6 +874,9 @@ def main():
         out["chunked_rope"]["cpu_baseline"] = cpu_baseline_chunked(xc, cc, rope=W.rope_table(16384, cc.D))
         log("[bench] cpu baseline: float64 oracle on the linear layers")
         out["gemm"]["cpu_baseline"] = cpu_baseline_gemm(gx)
+        for key, case in (("bert_prefill", W.BERT), ("llama_prefill", W.LLAMA)):
+            log(f"[bench] cpu baseline: float64 oracle on the whole {key} workload")
+            out[key]["cpu_baseline"] = cpu_baseline_small_prefill(small[key][1], case)
         log("[bench] parity of the timed calls' outputs against the oracle (sampled)")
         pcalls = {name: call for name, call, _ in parts}
         chunk_calls = [("chunked", pcalls["chunked_prefill"]), ("chunked_rope", pcalls["chunked_prefill_rope"]),
@@ -830,6 +884,19 @@ def main():
         out["parity_on_timed_buffers"] = parity_on_timed_buffers(
             ta, torch, np, W, pc, xp, o, lse, xp8, (QS8, KSP8, VSP8), o8, lse8, dc, xd, do, dlse, xd8, KS8, VS8,
             do8, dlse8, cc, xc, rope_tab, chunk_calls, co, clse, ck8.cpu().numpy(), cv8.cpu().numpy(), gx, gdev)
+        from oracle import oracle as O
+        pr = out["parity_on_timed_buffers"]
+        for key, case in (("bert_prefill", W.BERT), ("llama_prefill", W.LLAMA)):
+            _, xs, os_, ls_ = small[key]
+            orf, lrf = O.prefill(xs["q"], xs["k"], xs["v"], case.scale, case.causal, xs["seq_lens"])
+            valid = np.isfinite(lrf)
+            tol = 2e-3 if case.dtype == "fp16" else 1e-2
+            og, lg = os_.float().cpu().numpy(), ls_.cpu().numpy()
+            pr[key] = _parity(og[valid], orf[valid], lg[valid], lrf[valid], tol=tol, strict=True,
+                              what="every valid row of the timed call's output")
+            pr[key]["padding_rows_exact"] = bool((og[~valid] == 0).all() and np.isneginf(lg[~valid]).all())
+            pr[key]["ok"] = pr[key]["ok"] and pr[key]["padding_rows_exact"]
+        pr["all_ok"] = all(v.get("ok", False) for v in pr.values() if isinstance(v, dict))
         log(f"[bench] parity on timed buffers: all ok = {out['parity_on_timed_buffers']['all_ok']}")
     print(json.dumps(out), flush=True)
 

@@ -338,6 +338,17 @@ def prefill_flops(B, Hq, Tq, Tk, D, causal, seq_lens=None):
     return 4.0 * D * Hq * pairs
 
 
+def prefill_bytes(B, Hq, Hkv, Tq, Tk, D, seq_lens=None, elem=2):
+    """Algorithmic HBM bytes of one prefill call: q and o of the valid rows, k and v of the valid keys (once per
+    kv head), and the lse of the valid rows (fp32)."""
+    total = 0
+    for b in range(B):
+        Lq = Tq if seq_lens is None else int(seq_lens[b])
+        Lk = Tk if seq_lens is None else int(seq_lens[b])
+        total += 2 * Hq * Lq * D * elem + 2 * Hkv * Lk * D * elem + Hq * Lq * 4
+    return total
+
+
 def decode_bytes(ctx_lens, Hq, Hkv, D, elem=2, max_blocks=None, kv_elem=None):
     """Algorithmic HBM bytes of one paged decode call.
 
