@@ -336,6 +336,27 @@ attn_status attn_gemm_splitk_cfg(const void* x, const void* w, void* y, int M, i
                                  attn_dtype dtype, int rows, int waves, int unroll,
                                  hipStream_t stream);
 
+/*
+ * attn_decode_paged without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Same arguments and results as
+ * attn_decode_paged; the split partials live in a static device array of 32
+ * MiB that the library holds on each GPU it runs on until the process ends
+ * (its address is looked up on a device's first call, with that device
+ * current). Nothing is allocated or freed by the call.
+ * Limit: attn_decode_workspace_bytes(B, Hq, Hkv, D, max_blocks_per_seq, 16)
+ * <= 32 MiB, else ATTN_ERR_UNSUPPORTED before anything is launched.
+ * Every call on one GPU shares that array: calls that overlap in time on one
+ * GPU (different streams, or different threads without ordering) race and
+ * give undefined results; calls ordered on one stream are safe. The array
+ * keeps the last call's contents; nothing needs to start at zero.
+ */
+attn_status attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                      const int* block_table, const int* ctx_lens, void* o, float* lse,
+                                      int B, int Hq, int Hkv, int D, int block_size,
+                                      int max_blocks_per_seq, int num_blocks, float scale,
+                                      attn_dtype dtype, hipStream_t stream);
+
 /* Workspace bytes attn_decode_paged needs for these sizes (0 if they are invalid). */
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_blocks_per_seq, int block_size);
 

@@ -84,6 +84,31 @@ def test_decode_rejects_before_launch(L, kw, code):
     assert ta.attn_last_error().startswith("attn_decode_paged:")
 
 
+def _dec_na(L, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, cl=FAKE, o=FAKE, lse=None, B=2, Hq=12, Hkv=2, D=128, bs=16,
+            maxb=64, nb=100, scale=0.1, dtype=1):
+    return L.attn_decode_paged_noalloc(q, kc, vc, bt, cl, o, lse, B, Hq, Hkv, D, bs, maxb, nb, ctypes.c_float(scale),
+                                       dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bt=None), 1), (dict(o=None), 1), (dict(B=0), 1), (dict(Hkv=5), 1), (dict(bs=32), 2), (dict(D=80), 2),
+    (dict(Hq=34, Hkv=2), 2), (dict(dtype=9), 2), (dict(kc=FAKE_MIS), 1), (dict(cl=ctypes.c_void_p(0x10002)), 1),
+    # partials beyond the 32 MiB scratch: 4096 x 64 heads x 16 splits x 528 bytes
+    (dict(B=4096, Hq=64, Hkv=8, maxb=256), 2),
+])
+def test_decode_noalloc_rejects_before_launch(L, kw, code):
+    import tiled_attention_02_amd as ta
+    assert _dec_na(L, **kw) == code
+    assert ta.attn_last_error().startswith("attn_decode_paged_noalloc:")
+
+
+def test_decode_noalloc_names_the_scratch_limit(L):
+    import tiled_attention_02_amd as ta
+    assert _dec_na(L, B=4096, Hq=64, Hkv=8, maxb=256) == 2
+    msg = ta.attn_last_error()
+    assert "33554432-byte scratch" in msg and "attn_decode_paged with a workspace" in msg
+
+
 def _pfw(L, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, cl=FAKE, ql=None, o=FAKE, lse=None, B=2, Hq=8, Hkv=2, Tq=64,
          D=128, bs=16, maxb=64, nb=100, scale=0.1, causal=1, dtype=1):
     return L.attn_fwd_paged(q, kc, vc, bt, cl, ql, o, lse, B, Hq, Hkv, Tq, D, bs, maxb, nb, ctypes.c_float(scale),
@@ -218,12 +243,15 @@ calls = {
                                                f(0.1), 1, 1, None),
     "attn_cache_append": lambda: L.attn_cache_append(F, F, F, F, F, F, None, 2, 2, 64, 128, 16, 64, 100, 1, None),
     "attn_gemm_splitk": lambda: L.attn_gemm_splitk(F, F, F, 2, 4096, 4096, 1, None),
+    "attn_decode_paged_noalloc": lambda: L.attn_decode_paged_noalloc(F, F, F, F, F, F, None, 2, 12, 2, 128, 16, 64,
+                                                                     100, f(0.1), 1, None),
 }
 for name, call in calls.items():
     st = call()
     print(name, st, ta.attn_last_error())
     assert st == 3, (name, st)
-    assert ta.attn_last_error().startswith(name + ": launch failed"), ta.attn_last_error()
+    assert (ta.attn_last_error().startswith(name + ": launch failed") or
+            ta.attn_last_error().startswith(name + ": device address of the scratch array")), ta.attn_last_error()
 print("ALL_HIP_ERRORS")
 """
 

@@ -16,7 +16,8 @@ import os
 __all__ = ["attn_fwd", "attn_decode_paged", "attn_fwd_paged", "attn_cache_append", "attn_cache_append_fp8",
            "attn_decode_paged_fp8", "attn_fwd_paged_fp8", "attn_fwd_fp8", "attn_cache_append_rope",
            "attn_fwd_paged_rope", "attn_decode_paged_rope", "attn_decode_workspace_bytes",
-           "attn_gemm_splitk", "attn_status_str", "attn_last_error", "AttnError", "lib", "LIB_PATH", "EXPORTS",
+           "attn_gemm_splitk", "attn_decode_paged_noalloc", "attn_status_str", "attn_last_error", "AttnError", "lib",
+           "LIB_PATH", "EXPORTS",
            "BLOCK_SIZE", "decode_workspace"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
@@ -24,7 +25,7 @@ LIB_SINGLE_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liba
 EXPORTS = ("attn_fwd", "attn_decode_paged", "attn_fwd_paged", "attn_cache_append", "attn_cache_append_fp8",
            "attn_decode_paged_fp8", "attn_fwd_paged_fp8", "attn_fwd_fp8", "attn_cache_append_rope",
            "attn_fwd_paged_rope", "attn_decode_paged_rope", "attn_decode_workspace_bytes", "attn_gemm_splitk",
-           "attn_gemm_splitk_cfg", "attn_status_str", "attn_last_error")
+           "attn_gemm_splitk_cfg", "attn_decode_paged_noalloc", "attn_status_str", "attn_last_error")
 BLOCK_SIZE = 16
 
 ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
@@ -95,6 +96,8 @@ def _load(path) -> ctypes.CDLL:
     L.attn_fwd_paged_rope.restype = i
     L.attn_decode_paged_rope.argtypes = [vp, vp, vp, vp, i, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, sz, vp]
     L.attn_decode_paged_rope.restype = i
+    L.attn_decode_paged_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
+    L.attn_decode_paged_noalloc.restype = i
     L.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
     L.attn_decode_workspace_bytes.restype = sz
     L.attn_gemm_splitk.argtypes = [vp, vp, vp, i, i, i, i, vp]
@@ -250,6 +253,38 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, ctx_lens, scale: float |
     [B,max_blocks]; ctx_lens int32 [B]. rope: optional float32 table [max_pos, D] (cos | sin halves):
     the query is rotated at position ctx - 1. Returns (o [B,Hq,D], lse [B,Hq] float32 or None)."""
     return _decode(q, k_cache, v_cache, None, block_table, ctx_lens, scale, out, lse, workspace, need_lse, rope)
+
+
+def attn_decode_paged_noalloc(q, k_cache, v_cache, block_table, ctx_lens, scale: float | None = None, out=None,
+                              lse=None):
+    """attn_decode_paged with the library's static per-GPU scratch instead of a workspace (no allocation in
+    the library; out / lse may be passed in so that the call allocates nothing at all). Calls that overlap on
+    one GPU race; the split partials of one call must fit in 32 MiB."""
+    import torch
+    dt = _dtype_code(q)
+    _check(q.dim() == 3 and k_cache.dim() == 4 and v_cache.shape == k_cache.shape, "bad q / cache rank or shape")
+    _check(k_cache.dtype == q.dtype and v_cache.dtype == q.dtype, "q and caches must share a dtype")
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (block_table, "block_table"),
+                 (ctx_lens, "ctx_lens")):
+        _check(t.is_cuda and t.is_contiguous(), f"{n} must be a contiguous GPU tensor")
+    _check(block_table.dtype == torch.int32 and ctx_lens.dtype == torch.int32, "block_table/ctx_lens: int32")
+    B, Hq, D = q.shape
+    NB, Hkv, bs, Dk = k_cache.shape
+    _check(Dk == D, "head size mismatch")
+    _check(block_table.dim() == 2 and block_table.shape[0] == B and ctx_lens.numel() == B, "table shape")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out.shape == q.shape and out.dtype == q.dtype and out.is_contiguous(), "bad out")
+    if lse is not None:
+        _check(lse.shape == (B, Hq) and lse.dtype == torch.float32 and lse.is_contiguous(), "bad lse")
+    with _on(q, k_cache, v_cache, block_table, ctx_lens, out, lse):
+        st = lib().attn_decode_paged_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                             _ptr(ctx_lens), _ptr(out), _ptr(lse), B, Hq, Hkv, D, bs,
+                                             block_table.shape[1], NB, ctypes.c_float(scale), dt, _stream(q.device))
+    _raise(st)
+    return out, lse
 
 
 def attn_decode_paged_fp8(q, k_cache, v_cache, k_scale: float, v_scale: float, block_table, ctx_lens,

@@ -34,6 +34,8 @@
 // products: k_scale into the exponent factor of the scores, v_scale into the
 // final normalisation. This is the fusion of dequantisation into the
 // consuming product named on the-ai.news page's operator-fusion section.
+#include <mutex>
+
 #include "attn_device.h"
 #include "launch.h"
 
@@ -556,6 +558,34 @@ hipError_t launch_decode(const DecodeArgs& a, bool bf16, hipStream_t stream) {
 hipError_t launch_decode_fp8(const DecodeArgs& a, bool bf16, hipStream_t stream) {
   if (a.D == 128) return bf16 ? launch_d<BF16, 128, true>(a, stream) : launch_d<F16, 128, true>(a, stream);
   return bf16 ? launch_d<BF16, 64, true>(a, stream) : launch_d<F16, 64, true>(a, stream);
+}
+
+// Split partials of the entry point that allocates nothing: a file-scope device
+// array, one copy per GPU for the life of the process. In host code its name is
+// a host-side stand-in, not a device address; the device address of each GPU's
+// copy comes from hipGetSymbolAddress with that GPU current, once per device,
+// and only that address is ever handed to a kernel.
+static __device__ __align__(256) char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  *ptr = g_scratch_ptr[dev];
+  return g_scratch_err[dev];
 }
 
 }  // namespace attn

@@ -105,6 +105,13 @@ hipError_t launch_append_fp8(const AppendArgs& a, bool bf16, hipStream_t stream)
 hipError_t launch_append_rope(const AppendArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_decode_fp8(const DecodeArgs& a, bool bf16, hipStream_t stream);
+
+// The no-allocation decode's scratch: a static device array of this many bytes
+// per GPU (the split partials of up to 16 Ki (sequence, query head) pairs with
+// 16 splits of 256 tokens at D = 128). decode_scratch returns the current
+// device's copy's address, looked up once per device with that device current.
+constexpr size_t kDecodeScratchBytes = (size_t)32 << 20;
+hipError_t decode_scratch(void** ptr);
 hipError_t launch_gemm(const GemmArgs& a, const GemmConfig& cfg, bool bf16, hipStream_t stream);
 
 // Workspace: the per-split partials (Hkv is part of the signature so that a

@@ -58,11 +58,13 @@ void scale_mode(float scale, float* c, int* qmode) {
 }
 
 // Shared by the 16-bit and the E4M3 cache forms of the paged decode.
+// use_scratch: the partials go to the library's static per-device scratch array
+// (the no-allocation entry point) instead of the caller's workspace.
 attn_status decode_impl(const char* fn, bool fp8, const void* q, const void* k_cache, const void* v_cache,
                         float k_scale, float v_scale, const float* rope, int max_pos, const int* block_table,
                         const int* ctx_lens, void* o, float* lse, int B, int Hq, int Hkv, int D, int block_size,
                         int max_blocks_per_seq, int num_blocks, float scale, attn_dtype dtype, void* workspace,
-                        size_t workspace_bytes, hipStream_t stream) {
+                        size_t workspace_bytes, hipStream_t stream, bool use_scratch = false) {
   if (!q || !k_cache || !v_cache || !block_table || !ctx_lens || !o)
     return fail(ATTN_ERR_INVALID, "%s: q, caches, block_table, ctx_lens and o must be non-null", fn);
   if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || max_blocks_per_seq < 1 || num_blocks < 1)
@@ -88,7 +90,13 @@ attn_status decode_impl(const char* fn, bool fp8, const void* q, const void* k_c
   if (attn_status st = check_rope(fn, rope, max_pos, D); st != ATTN_OK) return st;
   const size_t need = attn::decode_workspace_bytes(B, Hq, Hkv, D, max_blocks_per_seq);
   const int nsplit = (max_blocks_per_seq + attn::kSplitBlocks - 1) / attn::kSplitBlocks;
-  if (nsplit > 1) {
+  if (use_scratch) {
+    if (need > attn::kDecodeScratchBytes)
+      return fail(ATTN_ERR_UNSUPPORTED,
+                  "%s: the split partials need %zu bytes, more than the %zu-byte scratch of this entry point "
+                  "(use attn_decode_paged with a workspace)",
+                  fn, need, attn::kDecodeScratchBytes);
+  } else if (nsplit > 1) {
     if (!workspace) return fail(ATTN_ERR_INVALID, "%s: workspace is null (%zu bytes needed)", fn, need);
     if (workspace_bytes < need)
       return fail(ATTN_ERR_INVALID, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
@@ -97,6 +105,12 @@ attn_status decode_impl(const char* fn, bool fp8, const void* q, const void* k_c
   }
   if (nsplit > 65535 || Hkv > 65535 || B > 65535 || Hq > 65535)
     return fail(ATTN_ERR_UNSUPPORTED, "%s: grid too large (splits=%d Hkv=%d Hq=%d B=%d)", fn, nsplit, Hkv, Hq, B);
+  if (use_scratch) {
+    // the current device's copy of the scratch array (looked up once per device)
+    const hipError_t e = attn::decode_scratch(&workspace);
+    if (e != hipSuccess || !workspace)
+      return fail(ATTN_ERR_HIP, "%s: device address of the scratch array: %s", fn, hipGetErrorString(e));
+  }
 
   attn::DecodeArgs a;
   a.q = q;
@@ -432,6 +446,15 @@ attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_
   return decode_impl("attn_decode_paged", false, q, k_cache, v_cache, 1.f, 1.f, nullptr, 0, block_table, ctx_lens, o, lse, B,
                      Hq, Hkv, D, block_size, max_blocks_per_seq, num_blocks, scale, dtype, workspace,
                      workspace_bytes, stream);
+}
+
+attn_status attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache, const int* block_table,
+                                      const int* ctx_lens, void* o, float* lse, int B, int Hq, int Hkv, int D,
+                                      int block_size, int max_blocks_per_seq, int num_blocks, float scale,
+                                      attn_dtype dtype, hipStream_t stream) {
+  return decode_impl("attn_decode_paged_noalloc", false, q, k_cache, v_cache, 1.f, 1.f, nullptr, 0, block_table,
+                     ctx_lens, o, lse, B, Hq, Hkv, D, block_size, max_blocks_per_seq, num_blocks, scale, dtype,
+                     nullptr, 0, stream, /*use_scratch=*/true);
 }
 
 attn_status attn_decode_paged_fp8(const void* q, const void* k_cache, const void* v_cache, float k_scale,
