@@ -8,6 +8,8 @@
 //   v_mfma_f32_16x16x32_{bf16,f16}:
 //     A[i = l%16][k = 8*(l/16)+e],  B[k = 8*(l/16)+e][j = l%16]
 //     C register r (4 per lane): row 4*(l/16) + r, column l%16
+//   v_mfma_f32_16x16x16_{bf16,f16} (4 elements per lane):
+//     A[i = l%16][k = 4*(l/16)+e],  B[k = 4*(l/16)+e][j = l%16], C as above
 // Any permutation of the contraction index k applied to both A and B leaves
 // C unchanged; the kernels use that freedom to make every lane's operand one
 // contiguous 16-byte read.
@@ -22,6 +24,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -38,6 +42,11 @@ struct BF16 {
   static __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  // 16x16x16: A[i = l%16][k = 4*(l/16)+e], B[k = 4*(l/16)+e][j = l%16], e < 4
+  static __device__ __forceinline__ f32x4 mfma16k16(u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b),
+                                                     c, 0, 0, 0);
   }
   // two fp32 -> packed pair, round to nearest even (v_cvt_pk_bf16_f32)
   static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
@@ -69,6 +78,10 @@ struct F16 {
   static __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16k16(u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c,
+                                                 0, 0, 0);
   }
   static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     f32x2 v = {lo, hi};

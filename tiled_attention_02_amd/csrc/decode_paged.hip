@@ -50,25 +50,29 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
-// LDS image of one step's cache blocks: K blocks 0 .. NB-1, then V blocks
+// LDS image of one half-step's cache blocks: K blocks 0 .. NB-1, then V blocks
 // 0 .. NB-1, each 16 token rows of RB bytes, row-major with a 16-byte-chunk
 // XOR swizzle: chunk c of row r sits in slot c ^ f(r). LDS serves 256 bytes
 // per cycle (16 lanes of a 16-byte access, 32 lanes of an 8-byte one); f makes
 // the K operand reads and the transposing V reads of each lane group hit
-// distinct banks.
+// distinct banks. A wavefront owns NBUF such buffers, 16 KiB together at
+// D = 128, so ten wavefronts fit a CU either way.
 template <int D, bool KV8>
 struct StepLds {
-  // cache blocks per step: 2 for the 16-bit cache, 4 for the E4M3 cache, so
-  // both move 16 KiB per step (ten wavefronts per CU either way; the E4M3
-  // cache with 2 blocks per step, 8 KiB, measured 3-4 % slower on the
-  // Qwen-shaped batch: fewer bytes in flight per wavefront)
-  static constexpr int NB = KV8 ? 4 : 2;
+  // 16-bit cache: steps of 1 block (16 tokens, 8 KiB of K and V) in two step
+  // buffers (one in flight during the other's compute; measured 2.7 % faster
+  // than one buffer of 2 blocks). E4M3 cache: steps of 4 blocks (64 tokens,
+  // 16 KiB) in one buffer, loaded after the step's reads (measured 2.7 %
+  // faster than two buffers of 2 blocks).
+  static constexpr int NB = KV8 ? 4 : 1;
+  static constexpr int NBUF = KV8 ? 1 : 2;
   static constexpr int EB = KV8 ? 1 : 2;     // bytes per cache element
   static constexpr int RB = EB * D;          // bytes per token row
   static constexpr int BLK = 16 * RB;        // one (block, kv head) of K or V
-  static constexpr int BYTES = 2 * NB * BLK;
+  static constexpr int BYTES = 2 * NB * BLK; // one step buffer
   static constexpr int RPI = 1024 / RB;      // rows filled by one wavefront load instruction
   static constexpr int NI = 16 / RPI;        // load instructions per block
+  static constexpr int LOADS = 2 * NB * NI;  // load instructions per step
   static constexpr int C8 = RB / 16;         // 16-byte chunks per row
 };
 
@@ -282,40 +286,54 @@ __device__ __forceinline__ void step_compute(WaveState<D>& st, char* buf, const 
       pv[4 * j + r] = fast_exp2(__builtin_fmaf(sacc[j][r], cexp, -msub));
       st.l += pv[4 * j + r];
     }
-  // P of each block pair h: in lane group g, tokens 4g .. 4g+3 of block 2h,
-  // then of block 2h + 1; the transposing reads give V in the same order
-  u32x4 pf[NB / 2];
+  if constexpr (NB == 1) {
+    // one 16-bit block: P (heads x 16 tokens; lane group g holds tokens 4g ..
+    // 4g + 3, the scores' own layout) times V (16 tokens x 16 columns, one
+    // transposing read) on the 16x16x16 instruction
+    const u32x2 pf = {T::pack2(pv[0], pv[1]), T::pack2(pv[2], pv[3])};
+    st.lr = T::sum2(pf[1], T::sum2(pf[0], st.lr));  // the rounded probabilities the product applies
 #pragma unroll
-  for (int h = 0; h < NB / 2; ++h) {
-    const float* v = pv + 8 * h;
-    pf[h] = u32x4{T::pack2(v[0], v[1]), T::pack2(v[2], v[3]), T::pack2(v[4], v[5]), T::pack2(v[6], v[7])};
-    // the running sum adds the rounded probabilities that the P.V product applies
+    for (int n = 0; n < VC; ++n) {
+      const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(buf + L::BLK + o.v[n]));
+      st.o[n] = T::mfma16k16(pf, __builtin_bit_cast(u32x2, v), st.o[n]);
+    }
+  } else {
+    // P of each block pair h: in lane group g, tokens 4g .. 4g+3 of block 2h,
+    // then of block 2h + 1; the transposing reads give V in the same order
+    u32x4 pf[NB / 2];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) st.lr = T::sum2(pf[h][e], st.lr);
-  }
+    for (int h = 0; h < NB / 2; ++h) {
+      const float* v = pv + 8 * h;
+      pf[h] = u32x4{T::pack2(v[0], v[1]), T::pack2(v[2], v[3]), T::pack2(v[4], v[5]), T::pack2(v[6], v[7])};
+      // the running sum adds the rounded probabilities that the P.V product applies
 #pragma unroll
-  for (int n = 0; n < VC; ++n) {
-    if constexpr (KV8) {
+      for (int e = 0; e < 4; ++e) st.lr = T::sum2(pf[h][e], st.lr);
+    }
 #pragma unroll
-      for (int h = 0; h < NB / 2; ++h) {
-        const i32x2 v8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(buf + o.v[n] + 2 * h * L::BLK));
-        st.o[n] = T::mfma16(pf[h], e4m3x8<T>(__builtin_bit_cast(u32x2, v8)), st.o[n]);
+    for (int n = 0; n < VC; ++n) {
+      if constexpr (KV8) {
+#pragma unroll
+        for (int h = 0; h < NB / 2; ++h) {
+          const i32x2 v8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(buf + o.v[n] + 2 * h * L::BLK));
+          st.o[n] = T::mfma16(pf[h], e4m3x8<T>(__builtin_bit_cast(u32x2, v8)), st.o[n]);
+        }
+      } else {
+        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(buf + NB * L::BLK + o.v[n]));
+        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(buf + (NB + 1) * L::BLK + o.v[n]));
+        const u32x2 a0 = __builtin_bit_cast(u32x2, v0);
+        const u32x2 a1 = __builtin_bit_cast(u32x2, v1);
+        st.o[n] = T::mfma16(pf[0], u32x4{a0[0], a0[1], a1[0], a1[1]}, st.o[n]);
       }
-    } else {
-      const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(buf + 2 * L::BLK + o.v[n]));
-      const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(buf + 3 * L::BLK + o.v[n]));
-      const u32x2 a0 = __builtin_bit_cast(u32x2, v0);
-      const u32x2 a1 = __builtin_bit_cast(u32x2, v1);
-      st.o[n] = T::mfma16(pf[0], u32x4{a0[0], a0[1], a1[0], a1[1]}, st.o[n]);
     }
   }
 }
 
-// One step buffer per wavefront (16 KiB at D = 128), loaded after the previous
-// step's reads: ten wavefronts per CU stay resident, so every workgroup of a
-// typical batch starts at once and the memory system has far more than the
-// bytes in flight it needs. A second buffer (the next step's loads in flight
-// during the math) halves the resident wavefronts and measured 4 % slower.
+// Step buffers per wavefront: 16 KiB together at D = 128. With two (16-bit
+// cache), step p + 1's blocks travel into one while step p computes from the
+// other, and step p + 2's loads start as soon as step p's reads have returned;
+// with one (E4M3 cache), step p + 1's loads start once step p's reads have
+// returned. Ten wavefronts per CU fit, so every workgroup of a typical batch
+// starts at once.
 template <class T, int D, bool KV8>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   using L = StepLds<D, KV8>;
@@ -324,7 +342,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   constexpr int NB = L::NB;
   constexpr int NS = kSplitBlocks / NB;  // steps per split
   static_assert(D == 128 || D == 64, "head size");
-  __shared__ __align__(16) char buf[L::BYTES];
+  static_assert(L::NBUF == 1 || L::LOADS == 8 || L::LOADS == 4, "step load count (the partial wait below)");
+  __shared__ __align__(16) char buf[L::NBUF * L::BYTES];
 
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
@@ -421,6 +440,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     int ph[NB];
     step_blocks(0, ph);
     load_step<D, KV8>(buf, kbase, vbase, block_stride, ph, a.num_blocks, o);
+    if (L::NBUF == 2 && ns > 1) {
+      step_blocks(1, ph);
+      load_step<D, KV8>(buf + L::BYTES, kbase, vbase, block_stride, ph, a.num_blocks, o);
+    }
   }
 
   if (a.rope) {
@@ -449,19 +472,30 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
   for (int p = 0; p < NS; ++p) {
     if (p >= ns) break;  // wave-uniform
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // step p (and q) have landed
+    // step p has landed: with step p + 1's loads issued after it, at most
+    // those LOADS instructions may still be outstanding (loads complete in
+    // order for this count)
+    if (L::NBUF == 2 && p + 1 < ns) {
+      if constexpr (L::LOADS == 8)
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    char* cur = buf + (L::NBUF == 2 ? (p & 1) * L::BYTES : 0);
     const int t0 = (blk0 + NB * p) * kDecodeBlock;
     if (t0 + 16 * NB > ctx)
-      step_compute<T, D, KV8, true>(st, buf, qf, o, t0, ctx, cexp, lane);
+      step_compute<T, D, KV8, true>(st, cur, qf, o, t0, ctx, cexp, lane);
     else
-      step_compute<T, D, KV8, false>(st, buf, qf, o, t0, ctx, cexp, lane);
-    if (p + 1 < NS && p + 1 < ns) {
-      // every read of the buffer has returned before new data is written to it
+      step_compute<T, D, KV8, false>(st, cur, qf, o, t0, ctx, cexp, lane);
+    if (p + L::NBUF < NS && p + L::NBUF < ns) {
+      // every read of this buffer has returned before a later step's data is written to it
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      const int q = p + 1 < NS ? p + 1 : 0;  // in range also where the branch is dead
+      const int q = p + L::NBUF < NS ? p + L::NBUF : 0;  // in range also where the branch is dead
       int ph[NB];
       step_blocks(q, ph);
-      load_step<D, KV8>(buf, kbase, vbase, block_stride, ph, a.num_blocks, o);
+      load_step<D, KV8>(cur, kbase, vbase, block_stride, ph, a.num_blocks, o);
     }
   }
 
