@@ -1,11 +1,15 @@
-"""Race check of the prefill's K/V staging: the pipelined kernel (libattn.so: K two tiles ahead, V one
-tile ahead, double-buffered in on-chip memory, one barrier per tile) against the same code built with
-its debug key loop (libattn_single.so: one K and one V buffer, each tile loaded, waited for and consumed
-before the next load, nothing overlapped). Both run the same arithmetic in the same order, so every
-output and lse must agree bit for bit; a wavefront that overwrote a buffer another wavefront was still
-reading would show as a difference. Every prefill form is covered (contiguous causal / non-causal /
-ragged, Tq != Tk, chunked through the block table over 16-bit, rotary and E4M3 caches, and the FP8
-prefill), at sizes of one, two, three and many key tiles (three is the first that reuses a buffer).
+"""Race check of the prefill's K/V staging: the pipelined kernel (libattn.so) against the same code built
+with its debug key loop (libattn_single.so: one K and one V buffer, each tile loaded, waited for and
+consumed before the next load, nothing overlapped). The pipelined kernel has two forms: double buffering
+(K two tiles ahead, V one ahead, every load awaited at the end of its step) and, in the FP8 prefill, the
+P.V product lagged by one tile over four-deep rings (K four tiles ahead of its scores, V three ahead of its
+product, loads left in flight across barriers, waits counted per tile). Both forms run the same arithmetic in the same order
+as the debug loop, so every output and lse must agree bit for bit; a wavefront that overwrote a buffer
+another wavefront was still reading, or read one before its loads landed, would show as a difference.
+Every prefill form is covered (contiguous causal / non-causal / ragged, Tq != Tk, chunked through the
+block table over 16-bit, rotary and E4M3 caches, and the FP8 prefill), at sizes of one, two, three and
+many key tiles (three is the first that reuses a double buffer, five the first that reuses a ring
+buffer), and a grid larger than the chip.
 """
 import numpy as np
 import pytest
@@ -88,6 +92,16 @@ def test_long_causal(ta):
     x = W.prefill_inputs(case)
     q, k, v = (_dev(x[n], "bf16") for n in ("q", "k", "v"))
     _both(ta, lambda: ta.attn_fwd(q, k, v, scale=case.scale, causal=True), "T=4096 causal bf16")
+
+
+@pytest.mark.parametrize("D,dtype", [(128, "bf16"), (64, "fp16")])
+def test_large_grid(ta, D, dtype):
+    # B * Hq * ceil(T / 128) = 576 workgroups: more than the chip holds at once
+    case = W.PrefillCase("sb-grid", B=2, Hq=32, Hkv=8, T=1100, D=D, dtype=dtype, causal=True, ragged=False,
+                         seed=514)
+    x = W.prefill_inputs(case)
+    q, k, v = (_dev(x[n], dtype) for n in ("q", "k", "v"))
+    _both(ta, lambda: ta.attn_fwd(q, k, v, scale=case.scale, causal=True), f"B=2 Hq=32 T=1100 D={D} causal")
 
 
 @pytest.mark.parametrize("form", ["16-bit", "rotary", "E4M3"])

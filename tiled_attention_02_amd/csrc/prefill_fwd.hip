@@ -47,16 +47,23 @@
 // the other's softmax), K/V tiles double-buffered in LDS with one barrier per
 // tile: tile j+1 travels HBM -> LDS directly (buffer loads that write LDS)
 // while tile j is consumed. LDS operand reads are issued ahead of the MFMAs
-// that consume them (register double buffering).
+// that consume them (register double buffering). Within a step, the scores of
+// tile j+1 are computed beside tile j's exponentials.
+//
+// The FP8 form lags the P.V product by one tile: step j computes the scores
+// of tile j+1 and the product of tile j-1 beside tile j's exponentials, over
+// four-deep K/V rings in LDS whose loads stay in flight across barriers (the
+// waits count tiles). Its 8-bit tiles keep the rings at 64 KiB per workgroup.
 //
 // FP8 form (contiguous E4M3 q, k, v; KV8 without PAGED): both products run on
 // v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales), twice the bf16 rate.
 // A lane's 32 contraction slots are 32 consecutive dims of its row for S^T,
 // and for O^T += V^T P^T the lane's own 32 keys of the tile (the B operand P^T
 // is the lane's 32 probabilities, rounded to E4M3 after scaling by 2^7; the
-// A operand V^T is 4 ds_read_b64_tr_b8 in the same key order). The running
-// max moves once it grows by more than 1 (log2), so p <= 2 and the scaled p
-// stay <= 2^8; O is divided by the fp32 sum of the unrounded scaled p. Error
+// A operand V^T is 4 ds_read_b64_tr_b8 in the same key order). Each tile's
+// max is taken before its exponentials; the running max moves once it grows
+// by more than 1 (log2), so p <= 2 and the scaled p stay <= 2^8; O is divided
+// by the fp32 sum of the unrounded scaled p. Error
 // of the rounding of P per output element (row i, column d): at most
 // 2^-4 sum_j P_ij |v_jd| + 2^-17 max_j P_ij sum_j |v_jd| over the row's keys
 // (2^-4 relative in E4M3's normal range, 2^-17 absolute below it).
@@ -258,22 +265,28 @@ __device__ __forceinline__ int q_col(int s, int h) {
   return KV8 ? 32 * (s >> 1) + 16 * h + 8 * (s & 1) : 16 * s + 8 * h;
 }
 
+// The sign flip (qmode 1) and zeroing (qmode 2, and rows past the sequence)
+// of Q's fragments, applied after load_q where Q is first used, so that Q's
+// loads stay in flight behind the first tiles' loads until then.
+template <class T, int D, bool F8>
+__device__ __forceinline__ void q_modes(Acc<D>& st, const Geo& g, int qmode, int qrow) {
+  const uint32_t flip = qmode == 1 ? (F8 ? 0x80808080u : 0x80008000u) : 0u;
+  const bool zero = qmode == 2 || !(qrow < g.Lq);
+#pragma unroll
+  for (int s = 0; s < (F8 ? D / 32 : D / 16); ++s) st.qf[s] = zero ? u32x4{0, 0, 0, 0} : st.qf[s] ^ flip;
+}
+
 template <class T, int D, bool KV8, bool F8 = false>
 __device__ __forceinline__ void load_q(Acc<D>& st, const Geo& g, int qmode, int qrow, int h, const float* rope,
                                        int max_pos, const uint8_t* q8 = nullptr) {
   const bool live = qrow < g.Lq;
   if constexpr (F8) {
     // k-step p (64 dims): lane half h holds dims 64p + 32h .. +32 (32 codes)
-    const uint32_t flip8 = qmode == 1 ? 0x80808080u : 0u;
-    const bool zero8 = qmode == 2 || !live;
     const uint8_t* src8 = q8 + (size_t)(live ? qrow : 0) * D + 32 * h;
 #pragma unroll
     for (int p = 0; p < D / 64; ++p)
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(src8 + 64 * p + 16 * u) ^ flip8;
-        st.qf[2 * p + u] = zero8 ? u32x4{0, 0, 0, 0} : x;
-      }
+      for (int u = 0; u < 2; ++u) st.qf[2 * p + u] = *reinterpret_cast<const u32x4*>(src8 + 64 * p + 16 * u);
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) st.oacc[i] = f32x16{};
     st.m = -__builtin_inff();
@@ -281,8 +294,6 @@ __device__ __forceinline__ void load_q(Acc<D>& st, const Geo& g, int qmode, int 
     st.lr = 0.f;
     return;
   }
-  const uint32_t flip = qmode == 1 ? 0x80008000u : 0u;
-  const bool zero = qmode == 2 || !live;
   const uint16_t* src = g.Qg + (size_t)(live ? qrow : 0) * D;
   u32x4 x[D / 16];
 #pragma unroll
@@ -303,10 +314,7 @@ __device__ __forceinline__ void load_q(Acc<D>& st, const Geo& g, int qmode, int 
     }
   }
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    x[s] ^= flip;
-    st.qf[s] = zero ? u32x4{0, 0, 0, 0} : x[s];
-  }
+  for (int s = 0; s < D / 16; ++s) st.qf[s] = x[s];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) st.oacc[i] = f32x16{};
   st.m = -__builtin_inff();
@@ -314,17 +322,23 @@ __device__ __forceinline__ void load_q(Acc<D>& st, const Geo& g, int qmode, int 
   st.lr = 0.f;
 }
 
-// Per-lane LDS read offsets (identical for every tile).
+// Per-lane LDS read offsets (identical for every tile). E4M3 tiles: one per
+// read. 16-bit tiles: a base per operand, from which koff / voff derive each
+// read's offset with one XOR (see make_offs), so the key loop holds 2
+// registers instead of D/8.
 template <int D, int BK>
 struct Offs {
   int k[D / 16];
   int v[D / 32][2];
+  int k0, v0;
 };
 
 template <int D, int BK, bool KV8, bool F8 = false>
 __device__ __forceinline__ void make_offs(Offs<D, BK>& o, int lane) {
   using S = Shape<D, BK, KV8>;
   const int h = lane >> 5, c32 = lane & 31, g16 = lane >> 4, i16 = lane & 15;
+  o.k0 = 0;
+  o.v0 = 0;
   if constexpr (KV8) {
     if constexpr (F8) {
       // K: 64-dim step p from two 16-byte reads of row c32 at chunks 4p + 2h, +1
@@ -352,25 +366,30 @@ __device__ __forceinline__ void make_offs(Offs<D, BK>& o, int lane) {
     return;
   }
   // K operand of k-step s: row kb*32 + c32, chunk (2s + h) ^ swz(row); swz(row)
-  // does not depend on kb because kb*32 is a multiple of 16.
-  const int sw = swz<D>(c32);
-#pragma unroll
-  for (int s = 0; s < S::KS; ++s) o.k[s] = c32 * S::RB + 16 * ((2 * s + h) ^ sw);
+  // does not depend on kb because kb*32 is a multiple of 16. As 2s + h =
+  // 2s ^ h, the chunk is (h ^ swz) ^ 2s: koff(s) = k0 ^ 32s (the row's bytes
+  // start at a multiple of RB, above the chunk bits).
+  o.k0 = c32 * S::RB + 16 * (h ^ swz<D>(c32));
   // V^T operand: k-step s covers keys 16s + 8r + 4h + (0..3) for element group
   // r = 0, 1; lane i of 16-lane group g addresses row (those keys' base) + i/4
   // at columns 32db + 16(g%2) + 4(i%4) and receives column 32db + 16(g%2) + i.
   // The swizzle of row 16s + 8r + vr depends only on r and the lane (16s + 8r
-  // is a multiple of 8), so the offset is v[db][r] + 16s * RB.
+  // is a multiple of 8), so the offset is voff(db, r) + 16s * RB. The column's
+  // chunk is 4db ^ (vc / 8), and swz(8r + vr) = swz(vr) ^ 2r (D = 128) or
+  // ^ r (D = 64), so voff(db, r) = (v0 ^ 64db ^ XR r) + 8r RB, XR = 32 or 16.
   const int vr = 4 * h + (i16 >> 2);
   const int vc = 16 * (g16 & 1) + 4 * (i16 & 3);
-#pragma unroll
-  for (int db = 0; db < S::DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int row = 8 * r + vr;
-      const int col = 32 * db + vc;
-      o.v[db][r] = row * S::RB + 16 * ((col >> 3) ^ swz<D>(row)) + 2 * (col & 7);
-    }
+  o.v0 = vr * S::RB + 16 * ((vc >> 3) ^ swz<D>(vr)) + 2 * (vc & 7);
+}
+
+template <int D, int BK, bool KV8>
+__device__ __forceinline__ int koff(const Offs<D, BK>& o, int s) {
+  return KV8 ? o.k[s] : (o.k0 ^ (32 * s));
+}
+template <int D, int BK, bool KV8>
+__device__ __forceinline__ int voff(const Offs<D, BK>& o, int db, int r) {
+  if constexpr (KV8) return o.v[db][r];
+  return (o.v0 ^ (64 * db) ^ ((D == 128 ? 32 : 16) * r)) + 8 * 2 * D * r;
 }
 
 // S^T = K Q^T for one tile in LDS. The K fragments of k-step s+2 are read
@@ -440,13 +459,14 @@ __device__ __forceinline__ void tile_qk_plain(f32x16 (&sacc)[BK / 32], const cha
   for (int s = 0; s < DEPTH; ++s)
 #pragma unroll
     for (int kb = 0; kb < S::KB; ++kb)
-      fr[s][kb] = *reinterpret_cast<const u32x4*>(Ks + kb * 32 * S::RB + o.k[s]);
+      fr[s][kb] = *reinterpret_cast<const u32x4*>(Ks + kb * 32 * S::RB + koff<D, BK, false>(o, s));
 #pragma unroll
   for (int s = 0; s < S::KS; ++s) {
     if (s + DEPTH < S::KS) {
 #pragma unroll
       for (int kb = 0; kb < S::KB; ++kb)
-        fr[(s + DEPTH) % (DEPTH + 1)][kb] = *reinterpret_cast<const u32x4*>(Ks + kb * 32 * S::RB + o.k[s + DEPTH]);
+        fr[(s + DEPTH) % (DEPTH + 1)][kb] =
+            *reinterpret_cast<const u32x4*>(Ks + kb * 32 * S::RB + koff<D, BK, false>(o, s + DEPTH));
     }
 #pragma unroll
     for (int kb = 0; kb < S::KB; ++kb) sacc[kb] = T::mfma32(fr[s % (DEPTH + 1)][kb], st.qf[s], sacc[kb]);
@@ -476,8 +496,10 @@ __device__ __forceinline__ u32x4 vt_frag(const char* Vs, const Offs<D, BK>& o, i
     const i32x2 v8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(Vs + 16 * s * S::RB + o.v[db][0]));
     return e4m3x8<T>(__builtin_bit_cast(u32x2, v8));
   }
-  const i16x4 p0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vs + 16 * s * S::RB + o.v[db][0]));
-  const i16x4 p1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vs + 16 * s * S::RB + o.v[db][1]));
+  const i16x4 p0 =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vs + 16 * s * S::RB + voff<D, BK, false>(o, db, 0)));
+  const i16x4 p1 =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vs + 16 * s * S::RB + voff<D, BK, false>(o, db, 1)));
   const u32x2 a0 = __builtin_bit_cast(u32x2, p0);
   const u32x2 a1 = __builtin_bit_cast(u32x2, p1);
   return u32x4{a0[0], a0[1], a1[0], a1[1]};
@@ -539,85 +561,112 @@ __device__ __forceinline__ void softmax_mask(f32x16 (&sacc)[BK / 32], const Geo&
   }
 }
 
-// Tile max and lazy rescale: the running max moves when the tile's max
-// exceeds it by more than the margin; returns the max to subtract.
-template <class T, int D, int BK, bool F8 = false>
-__device__ __forceinline__ float softmax_max(const f32x16 (&sacc)[BK / 32], Acc<D>& st, float cexp) {
-  // FP8 form: the max moves once it grows by more than 1 (log2 units), so
-  // p <= 2 and the scaled p * 2^7 stay <= 2^8, inside E4M3's range
-  constexpr float kMargin = F8 ? kF8Margin : kLazyRescale;
+// Tile max in log2 units (raw scores times cexp > 0; -inf stays -inf).
+template <int D, int BK>
+__device__ __forceinline__ float tile_max(const f32x16 (&sacc)[BK / 32], float cexp) {
   using S = Shape<D, BK>;
-  // tile max (raw scores; cexp > 0)
   float mx = sacc[0][0];
 #pragma unroll
   for (int kb = 0; kb < S::KB; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-  mx = half_swap_max(mx) * cexp;  // -inf stays -inf (cexp > 0)
-  const bool grow = mx > st.m + kMargin;
-  if (__builtin_amdgcn_ballot_w64(grow)) {
-    const float m_new = grow ? mx : st.m;
-    const float alpha = grow ? fast_exp2(st.m - m_new) : 1.f;  // m = -inf -> 0
-    st.m = m_new;
-    st.l *= alpha;
-    st.lr *= alpha;
+  return half_swap_max(mx) * cexp;
+}
+
+// Lazy rescale: the running max moves to the tile max mx where that exceeds
+// it by more than the margin (16-bit products: 8, so p <= 2^8; FP8 form: 1,
+// so p <= 2 and the scaled p * 2^7 stay <= 2^8, inside E4M3's range). Callers
+// take the wavefront-wide vote first; a lane whose max stays keeps alpha = 1.
+template <int D, bool F8>
+__device__ __forceinline__ bool max_grows(float mx, const Acc<D>& st) {
+  return mx > st.m + (F8 ? kF8Margin : kLazyRescale);
+}
+template <int D, bool F8>
+__device__ __forceinline__ void rescale(Acc<D>& st, float mx) {
+  const bool grow = max_grows<D, F8>(mx, st);
+  const float m_new = grow ? mx : st.m;
+  const float alpha = grow ? fast_exp2(st.m - m_new) : 1.f;  // m = -inf -> 0
+  st.m = m_new;
+  st.l *= alpha;
+  st.lr *= alpha;
 #pragma unroll
-    for (int i = 0; i < S::DB; ++i) st.oacc[i] *= alpha;
-  }
+  for (int i = 0; i < D / 32; ++i) st.oacc[i] *= alpha;
+}
+template <int D>
+__device__ __forceinline__ float max_to_subtract(const Acc<D>& st) {
   return st.m == -__builtin_inff() ? 0.f : st.m;
 }
 
-// p = 2^(s*c - m), the two running sums, and the P^T operand (no branches).
+// p = 2^(s*c - m) for the lane's 16 scores of key block kb, their fp32
+// partial sums and the P^T operand (no branches). 16-bit: two groups of 8
+// (group 2 kb + hf), each with the sum of its rounded p, which the normaliser
+// adds (the weights the P.V product applies). FP8 form: four groups of 4,
+// p * 2^7 rounded to E4M3; byte 16 kb + r of the lane's P^T operand is key
+// kb*32 + 8(r/4) + 4h + r%4, as in the scores' layout.
+template <class T, int D, int BK, bool F8>
+__device__ __forceinline__ void exp_block(const f32x16 (&sacc)[BK / 32], u32x4 (&pf)[BK / 16], int kb,
+                                          float (&lsum)[BK / 8], float (&lrsum)[BK / 8], float msub, float cexp) {
+  if constexpr (F8) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      float p[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p[e] = fast_exp2(__builtin_fmaf(sacc[kb][4 * w + e], cexp, kF8PScaleLog2 - msub));
+      lsum[4 * kb + w] = (p[0] + p[1]) + (p[2] + p[3]);
+      int r = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+      r = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], r, true);
+      pf[kb][w] = (uint32_t)r;
+    }
+    return;
+  }
+  // one partial sum per 8 probabilities keeps the dependency chains short, so
+  // the work interleaves with the matrix instructions beside it
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const int i = kb * 2 + hf;
+    float p[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p[e] = fast_exp2(__builtin_fmaf(sacc[kb][8 * hf + e], cexp, -msub));
+    lsum[i] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    const u32x4 pk = {T::pack2(p[0], p[1]), T::pack2(p[2], p[3]), T::pack2(p[4], p[5]), T::pack2(p[6], p[7])};
+    lrsum[i] = T::sum2(pk[3], T::sum2(pk[2], T::sum2(pk[1], T::sum2(pk[0], 0.f))));
+    pf[i] = pk;
+  }
+}
+
+// Adds a tile's partial sums to the running sums (in a fixed order); returns
+// the tile's fp32 sum.
+template <int D, int BK, bool F8>
+__device__ __forceinline__ float exp_finish(Acc<D>& st, const float (&lsum)[BK / 8], const float (&lrsum)[BK / 8]) {
+  constexpr int NG = F8 ? BK / 8 : BK / 16;
+  float ls = 0.f, lrs = 0.f;
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    ls += lsum[i];
+    if constexpr (!F8) lrs += lrsum[i];
+  }
+  st.l += ls;
+  // FP8 form: O is divided by the sum of the unrounded scaled p
+  st.lr = F8 ? st.l : st.lr + lrs;
+  return ls;
+}
+
+// The exponentials of a whole tile; returns its fp32 sum.
 template <class T, int D, int BK, bool F8 = false>
 __device__ __forceinline__ float softmax_exp(const f32x16 (&sacc)[BK / 32], u32x4 (&pf)[BK / 16], Acc<D>& st,
                                              float msub, float cexp) {
-  using S = Shape<D, BK>;
-  if constexpr (F8) {
-    // p * 2^7 (<= 2^8), rounded to E4M3: byte 16 kb + r of the lane's P^T
-    // operand is key kb*32 + 8(r/4) + 4h + r%4, as in the scores' layout
-    float ls = 0.f;
+  float lsum[BK / 8], lrsum[BK / 8];
 #pragma unroll
-    for (int kb = 0; kb < S::KB; ++kb)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        float p[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) p[e] = fast_exp2(__builtin_fmaf(sacc[kb][4 * w + e], cexp, kF8PScaleLog2 - msub));
-        ls += (p[0] + p[1]) + (p[2] + p[3]);
-        int r = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-        r = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], r, true);
-        pf[kb][w] = (uint32_t)r;
-      }
-    st.l += ls;
-    st.lr = st.l;
-    return ls;
-  }
-  // one partial sum per 8 probabilities keeps the dependency chains short, so
-  // the work interleaves with the matrix instructions of the next tile
-  float lsum[S::PS], lrsum[S::PS];
-#pragma unroll
-  for (int kb = 0; kb < S::KB; ++kb)
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const int i = kb * 2 + hf;
-      float p[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) p[e] = fast_exp2(__builtin_fmaf(sacc[kb][8 * hf + e], cexp, -msub));
-      lsum[i] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-      const u32x4 pk = {T::pack2(p[0], p[1]), T::pack2(p[2], p[3]), T::pack2(p[4], p[5]), T::pack2(p[6], p[7])};
-      // the normaliser adds the rounded probabilities the P.V product uses
-      lrsum[i] = T::sum2(pk[3], T::sum2(pk[2], T::sum2(pk[1], T::sum2(pk[0], 0.f))));
-      pf[i] = pk;
-    }
-  float ls = 0.f, lrs = 0.f;
-#pragma unroll
-  for (int i = 0; i < S::PS; ++i) {
-    ls += lsum[i];
-    lrs += lrsum[i];
-  }
-  st.l += ls;
-  st.lr += lrs;
-  return ls;
+  for (int kb = 0; kb < BK / 32; ++kb) exp_block<T, D, BK, F8>(sacc, pf, kb, lsum, lrsum, msub, cexp);
+  return exp_finish<D, BK, F8>(st, lsum, lrsum);
+}
+
+// Tile max and lazy rescale; returns the max to subtract.
+template <class T, int D, int BK, bool F8 = false>
+__device__ __forceinline__ float softmax_max(const f32x16 (&sacc)[BK / 32], Acc<D>& st, float cexp) {
+  const float mx = tile_max<D, BK>(sacc, cexp);
+  if (__builtin_amdgcn_ballot_w64(max_grows<D, F8>(mx, st))) rescale<D, F8>(st, mx);
+  return max_to_subtract(st);
 }
 
 // O = O^T / l, lse = (m + log2 l) ln 2; padding rows -> 0, -inf.
@@ -746,7 +795,15 @@ struct Stager {
   // only ever compiled for the device.
   static __device__ __forceinline__ void load_lds(__amdgpu_buffer_rsrc_t rsrc, char* dst, int voffset) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16, voffset, 0, 0, 0);
+    // The LDS address passes through an empty asm statement, which hides
+    // which LDS array the load writes: the compiler then inserts no waits of
+    // its own before LDS reads (its per-array tracking of these loads is
+    // coarse across loop iterations and would wait for tiles the kernel
+    // means to leave in flight). Every LDS read of a staged tile follows the
+    // kernel's explicit wait and barrier.
+    uint32_t lds = (uint32_t)(uintptr_t)(lds_void*)dst;
+    asm volatile("" : "+s"(lds));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(uintptr_t)lds, 16, voffset, 0, 0, 0);
 #else
     (void)rsrc;
     (void)dst;
@@ -762,47 +819,52 @@ __device__ __forceinline__ void staged_barrier() {
   __syncthreads();
 }
 
-// The end of a tile's arithmetic, shared by the pipelined and the debug key
-// loops: with 16-bit products, a lane whose 32 probabilities sum past 2^15
-// (or to inf / NaN: the first visible tile, where the running max is -inf)
-// needs the running max moved first, so the tile's exponentials are redone
-// after the lazy rescale (below that sum every p <= 2^15 stays inside fp16's
-// range and the P operand keeps the relative precision of any other p); then
-// O^T += V^T P^T.
-template <class T, int D, int BK, bool KV8, bool F8>
+// The end of a tile's arithmetic in the double-buffered key loop and its
+// debug form (16-bit products: contiguous and paged 16-bit tiles, paged E4M3
+// tiles): a lane whose 32 probabilities sum past 2^15 (or to inf / NaN: the
+// first visible tile, where the running max is -inf) needs the running max
+// moved first, so the tile's exponentials are redone after the lazy rescale
+// (below that sum every p <= 2^15 stays inside fp16's range and the P operand
+// keeps the relative precision of any other p); then O^T += V^T P^T.
+template <class T, int D, int BK, bool KV8>
 __device__ __forceinline__ void finish_tile(const f32x16 (&s_cur)[BK / 32], u32x4 (&pf)[BK / 16], Acc<D>& st,
                                             const Offs<D, BK>& o, const char* vcur, float ls, float l0, float lr0,
                                             float cexp) {
-  if constexpr (!F8) {
-    if (__builtin_amdgcn_ballot_w64(!(ls <= kOptimisticSum))) {
-      st.l = l0;
-      st.lr = lr0;
-      const float m2 = softmax_max<T, D, BK>(s_cur, st, cexp);
-      softmax_exp<T, D, BK>(s_cur, pf, st, m2, cexp);
-    }
+  if (__builtin_amdgcn_ballot_w64(!(ls <= kOptimisticSum))) {
+    st.l = l0;
+    st.lr = lr0;
+    const float m2 = softmax_max<T, D, BK>(s_cur, st, cexp);
+    softmax_exp<T, D, BK>(s_cur, pf, st, m2, cexp);
   }
   __builtin_amdgcn_s_setprio(2);
-  tile_pv<T, D, BK, KV8, F8>(st, pf, vcur, o);
+  tile_pv<T, D, BK, KV8>(st, pf, vcur, o);
   __builtin_amdgcn_s_setprio(0);
 }
 
-// One pipelined key step kt. On entry the scores of tile kt (s_cur) are in
-// registers, K of tile kt+1 and V of tile kt are in LDS. The step starts the
-// loads of K_{kt+2} and V_{kt+1} into the buffers read one step earlier, then
-//   * masks tile kt where needed, takes its max and rescales lazily (VALU);
+// One key step kt of the double-buffered loop (16-bit products). On entry
+// the scores of tile kt (s_cur) are in registers, K of tile kt+1 and V of
+// tile kt are in LDS. The step starts the loads of K_{kt+2} and V_{kt+1} into
+// the buffers read one step earlier, then
+//   * masks tile kt where needed (VALU);
 //   * computes S of tile kt+1 (MFMA) interleaved with the exponentials, sums
-//     and packing of tile kt (VALU): the matrix core and the vector ALU of
-//     the wavefront work at the same time;
+//     and packing of tile kt (VALU) under the running max as it stands (no
+//     tile max on the way): the matrix core and the vector ALU of the
+//     wavefront work at the same time;
 //   * accumulates O^T += V^T P^T for tile kt (MFMA);
 // and ends with the wait for its loads and a barrier.
-template <class T, int D, int BK, bool CAUSAL, bool KV8, bool F8, class KStg, class VStg>
+template <class T, int D, int BK, bool CAUSAL, bool KV8, class KStg, class VStg>
 __device__ __forceinline__ void pipe_step(int kt, const char* kcur, const char* vcur, char* kload, char* vload,
                                           f32x16 (&s_cur)[BK / 32], f32x16 (&s_nxt)[BK / 32],
                                           const KStg& ks, const VStg& vs,
-                                          int (&ecar)[KStg::EPT], Acc<D>& st, const Offs<D, BK>& o,
+                                          int (&ecar)[KStg::EPT], Acc<D>& st, const Offs<D, BK>& o_in,
                                           const Geo& g, bool wave_live, int w_last, int w_lo, int qrow, int h,
                                           float cexp) {
   using S = Shape<D, BK>;
+  // 16-bit tiles: the offset bases pass through an empty asm statement, so the
+  // per-read offsets derived from them are computed inside the step, where
+  // they are used, instead of living in registers across the loop
+  Offs<D, BK> o = o_in;
+  if constexpr (!KV8) asm volatile("" : "+v"(o.k0), "+v"(o.v0));
   // (paged form) ecar: the physical blocks of tile kt+1, read one step earlier
   // for its K and reused now for its V
   if (kt + 2 < g.nkt) {
@@ -822,15 +884,13 @@ __device__ __forceinline__ void pipe_step(int kt, const char* kcur, const char* 
   if (work) {
     u32x4 pf[S::PS];
     softmax_mask<D, BK, CAUSAL>(s_cur, g, kt * BK, qrow, w_lo, h);
-    // 16-bit products: the exponentials use the running max as it stands
-    // (no tile max on the way); the FP8 form needs the max first
     const float l0 = st.l, lr0 = st.lr;
-    const float msub = F8 ? softmax_max<T, D, BK, true>(s_cur, st, cexp) : st.m;
+    const float msub = st.m;
     float ls;
     if (work_next && KV8) {
       // E4M3 tiles: the compiler schedules the reads and the exponentials
-      tile_qk_plain<T, D, BK, KV8, F8>(s_nxt, kcur, o, st);
-      ls = softmax_exp<T, D, BK, F8>(s_cur, pf, st, msub, cexp);
+      tile_qk_plain<T, D, BK, KV8>(s_nxt, kcur, o, st);
+      ls = softmax_exp<T, D, BK>(s_cur, pf, st, msub, cexp);
     } else if (work_next) {
       tile_qk_plain<T, D, BK>(s_nxt, kcur, o, st);
       ls = softmax_exp<T, D, BK>(s_cur, pf, st, msub, cexp);
@@ -850,11 +910,111 @@ __device__ __forceinline__ void pipe_step(int kt, const char* kcur, const char* 
         }
       }
     } else {
-      ls = softmax_exp<T, D, BK, F8>(s_cur, pf, st, msub, cexp);
+      ls = softmax_exp<T, D, BK>(s_cur, pf, st, msub, cexp);
     }
-    finish_tile<T, D, BK, KV8, F8>(s_cur, pf, st, o, vcur, ls, l0, lr0, cexp);
+    finish_tile<T, D, BK, KV8>(s_cur, pf, st, o, vcur, ls, l0, lr0, cexp);
   }
   staged_barrier();
+}
+
+// The matrix and vector work of a lagged step (FP8 form): O^T +=
+// V_{kt-1}^T P_{kt-1}^T (PREV) and S_{kt+1} = K_{kt+1} Q^T (NEXT) on the
+// matrix cores, while the vector ALU computes tile kt's exponentials, sums and
+// P^T operand. Neither product reads what the exponentials write, so the two
+// units overlap (the compiler interleaves them).
+template <class T, int D, int BK, bool KV8, bool F8, bool PREV, bool NEXT>
+__device__ __forceinline__ void lag_body(const f32x16 (&s_cur)[BK / 32], f32x16 (&s_nxt)[BK / 32],
+                                         u32x4 (&pcur)[BK / 16], const u32x4 (&pprev)[BK / 16], const char* kcur,
+                                         const char* vprev, Acc<D>& st, const Offs<D, BK>& o, float msub,
+                                         float cexp) {
+  float lsum[BK / 8], lrsum[BK / 8];
+  if constexpr (PREV) tile_pv<T, D, BK, KV8, F8>(st, pprev, vprev, o);
+  exp_block<T, D, BK, F8>(s_cur, pcur, 0, lsum, lrsum, msub, cexp);
+  if constexpr (NEXT) tile_qk_plain<T, D, BK, KV8, F8>(s_nxt, kcur, o, st);
+  exp_block<T, D, BK, F8>(s_cur, pcur, 1, lsum, lrsum, msub, cexp);
+  exp_finish<D, BK, F8>(st, lsum, lrsum);
+}
+
+// Waits until at most N tiles of this wavefront's loads (CPT instructions
+// each) are in flight, then synchronises the workgroup (deep ring). The vector
+// memory counter drains in issue order, so the older tiles have landed. The
+// barrier is written without __syncthreads, whose fence would wait for every
+// load; the LDS counter is drained so that no read of a buffer is still in
+// flight when another wavefront's loads may refill it, and the memory clobber
+// keeps the compiler's LDS accesses on their side of the barrier.
+template <int N, int CPT>
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N * CPT) : "memory");
+}
+
+// One key step kt of the lagged pipeline of the FP8 form, over four-deep K
+// and V rings (K four tiles ahead of the scores that use it, V three ahead of
+// its product). With the matrix products twice as fast as in 16 bits, the
+// exponentials would otherwise dominate the step; the lag puts both products
+// of a step beside them. (The 16-bit forms keep the double-buffered step
+// above: holding the previous tile's P^T as well would take the registers
+// their fragment prefetch needs at two wavefronts per SIMD, and a 16-bit ring
+// would leave room for one workgroup per CU only.) On entry the scores of
+// tile kt are in registers (s_cur), and so is the P^T operand of tile kt-1
+// (pprev); LDS holds K_{kt+1} and V_{kt-1}. The step
+//   * starts the loads of K_{kt+4} and V_{kt+2} into the buffers that held
+//     K_kt and V_{kt-2} (read last in step kt-1, which ended with a barrier);
+//     both are issued every step, also past the last tile (an empty
+//     descriptor: nothing is read, the LDS rows receive zeros), so the number
+//     of loads in flight at each wait is fixed;
+//   * masks tile kt where needed and takes its max; if the running max moves,
+//     tile kt-1's product (relative to the old max) is added to O first, then
+//     O and the sums are rescaled;
+//   * runs lag_body: the product of tile kt-1 and the scores of tile kt+1
+//     beside tile kt's exponentials;
+//   * waits for K_{kt+2} and V_kt, the loads issued in step kt-2, leaving the
+//     four later tile loads in flight, and synchronises the workgroup.
+// O receives the tiles' products in key order, each after the rescales of the
+// tiles before it: the arithmetic and its order are those of taking each tile
+// whole (the debug key loop below).
+template <class T, int D, int BK, bool CAUSAL, bool KV8, bool F8, class KStg, class VStg>
+__device__ __forceinline__ void lag_step(int kt, const char* kcur, const char* vprev, char* kload, char* vload,
+                                         f32x16 (&s_cur)[BK / 32], f32x16 (&s_nxt)[BK / 32],
+                                         u32x4 (&pcur)[BK / 16], const u32x4 (&pprev)[BK / 16], const KStg& ks,
+                                         const VStg& vs, Acc<D>& st, const Offs<D, BK>& o, const Geo& g,
+                                         bool wave_live, int w_last, int w_lo, int qrow, int h, float cexp) {
+  static_assert(F8, "the lagged step serves the FP8 form");
+  const int n = g.nkt;
+  const int e[KStg::EPT] = {};  // contiguous tiles: no block table
+  __builtin_amdgcn_sched_barrier(0);
+  ks.load(kt + 4, g.Lk, kload, e);
+  __builtin_amdgcn_sched_barrier(0);
+  vs.load(kt + 2, g.Lk, vload, e);
+  __builtin_amdgcn_sched_barrier(0);
+  // causal: tiles entirely above this wavefront's part of the diagonal are
+  // skipped (monotone in kt: work implies prev and work_next implies work)
+  const bool work = wave_live && (!CAUSAL || kt * BK <= w_last);
+  const bool prev = kt > 0 && wave_live && (!CAUSAL || (kt - 1) * BK <= w_last);
+  const bool work_next = kt + 1 < n && wave_live && (!CAUSAL || (kt + 1) * BK <= w_last);
+  if (work) {
+    softmax_mask<D, BK, CAUSAL>(s_cur, g, kt * BK, qrow, w_lo, h);
+    const float mx = tile_max<D, BK>(s_cur, cexp);
+    bool pv_due = prev;
+    if (__builtin_amdgcn_ballot_w64(max_grows<D, F8>(mx, st))) {
+      if (prev) {
+        tile_pv<T, D, BK, KV8, F8>(st, pprev, vprev, o);
+        pv_due = false;
+      }
+      rescale<D, F8>(st, mx);
+    }
+    const float msub = max_to_subtract(st);
+    if (pv_due && work_next)
+      lag_body<T, D, BK, KV8, F8, true, true>(s_cur, s_nxt, pcur, pprev, kcur, vprev, st, o, msub, cexp);
+    else if (pv_due)
+      lag_body<T, D, BK, KV8, F8, true, false>(s_cur, s_nxt, pcur, pprev, kcur, vprev, st, o, msub, cexp);
+    else if (work_next)
+      lag_body<T, D, BK, KV8, F8, false, true>(s_cur, s_nxt, pcur, pprev, kcur, vprev, st, o, msub, cexp);
+    else
+      lag_body<T, D, BK, KV8, F8, false, false>(s_cur, s_nxt, pcur, pprev, kcur, vprev, st, o, msub, cexp);
+  } else if (prev) {
+    tile_pv<T, D, BK, KV8, F8>(st, pprev, vprev, o);
+  }
+  ring_barrier<4, KStg::CPT>();
 }
 
 // Debug form of the key loop (built with ATTN_SINGLE_BUFFER): one K and one V
@@ -878,10 +1038,15 @@ __device__ __forceinline__ void single_buffer_loop(char* kbuf, char* vbuf, const
       u32x4 pf[S::PS];
       tile_qk_plain<T, D, BK, KV8, F8>(s, kbuf, o, st);
       softmax_mask<D, BK, CAUSAL>(s, g, kt * BK, qrow, w_lo, h);
-      const float l0 = st.l, lr0 = st.lr;
-      const float msub = F8 ? softmax_max<T, D, BK, true>(s, st, cexp) : st.m;
-      const float ls = softmax_exp<T, D, BK, F8>(s, pf, st, msub, cexp);
-      finish_tile<T, D, BK, KV8, F8>(s, pf, st, o, vbuf, ls, l0, lr0, cexp);
+      if constexpr (F8) {
+        const float msub = softmax_max<T, D, BK, true>(s, st, cexp);
+        softmax_exp<T, D, BK, true>(s, pf, st, msub, cexp);
+        tile_pv<T, D, BK, KV8, true>(st, pf, vbuf, o);
+      } else {
+        const float l0 = st.l, lr0 = st.lr;
+        const float ls = softmax_exp<T, D, BK>(s, pf, st, st.m, cexp);
+        finish_tile<T, D, BK, KV8>(s, pf, st, o, vbuf, ls, l0, lr0, cexp);
+      }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __syncthreads();
@@ -889,19 +1054,27 @@ __device__ __forceinline__ void single_buffer_loop(char* kbuf, char* vbuf, const
 }
 
 // ---------------------------------------------------------------------------
-// 4 wavefronts x 32 rows, pipelined key steps over double-buffered K and V.
-template <class T, int D, int BQ, int BK, bool CAUSAL, bool PAGED, bool KV8>
-__global__ __launch_bounds__(BQ * 2, 2) void prefill_kernel(PrefillArgs a) {
+// 4 wavefronts x 32 rows, pipelined key steps over R-deep rings of K and V
+// buffers (R = 2: double buffering; R = 4: the deep ring of the FP8 prefill).
+template <class T, int D, int BQ, int BK, bool CAUSAL, bool PAGED, bool KV8, int R>
+__global__ __launch_bounds__(BQ * 2, (2 * R * Shape<D, BK, KV8>::TILE > 80 * 1024 ? 1 : 2)) void prefill_kernel(
+    PrefillArgs a) {
   // E4M3 tiles: from the paged cache (16-bit products), or, contiguous, the FP8 form
   constexpr bool F8 = KV8 && !PAGED;
   using S = Shape<D, BK, KV8>;
   constexpr int THREADS = (BQ / 32) * 64;
-  // K of tile t lives in kb[t & 1], V of tile t in vb[t & 1]; separate LDS
-  // arrays, so reads of one are never ordered behind the loads into another
+  static_assert(R == 2 || (R == 4 && F8), "ring depth");
+  // K of tile t lives in kb[t % R], V of tile t in vb[t % R]; separate LDS
+  // arrays, so the compiler never orders reads of one behind loads into another
+  constexpr int XTRA = R > 2 ? S::TILE : 16;
   __shared__ __align__(16) char kb0[S::TILE];
   __shared__ __align__(16) char kb1[S::TILE];
   __shared__ __align__(16) char vb0[S::TILE];
   __shared__ __align__(16) char vb1[S::TILE];
+  __shared__ __align__(16) char kb2[XTRA];
+  __shared__ __align__(16) char kb3[XTRA];
+  __shared__ __align__(16) char vb2[XTRA];
+  __shared__ __align__(16) char vb3[XTRA];
 
   // paged form: the sequence's block-table row, read once into LDS
   __shared__ __align__(16) int tbl[PAGED ? kMaxPagedPrefillBlocks : 4];
@@ -948,37 +1121,102 @@ __global__ __launch_bounds__(BQ * 2, 2) void prefill_kernel(PrefillArgs a) {
 #if defined(ATTN_SINGLE_BUFFER)
   (void)kb1;
   (void)vb1;
+  (void)kb2;
+  (void)kb3;
+  (void)vb2;
+  (void)vb3;
+  q_modes<T, D, F8>(st, g, a.qmode, qrow);
   single_buffer_loop<T, D, BK, CAUSAL, KV8, F8>(kb0, vb0, ks, vs, st, o, g, wave_live, w_last, w_lo, qrow, h, cexp);
 #else
-  int ecar[KStg::EPT] = {};  // physical blocks of the tile after the current one
-  if (g.nkt > 0) {
-    int e0[KStg::EPT];
-    ks.entries(0, e0);
-    ks.load(0, g.Lk, kb0, e0);
-    vs.load(0, g.Lk, vb0, e0);
-    if (g.nkt > 1) {
-      ks.entries(1, ecar);
-      ks.load(1, g.Lk, kb1, ecar);
-    }
-  }
-  staged_barrier();
+  const int n = g.nkt;
   f32x16 s0[S::KB], s1[S::KB];
-  if (g.nkt > 0 && wave_live && (!CAUSAL || 0 <= w_last)) tile_qk<T, D, BK, KV8, F8>(s0, kb0, o, st);
-  // The first step loads K_2 into kb0, which every wavefront has just read as
-  // K_0 (each wavefront stages only its own rows of a tile but reads all of
-  // them): no wavefront may start those loads before all have finished
-  // reading. Later steps reuse a buffer only after the barrier ending the step
-  // that read it.
-  if (g.nkt > 2) {
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __syncthreads();
-  }
-  for (int kt = 0; kt < g.nkt; kt += 2) {
-    pipe_step<T, D, BK, CAUSAL, KV8, F8>(kt, kb1, vb0, kb0, vb1, s0, s1, ks, vs, ecar, st, o, g, wave_live, w_last,
-                                         w_lo, qrow, h, cexp);
-    if (kt + 1 < g.nkt)
-      pipe_step<T, D, BK, CAUSAL, KV8, F8>(kt + 1, kb0, vb1, kb1, vb0, s1, s0, ks, vs, ecar, st, o, g, wave_live,
-                                           w_last, w_lo, qrow, h, cexp);
+  if constexpr (!F8) {
+    // 16-bit products: the double-buffered loop (K two tiles ahead, V one)
+    static_assert(R == 2, "16-bit products: double buffering");
+    (void)kb2;
+    (void)kb3;
+    (void)vb2;
+    (void)vb3;
+    int ecar[KStg::EPT] = {};  // physical blocks of the tile after the current one
+    if (n > 0) {
+      int e0[KStg::EPT];
+      ks.entries(0, e0);
+      ks.load(0, g.Lk, kb0, e0);
+      vs.load(0, g.Lk, vb0, e0);
+      if (n > 1) {
+        ks.entries(1, ecar);
+        ks.load(1, g.Lk, kb1, ecar);
+      }
+    }
+    staged_barrier();
+    q_modes<T, D, F8>(st, g, a.qmode, qrow);
+    if (n > 0 && wave_live && (!CAUSAL || 0 <= w_last)) tile_qk<T, D, BK, KV8, F8>(s0, kb0, o, st);
+    // The first step loads K_2 into kb0, which every wavefront has just read as
+    // K_0 (each wavefront stages only its own rows of a tile but reads all of
+    // them): no wavefront may start those loads before all have finished
+    // reading. Later steps reuse a buffer only after the barrier ending the
+    // step that read it.
+    if (n > 2) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+    for (int kt = 0; kt < n; kt += 2) {
+      pipe_step<T, D, BK, CAUSAL, KV8>(kt, kb1, vb0, kb0, vb1, s0, s1, ks, vs, ecar, st, o, g, wave_live, w_last,
+                                       w_lo, qrow, h, cexp);
+      if (kt + 1 < n)
+        pipe_step<T, D, BK, CAUSAL, KV8>(kt + 1, kb0, vb1, kb1, vb0, s1, s0, ks, vs, ecar, st, o, g, wave_live,
+                                         w_last, w_lo, qrow, h, cexp);
+    }
+  } else {
+    // FP8 form: the lagged loop over four-deep rings
+    static_assert(R == 4, "FP8 form: the deep ring");
+    u32x4 p0[S::PS] = {}, p1[S::PS] = {};  // P^T of the even / odd tiles
+    // prologue: K0 K1 K2 V0 K3 V1, in this order (the waits count on it): the
+    // loads steps -4 .. -1 would have issued
+    const int e[KStg::EPT] = {};
+    ks.load(0, g.Lk, kb0, e);
+    __builtin_amdgcn_sched_barrier(0);
+    ks.load(1, g.Lk, kb1, e);
+    __builtin_amdgcn_sched_barrier(0);
+    ks.load(2, g.Lk, kb2, e);
+    __builtin_amdgcn_sched_barrier(0);
+    vs.load(0, g.Lk, vb0, e);
+    __builtin_amdgcn_sched_barrier(0);
+    ks.load(3, g.Lk, kb3, e);
+    __builtin_amdgcn_sched_barrier(0);
+    vs.load(1, g.Lk, vb1, e);
+    __builtin_amdgcn_sched_barrier(0);
+    // K0 has landed when at most K1, K2, V0, K3, V1 are in flight
+    ring_barrier<5, KStg::CPT>();
+    q_modes<T, D, F8>(st, g, a.qmode, qrow);
+    if (n > 0 && wave_live && (!CAUSAL || 0 <= w_last)) tile_qk<T, D, BK, KV8, F8>(s0, kb0, o, st);
+    // K1 has landed when at most K2, V0, K3, V1 are in flight; the barrier also
+    // keeps step 0's load of K4 into kb0 behind every wavefront's reads of K0
+    ring_barrier<4, KStg::CPT>();
+    for (int kt = 0; kt < n; kt += 4) {
+      lag_step<T, D, BK, CAUSAL, KV8, F8>(kt, kb1, vb3, kb0, vb2, s0, s1, p0, p1, ks, vs, st, o, g, wave_live,
+                                          w_last, w_lo, qrow, h, cexp);
+      if (kt + 1 >= n) break;
+      lag_step<T, D, BK, CAUSAL, KV8, F8>(kt + 1, kb2, vb0, kb1, vb3, s1, s0, p1, p0, ks, vs, st, o, g, wave_live,
+                                          w_last, w_lo, qrow, h, cexp);
+      if (kt + 2 >= n) break;
+      lag_step<T, D, BK, CAUSAL, KV8, F8>(kt + 2, kb3, vb1, kb2, vb0, s0, s1, p0, p1, ks, vs, st, o, g, wave_live,
+                                          w_last, w_lo, qrow, h, cexp);
+      if (kt + 3 >= n) break;
+      lag_step<T, D, BK, CAUSAL, KV8, F8>(kt + 3, kb0, vb2, kb3, vb1, s1, s0, p1, p0, ks, vs, st, o, g, wave_live,
+                                          w_last, w_lo, qrow, h, cexp);
+    }
+    // the loads past the last tile are still writing (zeros) into LDS
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // the product of the last tile (its V landed before the last step's barrier)
+    const int last = n - 1;
+    if (n > 0 && wave_live && (!CAUSAL || last * BK <= w_last)) {
+      const char* vlast = last % 4 == 0 ? vb0 : last % 4 == 1 ? vb1 : last % 4 == 2 ? vb2 : vb3;
+      if (last & 1)
+        tile_pv<T, D, BK, KV8, F8>(st, p1, vlast, o);
+      else
+        tile_pv<T, D, BK, KV8, F8>(st, p0, vlast, o);
+    }
   }
 #endif
   epilogue<T, D>(st, g, a.Tq, qrow, h, KV8 ? a.v_scale : 1.f, F8 ? kF8PScaleLog2 : 0.f);
@@ -995,7 +1233,10 @@ static hipError_t launch_D(const PrefillArgs& a, hipStream_t stream) {
   // longest-first order of the chunked prefill's groups (a ranking loop over
   // B * nqt groups per lane, so only for batches of at most 64 sequences)
   x.lpt = (PAGED && a.B <= 64 && (long long)x.nqt * a.B <= 256) ? 1 : 0;
-  hipLaunchKernelGGL((prefill_kernel<T, D, 128, BK, CAUSAL, PAGED, KV8>), dim3((unsigned)blocks), dim3(256), 0,
+  // the FP8 form (contiguous E4M3 tiles) runs the lagged loop over four-deep
+  // rings: 64 KiB of LDS at 8-bit tiles, two workgroups per CU as in 16 bits
+  constexpr int R = (!PAGED && KV8) ? 4 : 2;
+  hipLaunchKernelGGL((prefill_kernel<T, D, 128, BK, CAUSAL, PAGED, KV8, R>), dim3((unsigned)blocks), dim3(256), 0,
                      stream, x);
   return hipGetLastError();
 }
