@@ -121,6 +121,18 @@ def test_fp8_prefill_tq_ne_tk(ta, Tq, Tk):
     _case_check(ta, case, Tq=Tq, Tk=Tk, causal=False, what=f"Tq={Tq} Tk={Tk} non-causal")
 
 
+@pytest.mark.parametrize("T", [64, 128, 192, 256, 320, 513])
+@pytest.mark.parametrize("D", [64, 128])
+def test_fp8_prefill_ring_lengths(ta, T, D):
+    """Key lengths of 1 to 9 tiles of 64: the four-deep K/V rings' prologue (up to 4 K and 2 V tiles issued
+    before the first step, the empty ones past the end), their first reuse (tile 5) and the last step's
+    product after the loop, causal and not."""
+    case = W.PrefillCase("fp8 ring", B=1, Hq=4, Hkv=2, T=T, D=D, dtype="bf16", causal=True, ragged=False,
+                         seed=108 + T + D)
+    _case_check(ta, case, what=f"T={T} D={D} causal")
+    _case_check(ta, case, causal=False, what=f"T={T} D={D} non-causal")
+
+
 @pytest.mark.parametrize("scale", [0.0, -0.09, 0.5])
 def test_fp8_prefill_scale_values(ta, scale):
     case = W.PrefillCase("fp8 scale", B=1, Hq=2, Hkv=2, T=200, D=64, dtype="bf16", causal=True, ragged=False,

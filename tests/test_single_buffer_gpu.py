@@ -128,7 +128,7 @@ def test_chunked(ta, form):
     _both(ta, call, f"chunked {form}")
 
 
-@pytest.mark.parametrize("T,causal", [(200, True), (1000, False), (2048, True)])
+@pytest.mark.parametrize("T,causal", [(64, True), (200, True), (320, False), (1000, False), (2048, True)])
 def test_fp8_prefill(ta, T, causal):
     import torch
     case = W.PrefillCase("sb-fp8", B=1, Hq=8, Hkv=2, T=T, D=128, dtype="bf16", causal=causal, ragged=False,
