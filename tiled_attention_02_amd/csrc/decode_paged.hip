@@ -469,7 +469,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   st.l = 0.f;
   st.lr = 0.f;
 
-#pragma unroll
+  // (not unrolled: the loop has a data-dependent exit, and the buffer of
+  // step p is addressed from p's parity)
   for (int p = 0; p < NS; ++p) {
     if (p >= ns) break;  // wave-uniform
     // step p has landed: with step p + 1's loads issued after it, at most

@@ -277,7 +277,7 @@ __device__ __forceinline__ void q_modes(Acc<D>& st, const Geo& g, int qmode, int
 }
 
 template <class T, int D, bool KV8, bool F8 = false>
-__device__ __forceinline__ void load_q(Acc<D>& st, const Geo& g, int qmode, int qrow, int h, const float* rope,
+__device__ __forceinline__ void load_q(Acc<D>& st, const Geo& g, int qrow, int h, const float* rope,
                                        int max_pos, const uint8_t* q8 = nullptr) {
   const bool live = qrow < g.Lq;
   if constexpr (F8) {
@@ -1084,7 +1084,7 @@ __global__ __launch_bounds__(BQ * 2, (2 * R * Shape<D, BK, KV8>::TILE > 80 * 102
   const int w_lo = g.q_lo + w * 32;
   const int qrow = w_lo + (lane & 31);
   Acc<D> st;
-  load_q<T, D, KV8, F8>(st, g, a.qmode, qrow, h, PAGED ? a.rope : nullptr, a.max_pos,
+  load_q<T, D, KV8, F8>(st, g, qrow, h, PAGED ? a.rope : nullptr, a.max_pos,
                         static_cast<const uint8_t*>(a.q) + (size_t)(g.b * a.Hq + g.hq) * a.Tq * D);
   Offs<D, BK> o;
   make_offs<D, BK, KV8, F8>(o, lane);
