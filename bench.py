@@ -533,8 +533,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "libattn's benchmark runs on one GPU only: multi-GPU runs are not part of "
-                                   "this build (every figure is a single-GPU figure)", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "libattn's benchmark runs on one GPU only: it has no multi-GPU path "
+                                   "(every figure is a single-GPU figure)", "n_gpus": args.gpus}))
         sys.exit(2)
 
     import numpy as np
