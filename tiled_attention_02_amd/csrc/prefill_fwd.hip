@@ -613,7 +613,10 @@ __device__ __forceinline__ void exp_block(const f32x16 (&sacc)[BK / 32], u32x4 (
 #pragma unroll
       for (int e = 0; e < 4; ++e) p[e] = fast_exp2(__builtin_fmaf(sacc[kb][4 * w + e], cexp, kF8PScaleLog2 - msub));
       lsum[4 * kb + w] = (p[0] + p[1]) + (p[2] + p[3]);
-      int r = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+      // the first conversion keeps the other half of its destination: pass
+      // the register's old bits (overwritten by the second) rather than a
+      // zero that would cost a move per word
+      int r = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], (int)pf[kb][w], false);
       r = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], r, true);
       pf[kb][w] = (uint32_t)r;
     }
@@ -1035,7 +1038,7 @@ __device__ __forceinline__ void single_buffer_loop(char* kbuf, char* vbuf, const
     staged_barrier();
     if (wave_live && (!CAUSAL || kt * BK <= w_last)) {
       f32x16 s[S::KB];
-      u32x4 pf[S::PS];
+      u32x4 pf[S::PS] = {};
       tile_qk_plain<T, D, BK, KV8, F8>(s, kbuf, o, st);
       softmax_mask<D, BK, CAUSAL>(s, g, kt * BK, qrow, w_lo, h);
       if constexpr (F8) {
@@ -1079,7 +1082,13 @@ __global__ __launch_bounds__(BQ * 2, (2 * R * Shape<D, BK, KV8>::TILE > 80 * 102
   // paged form: the sequence's block-table row, read once into LDS
   __shared__ __align__(16) int tbl[PAGED ? kMaxPagedPrefillBlocks : 4];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5;
+  // w (and so w_lo, w_last, wave_live) is the same in every lane of a
+  // wavefront; readfirstlane lets the compiler see that, so the 16-bit
+  // forms' per-tile work / mask conditions become scalar branches instead of
+  // exec masks. (The FP8 form's lagged step keeps the vector form: with
+  // scalar branches the compiler's code for its four step variants spills.)
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
+  const int w = F8 ? tid >> 6 : __builtin_amdgcn_readfirstlane(tid >> 6);
   const Geo g = make_geo<D, BQ, BK, CAUSAL, PAGED>(a);
   const int w_lo = g.q_lo + w * 32;
   const int qrow = w_lo + (lane & 31);
