@@ -104,6 +104,37 @@ def test_large_grid(ta, D, dtype):
     _both(ta, lambda: ta.attn_fwd(q, k, v, scale=case.scale, causal=True), f"B=2 Hq=32 T=1100 D={D} causal")
 
 
+# Grids of several workgroups per CU (workgroups that start in later rounds, reusing the CU's LDS):
+# key tile counts of one to ten, ragged batches and Tq != Tk.
+@pytest.mark.parametrize("T", [64, 200, 256, 320, 577])
+@pytest.mark.parametrize("D,dtype,causal", [(128, "bf16", True), (64, "fp16", False), (128, "fp16", False),
+                                            (64, "bf16", True)])
+def test_many_workgroups(ta, T, D, dtype, causal):
+    B, Hq = (8, 64) if T <= 256 else (4, 64)
+    assert -(-T // 128) * Hq * B >= 512
+    case = W.PrefillCase("sb-many", B=B, Hq=Hq, Hkv=8, T=T, D=D, dtype=dtype, causal=causal, ragged=False,
+                         seed=520 + T)
+    x = W.prefill_inputs(case)
+    q, k, v = (_dev(x[n], dtype) for n in ("q", "k", "v"))
+    _both(ta, lambda: ta.attn_fwd(q, k, v, scale=case.scale, causal=causal),
+          f"many workgroups B={B} Hq={Hq} T={T} D={D} {dtype} causal={causal}")
+
+
+def test_many_workgroups_ragged_and_tq_ne_tk(ta):
+    import torch
+    case = W.PrefillCase("sb-many-ragged", B=8, Hq=16, Hkv=4, T=600, D=128, dtype="bf16", causal=True, ragged=True,
+                         seed=530)
+    x = W.prefill_inputs(case, nan_padding=True)
+    q, k, v = (_dev(x[n], "bf16") for n in ("q", "k", "v"))
+    sl = torch.from_numpy(x["seq_lens"]).cuda()
+    _both(ta, lambda: ta.attn_fwd(q, k, v, scale=case.scale, causal=True, seq_lens=sl),
+          "many workgroups, ragged causal")
+    c2 = W.PrefillCase("sb-many-tq", B=1, Hq=64, Hkv=16, T=0, D=64, dtype="fp16", causal=True, ragged=False, seed=531)
+    x = W.prefill_inputs(c2, Tq=1000, Tk=1300)
+    q, k, v = (_dev(x[n], "fp16") for n in ("q", "k", "v"))
+    _both(ta, lambda: ta.attn_fwd(q, k, v, scale=c2.scale, causal=True), "many workgroups, Tq=1000 Tk=1300 causal")
+
+
 @pytest.mark.parametrize("form", ["16-bit", "rotary", "E4M3"])
 def test_chunked(ta, form):
     import torch

@@ -133,6 +133,15 @@ __device__ __forceinline__ float half_swap_max(float x) {
                                             __builtin_bit_cast(uint32_t, x), false, false);
   return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
 }
+// max(x, x of lane l ^ 16) through v_permlane16_swap (rows of 16 lanes: the
+// odd rows of the first operand trade places with the even rows of the
+// second, so swap(x, x) gives each lane pair's even-row value in r[0] and its
+// odd-row value in r[1]); no LDS round trip, unlike a bpermute.
+__device__ __forceinline__ float row_swap_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x),
+                                            __builtin_bit_cast(uint32_t, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
 __device__ __forceinline__ float half_swap_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
                                             __builtin_bit_cast(uint32_t, x), false, false);

@@ -260,7 +260,7 @@ __device__ __forceinline__ void step_compute(WaveState<D>& st, char* buf, const 
 #pragma unroll
   for (int j = 0; j < NB; ++j)
     mx = fmaxf(mx, fmaxf(fmaxf(sacc[j][0], sacc[j][1]), fmaxf(sacc[j][2], sacc[j][3])));
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = row_swap_max(mx);
   mx = half_swap_max(mx) * cexp;
   const bool grow = mx > st.m + kDecodeLazy;
   if (__builtin_amdgcn_ballot_w64(grow)) {
@@ -333,9 +333,13 @@ __device__ __forceinline__ void step_compute(WaveState<D>& st, char* buf, const 
 // other, and step p + 2's loads start as soon as step p's reads have returned;
 // with one (E4M3 cache), step p + 1's loads start once step p's reads have
 // returned. Ten wavefronts per CU fit, so every workgroup of a typical batch
-// starts at once.
+// starts at once. Ten per CU means three on some SIMDs: the launch bound asks
+// for at least three wavefronts per SIMD, which caps a wavefront at 170
+// registers. (With the bare bound the compiler may use all 512 of one
+// wavefront, and did: the matrix instructions then accumulated in AGPRs and
+// every step copied O between them and the VGPRs the rescale works in.)
 template <class T, int D, bool KV8>
-__global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64, 3) void decode_split_kernel(DecodeArgs a) {
   using L = StepLds<D, KV8>;
   constexpr int KS = D / 32;
   constexpr int VC = D / 16;

@@ -776,10 +776,12 @@ struct Stager {
       // LDS table), gets none: nothing is read and the LDS rows receive zeros)
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
-        int phys = e[i * JW];
+        // e[i * JW + wblk], written as a mask-and-or over the JW candidates:
+        // as a select chain the compiler turns it into an indexed load from a
+        // stack copy of e (a scratch store and load per tile)
+        int phys = 0;
 #pragma unroll
-        for (int j = 1; j < JW; ++j)
-          if (wblk == j) phys = e[i * JW + j];
+        for (int j = 0; j < JW; ++j) phys |= e[i * JW + j] & -(int)(wblk == j);
         const int lb = k0 / 16 + i * JW + wblk;
         const int rows = __builtin_amdgcn_readfirstlane(phys < 0 ? 0 : min(max(Lk - 16 * lb, 0), 16));
         const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
