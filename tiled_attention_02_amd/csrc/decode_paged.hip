@@ -333,13 +333,16 @@ __device__ __forceinline__ void step_compute(WaveState<D>& st, char* buf, const 
 // other, and step p + 2's loads start as soon as step p's reads have returned;
 // with one (E4M3 cache), step p + 1's loads start once step p's reads have
 // returned. Ten wavefronts per CU fit, so every workgroup of a typical batch
-// starts at once. Ten per CU means three on some SIMDs: the launch bound asks
-// for at least three wavefronts per SIMD, which caps a wavefront at 170
-// registers. (With the bare bound the compiler may use all 512 of one
-// wavefront, and did: the matrix instructions then accumulated in AGPRs and
-// every step copied O between them and the VGPRs the rescale works in.)
+// starts at once. Ten per CU means three on some SIMDs: for the 16-bit cache
+// the launch bound asks for at least three wavefronts per SIMD, which caps a
+// wavefront at 170 registers. (With the bare bound the compiler may use all
+// 512 of one wavefront, and does: the matrix instructions then accumulate in
+// AGPRs and every step copies O between them and the VGPRs the rescale works
+// in.) The E4M3 form keeps the bare bound and those copies: capped, its
+// four-block steps measured 2-3 % slower per call (25.6-25.9 against
+// 26.2-26.7 µs on the Qwen-shaped batch, three boxes).
 template <class T, int D, bool KV8>
-__global__ __launch_bounds__(64, 3) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64, KV8 ? 1 : 3) void decode_split_kernel(DecodeArgs a) {
   using L = StepLds<D, KV8>;
   constexpr int KS = D / 32;
   constexpr int VC = D / 16;
