@@ -832,16 +832,21 @@ __device__ __forceinline__ void staged_barrier() {
 // moved first, so the tile's exponentials are redone after the lazy rescale
 // (below that sum every p <= 2^15 stays inside fp16's range and the P operand
 // keeps the relative precision of any other p); then O^T += V^T P^T.
-template <class T, int D, int BK, bool KV8>
-__device__ __forceinline__ void finish_tile(const f32x16 (&s_cur)[BK / 32], u32x4 (&pf)[BK / 16], Acc<D>& st,
-                                            const Offs<D, BK>& o, const char* vcur, float ls, float l0, float lr0,
-                                            float cexp) {
+template <class T, int D, int BK>
+__device__ __forceinline__ void redo_tile(const f32x16 (&s_cur)[BK / 32], u32x4 (&pf)[BK / 16], Acc<D>& st, float ls,
+                                          float l0, float lr0, float cexp) {
   if (__builtin_amdgcn_ballot_w64(!(ls <= kOptimisticSum))) {
     st.l = l0;
     st.lr = lr0;
     const float m2 = softmax_max<T, D, BK>(s_cur, st, cexp);
     softmax_exp<T, D, BK>(s_cur, pf, st, m2, cexp);
   }
+}
+template <class T, int D, int BK, bool KV8>
+__device__ __forceinline__ void finish_tile(const f32x16 (&s_cur)[BK / 32], u32x4 (&pf)[BK / 16], Acc<D>& st,
+                                            const Offs<D, BK>& o, const char* vcur, float ls, float l0, float lr0,
+                                            float cexp) {
+  redo_tile<T, D, BK>(s_cur, pf, st, ls, l0, lr0, cexp);
   __builtin_amdgcn_s_setprio(2);
   tile_pv<T, D, BK, KV8>(st, pf, vcur, o);
   __builtin_amdgcn_s_setprio(0);
@@ -852,11 +857,13 @@ __device__ __forceinline__ void finish_tile(const f32x16 (&s_cur)[BK / 32], u32x
 // tile kt are in LDS. The step starts the loads of K_{kt+2} and V_{kt+1} into
 // the buffers read one step earlier, then
 //   * masks tile kt where needed (VALU);
-//   * computes S of tile kt+1 (MFMA) and the exponentials, sums and packing
-//     of tile kt (VALU) under the running max as it stands (no tile max on
-//     the way); neither depends on the other;
+//   * computes the exponentials, sums and packing of tile kt (VALU) under
+//     the running max as it stands (no tile max on the way), and S of tile
+//     kt+1 (MFMA), which does not depend on them;
 //   * accumulates O^T += V^T P^T for tile kt (MFMA);
-// and ends with the wait for its loads and a barrier.
+// and ends with the wait for its loads and a barrier. The order of the three
+// differs between the contiguous and the paged forms (see below); the
+// arithmetic of each row does not.
 template <class T, int D, int BK, bool CAUSAL, bool KV8, class KStg, class VStg>
 __device__ __forceinline__ void pipe_step(int kt, const char* kcur, const char* vcur, char* kload, char* vload,
                                           f32x16 (&s_cur)[BK / 32], f32x16 (&s_nxt)[BK / 32],
@@ -891,6 +898,22 @@ __device__ __forceinline__ void pipe_step(int kt, const char* kcur, const char* 
     softmax_mask<D, BK, CAUSAL>(s_cur, g, kt * BK, qrow, w_lo, h);
     const float l0 = st.l, lr0 = st.lr;
     const float msub = st.m;
+    if constexpr (!KStg::kPaged) {
+      // contiguous tiles: this tile's exponentials first, then its product
+      // and the next tile's scores back to back at raised priority, so a
+      // step is one vector phase and one matrix phase; the two wavefronts of
+      // a SIMD overlap one's vector phase with the other's matrix phase
+      // (1-2 % faster than the next tile's scores first, which was itself
+      // 1.4-3.8 % faster than an explicit MFMA/VALU interleave)
+      const float ls = softmax_exp<T, D, BK>(s_cur, pf, st, msub, cexp);
+      redo_tile<T, D, BK>(s_cur, pf, st, ls, l0, lr0, cexp);
+      __builtin_amdgcn_s_setprio(2);
+      tile_pv<T, D, BK, KV8>(st, pf, vcur, o);
+      if (work_next) tile_qk_plain<T, D, BK, KV8>(s_nxt, kcur, o, st);
+      __builtin_amdgcn_s_setprio(0);
+      staged_barrier();
+      return;
+    }
     float ls;
     if (work_next && KStg::kPaged && !KV8) {
       // paged 16-bit tiles: each MFMA of the next tile's S is followed by a
@@ -913,10 +936,8 @@ __device__ __forceinline__ void pipe_step(int kt, const char* kcur, const char* 
         }
       }
     } else if (work_next) {
-      // contiguous and E4M3 tiles: the compiler schedules the next tile's
-      // products and this tile's exponentials (it issues the products first);
-      // the other wavefront of the SIMD overlaps them with its own phases,
-      // and the explicit interleave above measured 1.4-3.8 % slower here
+      // paged E4M3 tiles: the compiler schedules the next tile's products and
+      // this tile's exponentials
       tile_qk_plain<T, D, BK, KV8>(s_nxt, kcur, o, st);
       ls = softmax_exp<T, D, BK>(s_cur, pf, st, msub, cexp);
     } else {
