@@ -715,7 +715,6 @@ struct Stager {
   static_assert(CPT >= 1 && BK % (RPI * NW) == 0, "staging shape");
   static_assert(16 % RPI == 0, "an instruction's rows lie in one cache block");
   static constexpr int EPT = BK / 16;         // cache blocks per tile (paged form)
-  static constexpr bool kPaged = PAGED;
   static constexpr int JW = NW * RPI / 16;      // paged: distinct wave-dependent block choices per instruction
   int voff[CPT];  // per-lane byte offset of the fetched chunk (within the tile, or within the cache block)
   int loff[CPT];  // wave-uniform LDS byte offset of the instruction within the tile
@@ -861,9 +860,7 @@ __device__ __forceinline__ void finish_tile(const f32x16 (&s_cur)[BK / 32], u32x
 //     the running max as it stands (no tile max on the way), and S of tile
 //     kt+1 (MFMA), which does not depend on them;
 //   * accumulates O^T += V^T P^T for tile kt (MFMA);
-// and ends with the wait for its loads and a barrier. The order of the three
-// differs between the contiguous and the paged forms (see below); the
-// arithmetic of each row does not.
+// and ends with the wait for its loads and a barrier.
 template <class T, int D, int BK, bool CAUSAL, bool KV8, class KStg, class VStg>
 __device__ __forceinline__ void pipe_step(int kt, const char* kcur, const char* vcur, char* kload, char* vload,
                                           f32x16 (&s_cur)[BK / 32], f32x16 (&s_nxt)[BK / 32],
@@ -898,52 +895,17 @@ __device__ __forceinline__ void pipe_step(int kt, const char* kcur, const char* 
     softmax_mask<D, BK, CAUSAL>(s_cur, g, kt * BK, qrow, w_lo, h);
     const float l0 = st.l, lr0 = st.lr;
     const float msub = st.m;
-    if constexpr (!KStg::kPaged) {
-      // contiguous tiles: this tile's exponentials first, then its product
-      // and the next tile's scores back to back at raised priority, so a
-      // step is one vector phase and one matrix phase; the two wavefronts of
-      // a SIMD overlap one's vector phase with the other's matrix phase
-      // (1-2 % faster than the next tile's scores first, which was itself
-      // 1.4-3.8 % faster than an explicit MFMA/VALU interleave)
-      const float ls = softmax_exp<T, D, BK>(s_cur, pf, st, msub, cexp);
-      redo_tile<T, D, BK>(s_cur, pf, st, ls, l0, lr0, cexp);
-      __builtin_amdgcn_s_setprio(2);
-      tile_pv<T, D, BK, KV8>(st, pf, vcur, o);
-      if (work_next) tile_qk_plain<T, D, BK, KV8>(s_nxt, kcur, o, st);
-      __builtin_amdgcn_s_setprio(0);
-      staged_barrier();
-      return;
-    }
-    float ls;
-    if (work_next && KStg::kPaged && !KV8) {
-      // paged 16-bit tiles: each MFMA of the next tile's S is followed by a
-      // share of the current tile's vector work, K fragments kQkDepth steps
-      // ahead (3.4 % faster than the compiler's schedule on the chunked
-      // prefill)
-      tile_qk_plain<T, D, BK>(s_nxt, kcur, o, st);
-      ls = softmax_exp<T, D, BK>(s_cur, pf, st, msub, cexp);
-      constexpr int NMF = S::KS * S::KB;
-      constexpr int NVALU = S::KB * 16 * 3 + S::KB * 16;  // fma, exp, add; cvt and dot2 per pair
-      constexpr int PER = (NVALU + NMF - 1) / NMF;
-      __builtin_amdgcn_sched_group_barrier(0x100, kQkDepth * S::KB, 0);
-#pragma unroll
-      for (int s2 = 0; s2 < S::KS; ++s2) {
-        if (s2 + kQkDepth < S::KS) __builtin_amdgcn_sched_group_barrier(0x100, S::KB, 0);
-#pragma unroll
-        for (int kb = 0; kb < S::KB; ++kb) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, PER, 0);
-        }
-      }
-    } else if (work_next) {
-      // paged E4M3 tiles: the compiler schedules the next tile's products and
-      // this tile's exponentials
-      tile_qk_plain<T, D, BK, KV8>(s_nxt, kcur, o, st);
-      ls = softmax_exp<T, D, BK>(s_cur, pf, st, msub, cexp);
-    } else {
-      ls = softmax_exp<T, D, BK>(s_cur, pf, st, msub, cexp);
-    }
-    finish_tile<T, D, BK, KV8>(s_cur, pf, st, o, vcur, ls, l0, lr0, cexp);
+    // this tile's exponentials first, then its product and the next tile's
+    // scores back to back at raised priority: one vector phase and one matrix
+    // phase per step, which the two wavefronts of a SIMD overlap with each
+    // other (faster than the next tile's scores first, and than an explicit
+    // MFMA/VALU interleave of the two)
+    const float ls = softmax_exp<T, D, BK>(s_cur, pf, st, msub, cexp);
+    redo_tile<T, D, BK>(s_cur, pf, st, ls, l0, lr0, cexp);
+    __builtin_amdgcn_s_setprio(2);
+    tile_pv<T, D, BK, KV8>(st, pf, vcur, o);
+    if (work_next) tile_qk_plain<T, D, BK, KV8>(s_nxt, kcur, o, st);
+    __builtin_amdgcn_s_setprio(0);
   }
   staged_barrier();
 }
