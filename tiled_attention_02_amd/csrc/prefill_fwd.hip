@@ -47,8 +47,10 @@
 // the other's softmax), K/V tiles double-buffered in LDS with one barrier per
 // tile: tile j+1 travels HBM -> LDS directly (buffer loads that write LDS)
 // while tile j is consumed. LDS operand reads are issued ahead of the MFMAs
-// that consume them (register double buffering). Within a step, the scores of
-// tile j+1 are computed beside tile j's exponentials.
+// that consume them (register double buffering). A step is one vector phase
+// (tile j's exponentials) and one matrix phase (tile j's product, then tile
+// j+1's scores); the two wavefronts of a SIMD overlap one's vector phase
+// with the other's matrix phase.
 //
 // The FP8 form lags the P.V product by one tile: step j computes the scores
 // of tile j+1 and the product of tile j-1 beside tile j's exponentials, over
