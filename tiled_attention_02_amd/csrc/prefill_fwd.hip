@@ -1149,18 +1149,24 @@ __global__ __launch_bounds__(BQ * 2, (2 * R * Shape<D, BK, KV8>::TILE > 80 * 102
         ks.load(1, g.Lk, kb1, ecar);
       }
     }
-    staged_barrier();
+    // K_0 has landed when at most the loads issued after it (V_0's, and K_1's
+    // when there is a second tile) are in flight: the vector memory counter
+    // drains in issue order, so the scores of tile 0 start while V_0 and K_1
+    // still travel
+    if (n > 1)
+      ring_barrier<2, KStg::CPT>();
+    else if (n == 1)
+      ring_barrier<1, KStg::CPT>();
+    else
+      ring_barrier<0, KStg::CPT>();
     q_modes<T, D, F8>(st, g, a.qmode, qrow);
     if (n > 0 && wave_live && (!CAUSAL || 0 <= w_last)) tile_qk<T, D, BK, KV8, F8>(s0, kb0, o, st);
-    // The first step loads K_2 into kb0, which every wavefront has just read as
-    // K_0 (each wavefront stages only its own rows of a tile but reads all of
-    // them): no wavefront may start those loads before all have finished
-    // reading. Later steps reuse a buffer only after the barrier ending the
-    // step that read it.
-    if (n > 2) {
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      __syncthreads();
-    }
+    // Step 0 reads V_0 and K_1, which must have landed, and loads K_2 into
+    // kb0, which every wavefront has just read as K_0 (each wavefront stages
+    // only its own rows of a tile but reads all of them): no wavefront may
+    // start those loads before all have finished reading. Later steps reuse a
+    // buffer only after the barrier ending the step that read it.
+    if (n > 0) staged_barrier();
     for (int kt = 0; kt < n; kt += 2) {
       pipe_step<T, D, BK, CAUSAL, KV8>(kt, kb1, vb0, kb0, vb1, s0, s1, ks, vs, ecar, st, o, g, wave_live, w_last,
                                        w_lo, qrow, h, cexp);
