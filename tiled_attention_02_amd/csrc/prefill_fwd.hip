@@ -853,15 +853,38 @@ __device__ __forceinline__ void finish_tile(const f32x16 (&s_cur)[BK / 32], u32x
   __builtin_amdgcn_s_setprio(0);
 }
 
+// Issue order of the matrix phase of a 16-bit step (P.V of this tile, then
+// S of the next): the first 6 LDS reads (V^T fragments), then each MFMA
+// followed by the next 2 reads during P.V and the next one during S. Each
+// MFMA's operand was then read several MFMAs earlier. Left to itself the
+// compiler reads each pair of K fragments just before its two MFMAs, which
+// then wait for the full LDS latency; this order measured 3-4 % faster over
+// the whole kernel (first groups of 4 to 10 reads alike, 12 or 16 slower).
+template <int D, int BK>
+__device__ __forceinline__ void matrix_phase_order() {
+  constexpr int NPV = (D / 32) * (BK / 16), NQK = (D / 16) * (BK / 32);
+  __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // LDS reads
+#pragma unroll
+  for (int i = 0; i < NPV; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < NQK; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+}
+
 // One key step kt of the double-buffered loop (16-bit products). On entry
 // the scores of tile kt (s_cur) are in registers, K of tile kt+1 and V of
 // tile kt are in LDS. The step starts the loads of K_{kt+2} and V_{kt+1} into
 // the buffers read one step earlier, then
 //   * masks tile kt where needed (VALU);
 //   * computes the exponentials, sums and packing of tile kt (VALU) under
-//     the running max as it stands (no tile max on the way), and S of tile
-//     kt+1 (MFMA), which does not depend on them;
-//   * accumulates O^T += V^T P^T for tile kt (MFMA);
+//     the running max as it stands (no tile max on the way);
+//   * accumulates O^T += V^T P^T for tile kt and computes S of tile kt+1
+//     (MFMA, at raised priority);
 // and ends with the wait for its loads and a barrier.
 template <class T, int D, int BK, bool CAUSAL, bool KV8, class KStg, class VStg>
 __device__ __forceinline__ void pipe_step(int kt, const char* kcur, const char* vcur, char* kload, char* vload,
@@ -889,9 +912,8 @@ __device__ __forceinline__ void pipe_step(int kt, const char* kcur, const char* 
     vs.load(kt + 1, g.Lk, vload, ecar);
   }
   // causal: tiles entirely above this wavefront's part of the diagonal are
-  // skipped (monotone in kt, so work_next implies work)
+  // skipped (monotone in kt, so the next tile's work implies this one's)
   const bool work = wave_live && (!CAUSAL || kt * BK <= w_last);
-  const bool work_next = kt + 1 < g.nkt && wave_live && (!CAUSAL || (kt + 1) * BK <= w_last);
   if (work) {
     u32x4 pf[S::PS];
     softmax_mask<D, BK, CAUSAL>(s_cur, g, kt * BK, qrow, w_lo, h);
@@ -906,7 +928,18 @@ __device__ __forceinline__ void pipe_step(int kt, const char* kcur, const char* 
     redo_tile<T, D, BK>(s_cur, pf, st, ls, l0, lr0, cexp);
     __builtin_amdgcn_s_setprio(2);
     tile_pv<T, D, BK, KV8>(st, pf, vcur, o);
-    if (work_next) tile_qk_plain<T, D, BK, KV8>(s_nxt, kcur, o, st);
+    if constexpr (KV8) {
+      const bool work_next = kt + 1 < g.nkt && (!CAUSAL || (kt + 1) * BK <= w_last);
+      if (work_next) tile_qk_plain<T, D, BK, KV8>(s_nxt, kcur, o, st);
+    } else {
+      // The next tile's scores are computed with every tile's product, also
+      // past the last tile or above this wavefront's diagonal, where they are
+      // never read (the buffer then holds an older tile or unwritten LDS: no
+      // load is in flight into it). With no branch between them, both products
+      // are one block of code, and the K reads can go out under P.V.
+      tile_qk_plain<T, D, BK, KV8>(s_nxt, kcur, o, st);
+      matrix_phase_order<D, BK>();
+    }
     __builtin_amdgcn_s_setprio(0);
   }
   staged_barrier();
