@@ -853,24 +853,24 @@ __device__ __forceinline__ void finish_tile(const f32x16 (&s_cur)[BK / 32], u32x
   __builtin_amdgcn_s_setprio(0);
 }
 
-// Issue order of the matrix phase of a 16-bit step (P.V of this tile, then
-// S of the next): the first 6 LDS reads (V^T fragments), then each MFMA
-// followed by the next 2 reads during P.V and the next one during S. Each
-// MFMA's operand was then read several MFMAs earlier. Left to itself the
-// compiler reads each pair of K fragments just before its two MFMAs, which
-// then wait for the full LDS latency; this order measured 3-4 % faster over
-// the whole kernel (first groups of 4 to 10 reads alike, 12 or 16 slower).
+// Issue order of the matrix phase of a 16-bit step (S of the next tile, then
+// P.V of this one): the first 6 LDS reads (K fragments), then each MFMA
+// followed by the next 2 reads during S and the next one during P.V (the
+// reads run K, then V^T). Each MFMA's operand was then read several MFMAs
+// earlier. Left to itself the compiler reads each pair of K fragments just
+// before its two MFMAs, which then wait for the full LDS latency; ordered,
+// the kernel measured 3-4 % faster.
 template <int D, int BK>
 __device__ __forceinline__ void matrix_phase_order() {
   constexpr int NPV = (D / 32) * (BK / 16), NQK = (D / 16) * (BK / 32);
   __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // LDS reads
 #pragma unroll
-  for (int i = 0; i < NPV; ++i) {
+  for (int i = 0; i < NQK; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
   }
 #pragma unroll
-  for (int i = 0; i < NQK; ++i) {
+  for (int i = 0; i < NPV; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
@@ -883,7 +883,7 @@ __device__ __forceinline__ void matrix_phase_order() {
 //   * masks tile kt where needed (VALU);
 //   * computes the exponentials, sums and packing of tile kt (VALU) under
 //     the running max as it stands (no tile max on the way);
-//   * accumulates O^T += V^T P^T for tile kt and computes S of tile kt+1
+//   * computes S of tile kt+1 and accumulates O^T += V^T P^T for tile kt
 //     (MFMA, at raised priority);
 // and ends with the wait for its loads and a barrier.
 template <class T, int D, int BK, bool CAUSAL, bool KV8, class KStg, class VStg>
@@ -927,8 +927,8 @@ __device__ __forceinline__ void pipe_step(int kt, const char* kcur, const char* 
     const float ls = softmax_exp<T, D, BK>(s_cur, pf, st, msub, cexp);
     redo_tile<T, D, BK>(s_cur, pf, st, ls, l0, lr0, cexp);
     __builtin_amdgcn_s_setprio(2);
-    tile_pv<T, D, BK, KV8>(st, pf, vcur, o);
     if constexpr (KV8) {
+      tile_pv<T, D, BK, KV8>(st, pf, vcur, o);
       const bool work_next = kt + 1 < g.nkt && (!CAUSAL || (kt + 1) * BK <= w_last);
       if (work_next) tile_qk_plain<T, D, BK, KV8>(s_nxt, kcur, o, st);
     } else {
@@ -936,8 +936,12 @@ __device__ __forceinline__ void pipe_step(int kt, const char* kcur, const char* 
       // past the last tile or above this wavefront's diagonal, where they are
       // never read (the buffer then holds an older tile or unwritten LDS: no
       // load is in flight into it). With no branch between them, both products
-      // are one block of code, and the K reads can go out under P.V.
+      // are one block of code whose LDS reads can be issued ahead. The scores
+      // go first: the next step's exponentials wait for them, while P.V's
+      // results are not read again until the next P.V, so its last MFMAs
+      // overlap the wavefront's barrier and next vector phase.
       tile_qk_plain<T, D, BK, KV8>(s_nxt, kcur, o, st);
+      tile_pv<T, D, BK, KV8>(st, pf, vcur, o);
       matrix_phase_order<D, BK>();
     }
     __builtin_amdgcn_s_setprio(0);
