@@ -919,11 +919,11 @@ __device__ __forceinline__ void pipe_step(int kt, const char* kcur, const char* 
     softmax_mask<D, BK, CAUSAL>(s_cur, g, kt * BK, qrow, w_lo, h);
     const float l0 = st.l, lr0 = st.lr;
     const float msub = st.m;
-    // this tile's exponentials first, then its product and the next tile's
-    // scores back to back at raised priority: one vector phase and one matrix
-    // phase per step, which the two wavefronts of a SIMD overlap with each
-    // other (faster than the next tile's scores first, and than an explicit
-    // MFMA/VALU interleave of the two)
+    // this tile's exponentials first, then the next tile's scores and this
+    // tile's product back to back at raised priority: one vector phase and
+    // one matrix phase per step, which the two wavefronts of a SIMD overlap
+    // with each other (faster than the next tile's scores before the
+    // exponentials, and than an explicit MFMA/VALU interleave of the two)
     const float ls = softmax_exp<T, D, BK>(s_cur, pf, st, msub, cexp);
     redo_tile<T, D, BK>(s_cur, pf, st, ls, l0, lr0, cexp);
     __builtin_amdgcn_s_setprio(2);
