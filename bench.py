@@ -42,6 +42,7 @@ prefill workload on this host.
 import argparse
 import hashlib
 import json
+import re
 import math
 import os
 import sys
@@ -71,12 +72,26 @@ APPEND_LAYERS = 8
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
 
-def source_sha(kind):
+_COMMENTS = re.compile(r"//[^\n]*|/\*.*?\*/", re.S)
+
+
+def code_sha(texts):
+    """Hash of C++/HIP source texts with comments, trailing blanks and empty lines removed."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES[kind]:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+    for text in texts:
+        code = "\n".join(ln.rstrip() for ln in _COMMENTS.sub("", text).splitlines() if ln.strip())
+        h.update(code.encode())
     return h.hexdigest()[:16]
+
+
+def source_sha(kind):
+    """The code (not the comments) of the kernel sources the committed traffic counters are tied to: a change
+    of code voids the counters, a change of comments does not."""
+    texts = []
+    for rel in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, rel)) as f:
+            texts.append(f.read())
+    return code_sha(texts)
 
 
 def measured_traffic(kind):

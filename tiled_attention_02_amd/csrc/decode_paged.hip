@@ -13,13 +13,15 @@
 // key axis; the merge is the softmax-statistics update of blockwise attention.
 //
 // Decomposition: one wavefront per (split of 256 tokens = 16 cache blocks,
-// kv head, sequence). It streams its blocks two at a time (a step of 32
-// tokens) through one 16 KiB LDS buffer, and serves all G = Hq/Hkv
-// query heads of the kv head from one read of each block:
+// kv head, sequence). It streams its blocks through 16 KiB of LDS (16-bit
+// cache: one block per step, in two 8 KiB step buffers; E4M3 cache: four
+// blocks per step in one buffer) and serves all G = Hq/Hkv query heads of
+// the kv head from one read of each block:
 //   S^T = K Q^T       v_mfma_f32_16x16x32: rows = 16 tokens of a block,
 //                     columns = query heads (G <= 16, the rest zero).
-//   O  += P V         v_mfma_f32_16x16x32: rows = heads, columns = 16 of D,
-//                     contraction = 32 tokens (two blocks) per product.
+//   O  += P V         rows = heads, columns = 16 of D; 16-bit cache:
+//                     v_mfma_f32_16x16x16 over one block's 16 tokens; E4M3
+//                     cache: v_mfma_f32_16x16x32 over a block pair's 32.
 // Every (block, kv head) of K and V is 16*D contiguous elements, read once,
 // straight into LDS; the transposed scores of two blocks are already the
 // A operand (P) of the second product, and V's operand comes from LDS through
