@@ -717,10 +717,12 @@ struct Stager {
   static_assert(CPT >= 1 && BK % (RPI * NW) == 0, "staging shape");
   static_assert(16 % RPI == 0, "an instruction's rows lie in one cache block");
   static constexpr int EPT = BK / 16;         // cache blocks per tile (paged form)
-  static constexpr int JW = NW * RPI / 16;      // paged: distinct wave-dependent block choices per instruction
+  // paged form: wavefront w stages cache block w of each tile (its 16 rows in
+  // CPT instructions), so one descriptor covers all its loads of the tile
+  static_assert(!PAGED || EPT == NW, "paged staging: one cache block per wavefront");
   int voff[CPT];  // per-lane byte offset of the fetched chunk (within the tile, or within the cache block)
   int loff[CPT];  // wave-uniform LDS byte offset of the instruction within the tile
-  int wblk;       // paged: the wave's share of an instruction's block index, in [0, JW)
+  int wblk;       // paged: the wave's cache block within a tile
   const char* base;
   size_t bstride;   // paged: bytes per physical block (all kv heads)
   const int* tbl;   // paged: the sequence's block-table row, in LDS
@@ -731,14 +733,15 @@ struct Stager {
     const int l = tid & 63;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int n = i * NW + w;
-      const int row = n * RPI + l / S::C8;
+      // contiguous: instruction i of wave w covers rows (i*NW + w)*RPI ..;
+      // paged: rows 16w + i*RPI .. (block w of the tile)
+      const int r0 = PAGED ? 16 * w + i * RPI : (i * NW + w) * RPI;
+      const int row = r0 + l / S::C8;
       const int chunk = 16 * ((l % S::C8) ^ tswz<D, KV8, V>(row));
       voff[i] = (PAGED ? row % 16 : row) * S::RB + chunk;
-      loff[i] = n * RPI * S::RB;
+      loff[i] = r0 * S::RB;
     }
-    // instruction i of wave w covers rows (i*NW + w)*RPI ..: cache block i*JW + (w*RPI)/16 of the tile
-    wblk = (w * RPI) / 16;
+    wblk = w;
     base = b;
     bstride = block_stride;
     tbl = table;
@@ -773,23 +776,21 @@ struct Stager {
       for (int i = 0; i < CPT; ++i) load_lds(rsrc, tile + loff[i], voff[i]);
       (void)e;
     } else {
-      // one descriptor per cache block: its physical block, and only its rows
-      // below Lk (a block past the sequence, or an unmapped one (id -1 in the
-      // LDS table), gets none: nothing is read and the LDS rows receive zeros)
+      // the wave's cache block: its physical block, and only its rows below
+      // Lk (a block past the sequence, or an unmapped one (id -1 in the LDS
+      // table), gets none: nothing is read and the LDS rows receive zeros).
+      // e[wblk], written as a mask-and-or over the candidates: as a select
+      // chain the compiler turns it into an indexed load from a stack copy of
+      // e (a scratch store and load per tile)
+      int phys = 0;
 #pragma unroll
-      for (int i = 0; i < CPT; ++i) {
-        // e[i * JW + wblk], written as a mask-and-or over the JW candidates:
-        // as a select chain the compiler turns it into an indexed load from a
-        // stack copy of e (a scratch store and load per tile)
-        int phys = 0;
+      for (int j = 0; j < EPT; ++j) phys |= e[j] & -(int)(wblk == j);
+      const int lb = k0 / 16 + wblk;
+      const int rows = __builtin_amdgcn_readfirstlane(phys < 0 ? 0 : min(max(Lk - 16 * lb, 0), 16));
+      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(base + (size_t)(rows > 0 ? phys : 0) * bstride), (short)0, rows * S::RB, kBufferDword3);
 #pragma unroll
-        for (int j = 0; j < JW; ++j) phys |= e[i * JW + j] & -(int)(wblk == j);
-        const int lb = k0 / 16 + i * JW + wblk;
-        const int rows = __builtin_amdgcn_readfirstlane(phys < 0 ? 0 : min(max(Lk - 16 * lb, 0), 16));
-        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(base + (size_t)(rows > 0 ? phys : 0) * bstride), (short)0, rows * S::RB, kBufferDword3);
-        load_lds(rsrc, tile + loff[i], voff[i]);
-      }
+      for (int i = 0; i < CPT; ++i) load_lds(rsrc, tile + loff[i], voff[i]);
     }
   }
   static __device__ __forceinline__ void* uniform_ptr(const char* ptr) {
